@@ -1,0 +1,358 @@
+"""Pins the CPU oracle to facts fixed outside itself (no GPU needed).
+
+Each test checks the oracle against something independent of its code: a
+value printed on the pages, a hand-worked case, a library routine (numpy /
+torch sorting, counting, matmul, bf16 conversion), a closed form, or brute
+force on tiny inputs.  A dropped term, a wrong sign or index, or a transposed
+operand anywhere in the oracle fails at least one of these.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import compare_bf16, tolerance
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _bf16_lib(x):
+    """Library bf16 conversion (torch, round to nearest even) of float32-exact reals."""
+    return torch.tensor(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+
+
+def _bits_to_f(h):
+    return float(np.array([h], np.uint16).astype(np.uint32).__lshift__(16).view(np.float32)[0])
+
+
+# ------------------------------------------------------------------ bf16 --
+
+def test_bf16_round_matches_library_on_float_exact_values():
+    r = np.random.default_rng(7)
+    xs = np.concatenate([r.standard_normal(2000).astype(np.float32) * 10,
+                         np.array([0.0, -0.0, 1.0, 257.0, 259.0, 1e-40, -3.0e38], np.float32)])
+    lib = _bf16_lib(xs)
+    mine = np.array([oracle.bf16_round(float(x)) for x in xs], np.uint16)
+    # -0.0 keeps its sign in both
+    np.testing.assert_array_equal(mine, lib)
+
+
+# --------------------------------------------------------------- dequant --
+
+def test_dequant_hand_cases():
+    g = _gold("dequant_cases.json")
+    for c in g["cases"]:
+        s, b, q = int(c["scale"], 16), int(c["bias"], 16), c["code"]
+        got = oracle.dequant_one(s, b, q)
+        assert oracle.bf16_round(got) == int(c["expect"], 16), c
+
+
+def test_dequant_code0_is_bias_code15_is_15s_plus_b():
+    r = np.random.default_rng(1)
+    s_bits = W.to_bf16_bits(np.abs(r.standard_normal(64).astype(np.float32) * 0.02))
+    b_bits = W.to_bf16_bits(-8 * W.bf16_bits_to_f32(s_bits) + r.standard_normal(64).astype(np.float32) * 0.002)
+    for s, b in zip(s_bits, b_bits):
+        assert oracle.dequant_one(int(s), int(b), 0) == _bits_to_f(int(b))
+        exact = Fraction(_bits_to_f(int(s))) * 15 + Fraction(_bits_to_f(int(b)))
+        # 15*s + b is exact in float32 here; the library rounds it to bf16 once
+        assert Fraction(float(np.float32(float(exact)))) == exact
+        want = _bits_to_f(int(_bf16_lib([float(exact)])[0]))
+        assert oracle.dequant_one(int(s), int(b), 15) == want
+
+
+def test_dequant_all_codes_against_library():
+    r = np.random.default_rng(2)
+    for _ in range(200):
+        s = int(W.to_bf16_bits(np.array([abs(r.standard_normal()) * 0.05], np.float32))[0])
+        b = int(W.to_bf16_bits(np.array([r.standard_normal() * 0.3], np.float32))[0])
+        for q in range(16):
+            exact = Fraction(_bits_to_f(s)) * q + Fraction(_bits_to_f(b))
+            if Fraction(float(np.float32(float(exact)))) != exact:
+                continue  # not float32-exact: the library would round twice
+            want = _bits_to_f(int(_bf16_lib([float(exact)])[0]))
+            assert oracle.dequant_one(s, b, q) == want, (s, b, q)
+
+
+def test_dequant_matrix_nibble_order_and_group_layout():
+    # scale 1, bias 0 in group 0; scale 2, bias -1 in group 1: W = s*code + b exactly
+    N, K = 2, 128
+    codes = np.zeros((N, K // 2), np.uint8)
+    codes[0, 0] = 0x21          # kk=0 -> 1 (low nibble), kk=1 -> 2 (high nibble)
+    codes[1, 40] = 0xF3         # kk=80 -> 3, kk=81 -> 15  (group 1)
+    S = np.array([[0x3F80, 0x4000]] * N, np.uint16)   # 1.0, 2.0
+    B = np.array([[0x0000, 0xBF80]] * N, np.uint16)   # 0.0, -1.0
+    Wd = oracle.dequant_q4(codes, S, B)
+    assert Wd[0, 0] == 1.0 and Wd[0, 1] == 2.0 and Wd[0, 2] == 0.0
+    assert Wd[1, 80] == 2.0 * 3 - 1 and Wd[1, 81] == 2.0 * 15 - 1
+    assert Wd[1, 63] == 0.0 and Wd[1, 79] == -1.0 and Wd[1, 82] == -1.0 and Wd[0, 64] == -1.0
+
+
+def test_q4_byte_formula_matches_checkpoint_sizes():
+    g = _gold("q4_format.json")
+    bits = g["code_bits"] + (g["scale_bits"] + g["bias_bits"]) / g["group"]
+    assert bits == 4.5
+    # about 70 GB of bf16 (16 bits/weight) -> 19.4 GB: the ratio must be close to 4.5/16
+    ratio = g["q4_checkpoint_gb"] / g["bf16_checkpoint_gb_about"]
+    assert abs(ratio - bits / 16) < 0.01
+    # byte formula used by the roofline: N*K/2 code bytes + (N*K/64)*4 scale+bias bytes
+    for N, K, want in [(512, 2048, 589824), (1024, 2048, 1179648), (2048, 512, 589824)]:
+        assert N * K // 2 + (N * K // 64) * 4 == want == N * K * bits / 8
+
+
+# ----------------------------------------------------------------- top-k --
+
+def _ref_topk_lexsort(logits, k):
+    T, E = logits.shape
+    out = np.empty((T, k), np.int32)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -logits[t].astype(np.float64)))
+        out[t] = order[:k]
+    return out
+
+
+@pytest.mark.parametrize("T,E,k", [(37, 16, 2), (20, 256, 8), (5, 64, 64), (9, 1, 1), (8, 1000, 7)])
+def test_topk_matches_library_sort(T, E, k):
+    logits = np.random.default_rng(T * E + k).standard_normal((T, E)).astype(np.float32)
+    ids, w = oracle.topk_softmax(logits, k)
+    np.testing.assert_array_equal(ids, _ref_topk_lexsort(logits, k))
+    for t in range(T):
+        assert len(set(ids[t])) == k
+        sel = logits[t, ids[t]]
+        rest = np.delete(logits[t], ids[t])
+        if rest.size:
+            assert sel.min() >= rest.max()
+
+
+def test_topk_ties_and_signed_zero():
+    E = 12
+    l = np.zeros((3, E), np.float32)
+    l[0] = [1, 3, 3, 2, 3, 0, 0, 0, 0, 0, 0, 0]          # three-way tie at 3
+    l[1, :] = -1.0
+    l[1, 4] = -0.0
+    l[1, 2] = 0.0                                        # -0 == +0: lower id (2) first
+    l[2, :] = 5.0                                        # all equal: ids ascending
+    ids, w = oracle.topk_softmax(l, 4)
+    assert list(ids[0]) == [1, 2, 4, 3]
+    assert list(ids[1][:2]) == [2, 4] and list(ids[1][2:]) == [0, 1]
+    assert list(ids[2]) == [0, 1, 2, 3]
+    np.testing.assert_allclose(w[2], 0.25, rtol=0, atol=1e-15)
+
+
+def test_softmax_equals_renormalised_full_softmax():
+    r = np.random.default_rng(3)
+    logits = r.standard_normal((50, 256)).astype(np.float32) * 3
+    ids, w = oracle.topk_softmax(logits, 8)
+    full = torch.softmax(torch.tensor(logits, dtype=torch.float64), dim=1).numpy()
+    for t in range(50):
+        sel = full[t, ids[t]]
+        np.testing.assert_allclose(w[t], sel / sel.sum(), rtol=1e-12, atol=0)
+        assert abs(w[t].sum() - 1) < 1e-12
+        assert np.all(np.diff(w[t]) <= 0)
+
+
+# --------------------------------------------------------------- routing --
+
+@pytest.mark.parametrize("T,E,k,BM", [(64, 16, 2, 16), (33, 8, 3, 4), (1, 256, 8, 32), (0, 16, 2, 16),
+                                      (100, 4, 4, 128), (50, 300, 6, 16)])
+def test_route_against_library_counting_and_stable_sort(T, E, k, BM):
+    r = np.random.default_rng(T + 10 * E)
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    ids, _ = oracle.topk_softmax(logits, k)
+    rt = oracle.route(ids, E, BM)
+    flat = ids.reshape(-1)
+    A = T * k
+    np.testing.assert_array_equal(rt["counts"], np.bincount(flat, minlength=E))
+    assert rt["counts"].sum() == A
+    off = rt["offsets"]
+    assert off[0] == 0 and off[-1] == A and np.all(np.diff(off) >= 0)
+    np.testing.assert_array_equal(off[1:], np.cumsum(rt["counts"]))
+    np.testing.assert_array_equal(rt["perm"], np.argsort(flat, kind="stable"))
+    np.testing.assert_array_equal(rt["inv_perm"][rt["perm"]], np.arange(A))
+    # block map: tiles every group exactly once; only an expert's last block is partial
+    blocks = rt["blocks"]
+    assert rt["num_blocks"] == sum(-(-int(c) // BM) for c in rt["counts"])
+    assert rt["num_blocks"] <= oracle.max_blocks_bound(A, E, BM)
+    covered = np.zeros(A, np.int32)
+    for e_, r0, n, i in blocks:
+        assert 1 <= n <= BM
+        assert r0 == off[e_] + i * BM
+        covered[r0:r0 + n] += 1
+        assert np.all(flat[rt["perm"][r0:r0 + n]] == e_)
+        if n < BM:
+            assert r0 + n == off[e_ + 1]
+    assert np.all(covered == 1)
+    assert blocks[:, 2].sum() == A
+    # blocks listed expert by expert, block index ascending
+    if len(blocks):
+        keys = blocks[:, 0] * 1_000_000 + blocks[:, 3]
+        assert np.all(np.diff(keys) > 0)
+
+
+def test_route_pages_worked_example_volume():
+    g = _gold("routing_volume_2k.json")
+    T, E, k = g["T"], g["E"], g["k"]
+    logits = W.gen_logits(99, T, E)
+    ids, _ = oracle.topk_softmax(logits, k)
+    rt = oracle.route(ids, E, 32)
+    assert rt["counts"].sum() == g["assignments"]
+    assert rt["counts"].mean() == g["mean_rows_per_expert"]
+    assert rt["counts"].max() > g["mean_rows_per_expert"]    # imbalanced, as on the pages
+
+
+# ---------------------------------------------------------- grouped GEMM --
+
+def _tiny(T=24, E=5, k=2, K=128, N=32, cid=11):
+    w = W.custom(cid, T, E, k, K, N)
+    p = W.make_problem(w)
+    ids, wt = oracle.topk_softmax(p.logits, k)
+    rt = oracle.route(ids, E, 16)
+    return w, p, ids, wt, rt
+
+
+def test_grouped_gemm_brute_force_per_token():
+    w, p, ids, _, rt = _tiny()
+    Y = oracle.grouped_gemm_q4(p.X, w.k, p.Wq, p.S, p.B, rt["perm"], rt["offsets"])
+    x = W.bf16_bits_to_f32(p.X).astype(np.float64)
+    for t in range(w.T):
+        for j in range(w.k):
+            e = ids[t, j]
+            Wd = oracle.dequant_q4(p.Wq[e], p.S[e], p.B[e])
+            ref = Wd @ x[t]
+            np.testing.assert_allclose(Y[rt["inv_perm"][t * w.k + j]], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_gemm_dense_case_against_library_matmul():
+    # E=1, k=1: every token goes to expert 0, and the GEMM is X . Wdq^T
+    w = W.custom(12, 40, 1, 1, 192, 48)
+    p = W.make_problem(w)
+    ids, _ = oracle.topk_softmax(p.logits, 1)
+    rt = oracle.route(ids, 1, 16)
+    Y = oracle.grouped_gemm_q4(p.X, 1, p.Wq, p.S, p.B, rt["perm"], rt["offsets"])
+    # independent dequant: unpack with numpy, scale*code+bias in float32 (exact here), bf16 via torch
+    c = p.Wq[0]
+    codes = np.empty((w.N, w.K), np.float32)
+    codes[:, 0::2] = c & 0x0F
+    codes[:, 1::2] = c >> 4
+    s = np.repeat(W.bf16_bits_to_f32(p.S[0]), 64, axis=1)
+    b = np.repeat(W.bf16_bits_to_f32(p.B[0]), 64, axis=1)
+    v = (s.astype(np.float64) * codes + b)
+    assert np.all(v.astype(np.float32).astype(np.float64) == v)
+    Wd = torch.tensor(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64)
+    X = torch.tensor(W.bf16_bits_to_f32(p.X).astype(np.float64))
+    ref = (X @ Wd.T).numpy()
+    np.testing.assert_array_equal(rt["perm"], np.arange(w.T))
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_gemm_zero_scale_closed_form_and_zero_weights():
+    w, p, ids, _, rt = _tiny(cid=13)
+    S0 = np.zeros_like(p.S)
+    Y = oracle.grouped_gemm_q4(p.X, w.k, p.Wq, S0, p.B, rt["perm"], rt["offsets"])
+    x = W.bf16_bits_to_f32(p.X).astype(np.float64)
+    xs = x.reshape(w.T, w.K // 64, 64).sum(axis=2)                # [T, G]
+    for pos in range(w.T * w.k):
+        a = rt["perm"][pos]
+        t, e = a // w.k, ids.reshape(-1)[a]
+        b = W.bf16_bits_to_f32(p.B[e]).astype(np.float64)          # [N, G]
+        np.testing.assert_allclose(Y[pos], b @ xs[t], rtol=1e-12, atol=1e-12)
+    Y0 = oracle.grouped_gemm_q4(p.X, w.k, p.Wq, S0, np.zeros_like(p.B), rt["perm"], rt["offsets"])
+    assert np.all(Y0 == 0.0)
+
+
+def test_sampled_rows_agree_with_grouped():
+    w, p, ids, _, rt = _tiny(T=30, E=7, k=3, cid=14)
+    Y = oracle.grouped_gemm_q4(p.X, w.k, p.Wq, p.S, p.B, rt["perm"], rt["offsets"])
+    a = rt["perm"]
+    Yr = oracle.expert_rows_q4(p.X, p.Wq, p.S, p.B, a // w.k, ids.reshape(-1)[a])
+    np.testing.assert_allclose(Yr, Y, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ expert FFN --
+
+def _ffn_brute(p, ids, wt, t, shared=True):
+    x = W.bf16_bits_to_f32(p.X[t]).astype(np.float64)
+    I = p.w.N
+
+    def one(guq, gus, gub, dnq, dns, dnb):
+        gu = oracle.dequant_q4(guq, gus, gub) @ x
+        g, u = gu[:I], gu[I:]
+        h = torch.tensor(g / (1 + np.exp(-g)) * u).to(torch.float32)
+        # float32 -> bf16 by the library; exact reals here differ from float32 by < 1 bf16 tie
+        h = h.to(torch.bfloat16).to(torch.float64).numpy()
+        return oracle.dequant_q4(dnq, dns, dnb) @ h
+
+    out = np.zeros(p.w.K)
+    for j in range(ids.shape[1]):
+        e = ids[t, j]
+        out += wt[t, j] * one(p.gu_q[e], p.gu_s[e], p.gu_b[e], p.dn_q[e], p.dn_s[e], p.dn_b[e])
+    if shared:
+        out += one(p.sh_gu_q[0], p.sh_gu_s[0], p.sh_gu_b[0], p.sh_dn_q[0], p.sh_dn_s[0], p.sh_dn_b[0])
+    return out
+
+
+def _ffn_problem(T=6, E=4, k=2, H=128, I=64, cid=21):
+    w = W.custom(cid, T, E, k, H, I, ffn=True)
+    p = W.make_problem(w)
+    ids, wt = oracle.topk_softmax(p.logits, k)
+    sh = (p.sh_gu_q, p.sh_gu_s, p.sh_gu_b, p.sh_dn_q, p.sh_dn_s, p.sh_dn_b)
+    return w, p, ids, wt, sh
+
+
+def test_ffn_brute_force_per_token():
+    w, p, ids, wt, sh = _ffn_problem()
+    out = oracle.expert_ffn_q4(p.X, ids, wt, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b, sh=sh)
+    for t in range(w.T):
+        ref = _ffn_brute(p, ids, wt, t)
+        # the brute force rounds h through float32 first: allow its rare one-ulp h flips
+        ok, st = compare_bf16(np.array([oracle.bf16_round(v) for v in out[t]], np.uint16), ref)
+        assert ok, st
+        np.testing.assert_allclose(out[t], ref, rtol=0, atol=tolerance(ref))
+
+
+def test_ffn_single_expert_and_zero_shared():
+    w, p, ids, wt, sh = _ffn_problem(T=5, E=3, k=1, cid=22)
+    one = np.ones_like(wt)
+    zero_sh = (sh[0], np.zeros_like(sh[1]), np.zeros_like(sh[2]), sh[3], np.zeros_like(sh[4]),
+               np.zeros_like(sh[5]))
+    with_zero = oracle.expert_ffn_q4(p.X, ids, one, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b,
+                                     sh=zero_sh)
+    routed = oracle.expert_ffn_q4(p.X, ids, one, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b)
+    np.testing.assert_array_equal(with_zero, routed)
+    for t in range(w.T):
+        np.testing.assert_allclose(routed[t], _ffn_brute(p, ids, one, t, shared=False),
+                                   rtol=0, atol=1e-9 + 1e-2 * np.abs(routed[t]).max())
+
+
+def test_ffn_zero_gate_gives_zero():
+    w, p, ids, wt, sh = _ffn_problem(T=3, cid=23)
+    gs, gb = p.gu_s.copy(), p.gu_b.copy()
+    gs[:, : w.N] = 0
+    gb[:, : w.N] = 0          # gate == 0 -> silu(0) = 0 -> h = 0 -> zero output
+    out = oracle.expert_ffn_q4(p.X, ids, wt, p.gu_q, gs, gb, p.dn_q, p.dn_s, p.dn_b)
+    assert np.all(out == 0.0)
+
+
+# ---------------------------------------------------------- the tolerance --
+
+def test_tolerance_rule_accepts_honest_rounding_and_rejects_errors():
+    r = np.random.default_rng(5)
+    ref = r.standard_normal(200_000) * 4.2
+    honest = np.array(_bf16_lib(ref.astype(np.float32)), np.uint16)
+    ok, st = compare_bf16(honest, ref)
+    assert ok, st
+    bad = np.array(_bf16_lib((ref * 1.01).astype(np.float32)), np.uint16)
+    ok, st = compare_bf16(bad, ref)
+    assert not ok and st["n_bad"] > 1000
+    nan = honest.copy()
+    nan[17] = 0x7FC0
+    assert not compare_bf16(nan, ref)[0]
