@@ -1,0 +1,146 @@
+/*
+ * moeq4.h -- C ABI of the MoE routing + group-wise affine 4-bit grouped GEMM
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the problem statement of Perplexity Engineering,
+ * "Optimizing on-device inference for Apple Silicon" (2026):
+ *   - section "Keep expert routing on the GPU": after the per-token expert
+ *     selection, a histogram counts assignments per expert, a prefix scan
+ *     turns the counts into start offsets, a scatter places rows into their
+ *     expert groups and a block map lists the fixed-size blocks the grouped
+ *     GEMM processes; nothing waits on the host inside the layer.
+ *   - section "Dequantize weights during matrix multiplication": each weight is
+ *     a 4-bit code, 64 weights along K share one bf16 scale and one bf16 bias;
+ *     the weights are rebuilt in bf16 a small tile at a time on chip and never
+ *     written back to memory as a bf16 array; fp32 accumulation, bf16 output.
+ *   - section "Qwen creates three workload shapes": a router scores the
+ *     experts and picks 8 of 256 per token.
+ *
+ * Conventions for every call below.
+ *   - Array arguments are DEVICE pointers owned by the caller (allocate them
+ *     with hipMalloc or any device allocator); scalar sizes are host ints.
+ *     All arrays are dense and row-major.  bf16 values travel as uint16_t bit
+ *     patterns.  The library never allocates, frees, copies to the host or
+ *     synchronises; it enqueues kernels on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream) and returns.
+ *   - Return value: MOEQ4_OK (0) or a negative MOEQ4_ERR_* code.  All argument
+ *     checks run on the host before anything is enqueued; on an error nothing
+ *     is written.  MOEQ4_ERR_HIP reports a failed launch; faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Alignment: every array pointer must be 16-byte aligned.
+ *   - Calls on different streams may run concurrently as long as their output
+ *     and workspace buffers do not overlap.
+ *
+ * Group-wise affine 4-bit matrix [N, K] (K % 64 == 0):
+ *   codes  uint8  [N, K/2]   byte i of a row holds the code of K index 2i in
+ *                             its low nibble and of 2i+1 in its high nibble
+ *   scales uint16 [N, K/64]  bf16
+ *   biases uint16 [N, K/64]  bf16
+ *   weight(n, kk) = bf16( scale[n, kk/64] * code(n, kk) + bias[n, kk/64] )
+ * A stack of E such matrices is [E, N, K/2] / [E, N, K/64].
+ */
+#ifndef MOEQ4_H
+#define MOEQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEQ4_OK 0
+#define MOEQ4_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOEQ4_ERR_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define MOEQ4_ERR_ALIGN (-3)       /* a pointer is not 16-byte aligned */
+#define MOEQ4_ERR_WORKSPACE (-4)   /* workspace smaller than required */
+#define MOEQ4_ERR_UNSUPPORTED (-5) /* valid request this build does not implement */
+#define MOEQ4_ERR_HIP (-6)         /* a HIP launch failed (no device, bad stream, ...) */
+
+#define MOEQ4_MAX_EXPERTS 1024
+#define MOEQ4_MAX_TOPK 64
+
+/* Human-readable text for a status code.  Never NULL; static storage. */
+const char* moe_strerror(int status);
+
+/* Diagnostics: the HIP error text and the kernel of the calling thread's most
+ * recent MOEQ4_ERR_HIP ("" if none).  Never NULL; valid until the thread's next
+ * library call. */
+const char* moe_last_error_detail(void);
+
+/* Block-map tile height used when a call passes block_rows = 0: chosen from
+ * the mean rows per expert, T*k/E (section "Match tile size to expert load":
+ * tile height is matched to the expert load).  Returns 16, 32, 64 or 128, or
+ * a negative error code for invalid T, E, k. */
+int moe_default_block_rows(int T, int E, int k);
+
+/* Host-side upper bound on the number of block-map entries for any routing of
+ * T tokens to k of E experts with tile height block_rows (0 = default):
+ *   floor((A + m*(block_rows-1)) / block_rows),  A = T*k,  m = min(E, A).
+ * Size `blocks` for this many entries and pass it to the GEMM as max_blocks.
+ * Negative error code on invalid arguments. */
+int moe_max_blocks(int T, int E, int k, int block_rows);
+
+/* Bytes of device scratch moe_route needs (0 is possible).  Returns 0 on
+ * invalid arguments as well; moe_route then reports the error. */
+size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows);
+
+/* Routing on the GPU (section "Keep expert routing on the GPU").
+ *
+ * In:  logits     float [T, E]   router scores; must be finite.
+ * Out: topk_ids   int32 [T, k]   per token the k largest logits, in
+ *                                descending order; equal logits are ordered
+ *                                by ascending expert id; -0 equals +0.
+ *      topk_w     float [T, k]   softmax over the k selected logits (fp32).
+ *      counts     int32 [E]      assignments per expert (histogram).
+ *      offsets    int32 [E+1]    exclusive prefix sum of counts; offsets[E] = T*k.
+ *      perm       int32 [T*k]    sorted position p -> assignment a = t*k + j;
+ *                                experts in ascending order, and inside an
+ *                                expert group ascending a (a stable sort).
+ *      inv_perm   int32 [T*k]    assignment a -> sorted position p.
+ *      blocks     int32 [max_blocks, 4]  entries {expert, first sorted row,
+ *                                rows (1..block_rows), block index inside the
+ *                                expert}, expert by expert; only the first
+ *                                *num_blocks entries are written.
+ *      num_blocks int32 [1]      number of block-map entries (stays on the device).
+ * workspace: device scratch of at least moe_route_workspace_bytes(...) bytes
+ *            (may be NULL when that is 0).
+ * Sizes: T >= 0, 1 <= k <= min(E, MOEQ4_MAX_TOPK), E <= MOEQ4_MAX_EXPERTS,
+ *        block_rows in {0 (default), 16, 32, 64, 128}.
+ * T = 0 writes zero counts and offsets and num_blocks = 0.
+ * Output buffers must not overlap each other or the workspace. */
+int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t* topk_ids,
+              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+              int32_t* blocks, int32_t* num_blocks, void* workspace, size_t ws_bytes, void* stream);
+
+/* Grouped GEMM over group-wise affine 4-bit expert weights (section
+ * "Dequantize weights during matrix multiplication").
+ *
+ * For every block-map entry b < *num_blocks with expert e and sorted rows
+ * [r0, r0 + rows):
+ *   Y[p, n] = bf16( sum_kk X[perm[p] / k, kk] * weight_e(n, kk) ),  p in [r0, r0+rows)
+ * with fp32 accumulation.  Weights are rebuilt in bf16 on chip, tile by tile.
+ *
+ * In:  X        uint16 (bf16) [T, K]  token activations (rows gathered via perm).
+ *      Wq, scales, biases    [E, N, K/2], [E, N, K/64], [E, N, K/64]  (format above).
+ *      perm, blocks, num_blocks  as produced by moe_route for the same T, E, k,
+ *                            block_rows.
+ *      max_blocks            host bound from moe_max_blocks (sizes the grid;
+ *                            entries past *num_blocks exit at once).
+ * Out: Y        uint16 (bf16) [T*k, N]  in sorted order (row p belongs to
+ *                            assignment perm[p]); rows not covered by a block
+ *                            are not written.
+ * Sizes: T >= 0, K % 64 == 0, K >= 64, N % 16 == 0, N >= 16, 1 <= k <= E,
+ *        E <= MOEQ4_MAX_EXPERTS, block_rows in {0, 16, 32, 64, 128} and equal
+ *        to the value given to moe_route, max_blocks >= moe_max_blocks(T, E,
+ *        k, block_rows).  Y must not overlap the inputs. */
+int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wq,
+                        const uint16_t* scales, const uint16_t* biases, const int32_t* perm,
+                        const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
+                        int block_rows, uint16_t* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ4_H */

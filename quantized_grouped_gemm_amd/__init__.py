@@ -1,0 +1,173 @@
+"""Python binding of libmoeq4 (MoE routing + group-wise affine 4-bit grouped GEMM, gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of the shared
+library.  Functions take torch tensors (device memory) or raw integer device
+addresses and pass their pointers, with the caller's current HIP stream,
+straight to the C ABI declared in include/moeq4.h.  There is no fallback: if
+the library has not been built, importing the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# The HIP runtime that torch loads must be the only one in the process: torch
+# hands out its streams and device pointers, and a second copy of
+# libamdhip64 would not know them.  Loading torch first makes libmoeq4's
+# dependency on libamdhip64.so.7 bind to torch's copy.
+import torch  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libmoeq4.so")
+
+MOEQ4_OK = 0
+MOEQ4_ERR_NULL = -1
+MOEQ4_ERR_SHAPE = -2
+MOEQ4_ERR_ALIGN = -3
+MOEQ4_ERR_WORKSPACE = -4
+MOEQ4_ERR_UNSUPPORTED = -5
+MOEQ4_ERR_HIP = -6
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/moeq4.h
+SIGNATURES = {
+    "moe_strerror": (ctypes.c_char_p, [_i]),
+    "moe_last_error_detail": (ctypes.c_char_p, []),
+    "moe_default_block_rows": (_i, [_i, _i, _i]),
+    "moe_max_blocks": (_i, [_i, _i, _i, _i]),
+    "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "moe_route": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm_q4": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                 _vp, _vp]),
+}
+
+
+class MoeQ4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        detail = lib().moe_last_error_detail().decode() if status == MOEQ4_ERR_HIP else ""
+        super().__init__(f"{fn}: {strerror(status)} (status {status}) {detail}".rstrip())
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libmoeq4 is not built ({LIB_PATH} missing); run `python -m quantized_grouped_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoeq4 (loaded on first use; raises ImportError if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(int(status)).decode()
+
+
+def _p(x):
+    """Device address of a torch tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ok(fn, status):
+    if status != MOEQ4_OK:
+        raise MoeQ4Error(fn, status)
+
+
+def moe_default_block_rows(T: int, E: int, k: int) -> int:
+    r = lib().moe_default_block_rows(T, E, k)
+    _ok("moe_default_block_rows", min(r, 0))
+    return r
+
+
+def moe_max_blocks(T: int, E: int, k: int, block_rows: int = 0) -> int:
+    r = lib().moe_max_blocks(T, E, k, block_rows)
+    _ok("moe_max_blocks", min(r, 0))
+    return r
+
+
+def moe_route_workspace_bytes(T: int, E: int, k: int, block_rows: int = 0) -> int:
+    return int(lib().moe_route_workspace_bytes(T, E, k, block_rows))
+
+
+def moe_route(logits, T, E, k, block_rows, topk_ids, topk_w, counts, offsets, perm, inv_perm,
+              blocks, num_blocks, workspace, ws_bytes, stream=None):
+    _ok("moe_route", lib().moe_route(
+        _p(logits), T, E, k, block_rows, _p(topk_ids), _p(topk_w), _p(counts), _p(offsets),
+        _p(perm), _p(inv_perm), _p(blocks), _p(num_blocks), _p(workspace), int(ws_bytes),
+        _stream(stream)))
+
+
+def moe_grouped_gemm_q4(X, T, K, N, E, k, Wq, scales, biases, perm, blocks, num_blocks, max_blocks,
+                        block_rows, Y, stream=None):
+    _ok("moe_grouped_gemm_q4", lib().moe_grouped_gemm_q4(
+        _p(X), T, K, N, E, k, _p(Wq), _p(scales), _p(biases), _p(perm), _p(blocks), _p(num_blocks),
+        max_blocks, block_rows, _p(Y), _stream(stream)))
+
+
+# ---------------------------------------------------------------- plumbing --
+# Device buffers come from torch (memory and streams only).
+
+def alloc_route(T: int, E: int, k: int, block_rows: int = 0, device="cuda"):
+    """Output and workspace tensors for moe_route / moe_grouped_gemm_q4."""
+    bm = block_rows or moe_default_block_rows(T, E, k)
+    mb = moe_max_blocks(T, E, k, bm)
+    ws = moe_route_workspace_bytes(T, E, k, bm)
+    i32 = dict(dtype=torch.int32, device=device)
+    A = T * k
+    return dict(
+        block_rows=bm, max_blocks=mb,
+        topk_ids=torch.empty(max(A, 1), **i32), topk_w=torch.empty(max(A, 1), dtype=torch.float32, device=device),
+        counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+        perm=torch.empty(max(A, 1), **i32), inv_perm=torch.empty(max(A, 1), **i32),
+        blocks=torch.empty(max(mb, 1) * 4, **i32), num_blocks=torch.empty(4, **i32),
+        workspace=torch.empty(max(ws, 1), dtype=torch.uint8, device=device), ws_bytes=ws,
+    )
+
+
+def route(logits, k: int, block_rows: int = 0, bufs=None, stream=None):
+    """Runs moe_route on a [T, E] float32 device tensor; returns the buffer dict."""
+    T, E = logits.shape
+    b = bufs or alloc_route(T, E, k, block_rows, device=logits.device)
+    moe_route(logits, T, E, k, b["block_rows"], b["topk_ids"], b["topk_w"], b["counts"], b["offsets"],
+              b["perm"], b["inv_perm"], b["blocks"], b["num_blocks"], b["workspace"], b["ws_bytes"],
+              stream)
+    return b
+
+
+def grouped_gemm_q4(X, k, Wq, scales, biases, rt, Y=None, stream=None):
+    """Y [T*k, N] bf16 bit patterns (int16 storage) in sorted order for routing tables ``rt``."""
+    T, K = X.shape
+    E, N, _ = Wq.shape
+    if Y is None:
+        Y = torch.empty((max(T * k, 1), N), dtype=torch.int16, device=X.device)
+    moe_grouped_gemm_q4(X, T, K, N, E, k, Wq, scales, biases, rt["perm"], rt["blocks"], rt["num_blocks"],
+                        rt["max_blocks"], rt["block_rows"], Y, stream)
+    return Y

@@ -1,0 +1,130 @@
+// api.hip -- the C ABI of include/moeq4.h: host-side argument checks, tile
+// choice from the workload shape, and kernel launches on the caller's stream.
+// Nothing here allocates, copies to the host or synchronises.
+#include "common.h"
+
+#include <stdio.h>
+
+using namespace moeq4;
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_block_rows(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+int check_routing_shape(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > MOEQ4_MAX_EXPERTS || k < 1 || k > E) return MOEQ4_ERR_SHAPE;
+  if (k > MOEQ4_MAX_TOPK) return MOEQ4_ERR_UNSUPPORTED;
+  if ((long long)T * k > (long long)INT32_MAX / 2) return MOEQ4_ERR_SHAPE;
+  return MOEQ4_OK;
+}
+
+// block_rows 0 -> default; returns <= 0 on error
+int resolve_block_rows(int T, int E, int k, int block_rows) {
+  if (block_rows == 0) return moe_default_block_rows(T, E, k);
+  return valid_block_rows(block_rows) ? block_rows : MOEQ4_ERR_SHAPE;
+}
+
+}  // namespace
+
+namespace moeq4 {
+void note_hip_error(hipError_t err, const char* what) {
+  snprintf(g_detail, sizeof g_detail, "%s: %s (%d)", what, hipGetErrorString(err), (int)err);
+}
+}  // namespace moeq4
+
+extern "C" {
+
+const char* moe_last_error_detail(void) { return g_detail; }
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOEQ4_OK: return "ok";
+    case MOEQ4_ERR_NULL: return "a required pointer is NULL";
+    case MOEQ4_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOEQ4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOEQ4_ERR_WORKSPACE: return "workspace smaller than required";
+    case MOEQ4_ERR_UNSUPPORTED: return "request not supported by this build";
+    case MOEQ4_ERR_HIP: return "a HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_default_block_rows(int T, int E, int k) {
+  const int rc = check_routing_shape(T, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  // mean rows per expert, with headroom for the spread around it
+  const long long A = (long long)T * k;
+  const long long want = (A * 5 + 4LL * E - 1) / (4LL * E);  // ceil(1.25 * A / E)
+  int bm = 16;
+  while (bm < 128 && bm < want) bm <<= 1;
+  return bm;
+}
+
+int moe_max_blocks(int T, int E, int k, int block_rows) {
+  const int rc = check_routing_shape(T, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  const int bm = resolve_block_rows(T, E, k, block_rows);
+  if (bm <= 0) return bm;
+  const long long A = (long long)T * k;
+  const long long m = A < E ? A : E;
+  return (int)((A + m * (bm - 1)) / bm);
+}
+
+size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows) {
+  if (check_routing_shape(T, E, k) != MOEQ4_OK) return 0;
+  if (resolve_block_rows(T, E, k, block_rows) <= 0) return 0;
+  return route_plan(T, E, k).ws_bytes;
+}
+
+int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t* topk_ids,
+              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+              int32_t* blocks, int32_t* num_blocks, void* workspace, size_t ws_bytes,
+              void* stream) {
+  int rc = check_routing_shape(T, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  const int bm = resolve_block_rows(T, E, k, block_rows);
+  if (bm <= 0) return bm;
+  if (!counts || !offsets || !num_blocks) return MOEQ4_ERR_NULL;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv_perm || !blocks))
+    return MOEQ4_ERR_NULL;
+  const RoutePlan plan = route_plan(T, E, k);
+  if (ws_bytes < plan.ws_bytes) return MOEQ4_ERR_WORKSPACE;
+  if (plan.ws_bytes > 0 && !workspace) return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {logits, topk_ids, topk_w, counts, offsets, perm, inv_perm, blocks,
+                        num_blocks, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
+  const hipError_t err = route_launch(plan, logits, T, E, k, bm, topk_ids, topk_w, counts, offsets,
+                                      perm, inv_perm, blocks, num_blocks, workspace,
+                                      (hipStream_t)stream);
+  return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
+int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wq,
+                        const uint16_t* scales, const uint16_t* biases, const int32_t* perm,
+                        const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
+                        int block_rows, uint16_t* Y, void* stream) {
+  int rc = check_routing_shape(T, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  if (K < 64 || K % 64 != 0 || N < 16 || N % 16 != 0) return MOEQ4_ERR_SHAPE;
+  const int bm = resolve_block_rows(T, E, k, block_rows);
+  if (bm <= 0) return bm;
+  const int bound = moe_max_blocks(T, E, k, bm);
+  if (bound < 0) return bound;
+  if (max_blocks < bound) return MOEQ4_ERR_SHAPE;
+  if (T == 0) return MOEQ4_OK;
+  if (!X || !Wq || !scales || !biases || !perm || !blocks || !num_blocks || !Y)
+    return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {X, Wq, scales, biases, perm, blocks, num_blocks, Y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOEQ4_ERR_ALIGN;
+  const hipError_t err = gemm_q4_launch(X, T, K, N, E, k, Wq, scales, biases, perm, blocks,
+                                        num_blocks, max_blocks, bm, Y, (hipStream_t)stream);
+  return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
+}  // extern "C"

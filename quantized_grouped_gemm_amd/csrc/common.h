@@ -1,0 +1,95 @@
+// common.h -- device helpers shared by the HIP kernels of the MoE Q4 library
+// (gfx950 / CDNA4, wave64).  Internal: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moeq4.h"
+
+namespace moeq4 {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;  // weights per scale/bias group along K
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: round to nearest even
+}
+
+// ---- wave64 reductions through DPP; the full result lands in lane 63 and is
+// ---- broadcast with readlane (uniform, lives in an SGPR).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));         // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));         // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f32<0x141>(x));        // row_half_mirror
+  x = fmaxf(x, dpp_f32<0x140>(x));        // row_mirror
+  x = fmaxf(x, dpp_f32<0x142, 0xA>(x));   // row_bcast:15 into rows 1 and 3
+  x = fmaxf(x, dpp_f32<0x143, 0xC>(x));   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  x += dpp_f32<0x142, 0xA>(x);
+  x += dpp_f32<0x143, 0xC>(x);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// ---- host side: launch through hipLaunchKernel so the status is returned.
+void note_hip_error(hipError_t err, const char* what);  // api.hip: per-thread detail text
+
+template <typename... Args>
+inline hipError_t launch(const char* name, const void* fn, dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  const hipError_t err = hipLaunchKernel(fn, grid, block, argv, shmem, stream);
+  if (err != hipSuccess) note_hip_error(err, name);
+  return err;
+}
+
+// ---- internal entry points implemented in route.hip / gemm_q4.hip
+struct RoutePlan {
+  int tpc;        // tokens per chunk (one workgroup of the top-k/rank kernel)
+  int nchunks;    // ceil(T / tpc)
+  int nbits;      // bits that distinguish expert ids: ceil(log2(E))
+  size_t ws_chunk_counts;  // byte offset of chunk counts [nchunks][E]
+  size_t ws_local_rank;    // byte offset of in-chunk ranks [T*k]
+  size_t ws_bytes;         // total workspace
+};
+
+RoutePlan route_plan(int T, int E, int k);
+
+hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E, int k, int block_rows,
+                        int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* inv_perm, int32_t* blocks, int32_t* num_blocks,
+                        void* workspace, hipStream_t stream);
+
+hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wq,
+                          const uint16_t* S, const uint16_t* B, const int32_t* perm,
+                          const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
+                          int block_rows, uint16_t* Y, hipStream_t stream);
+
+}  // namespace moeq4

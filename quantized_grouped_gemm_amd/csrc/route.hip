@@ -1,0 +1,322 @@
+// route.hip -- GPU-resident MoE routing for gfx950.
+//
+// Perplexity Engineering, "Optimizing on-device inference for Apple Silicon",
+// section "Keep expert routing on the GPU": after each token picks its
+// experts, a histogram counts assignments per expert, a prefix scan turns the
+// counts into start offsets, a scatter places rows into their expert groups,
+// and a block map lists the fixed-size blocks the grouped GEMM processes.  The
+// whole sequence stays on the GPU: the block count never goes to the host.
+//
+// Three kernels, all on the caller's stream:
+//   k_topk_rank      one wave per token: top-k by k rounds of a wave-wide
+//                    argmax (DPP max + ballot), softmax over the k selected
+//                    logits; then, per workgroup "chunk" of tokens, the
+//                    histogram of its assignments and each assignment's stable
+//                    rank among same-expert assignments of the chunk (ballot
+//                    match masks over the expert-id bits + mbcnt popcounts).
+//   k_scan_blockmap  one workgroup: per-expert exclusive scan over chunks,
+//                    counts, offsets, block counts and their scan, block map.
+//   k_scatter        one thread per assignment: perm / inv_perm.
+// Only integer adds decide positions, so every output is deterministic.
+#include "common.h"
+
+namespace moeq4 {
+
+constexpr int kRouteThreads = 256;         // 4 waves per chunk workgroup
+constexpr int kChunkAssignMax = 2048;      // assignments per chunk (LDS bound)
+constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / 4;
+constexpr int kScanThreads = 1024;
+
+// ----------------------------------------------------------------------------
+// top-k + softmax + chunk histogram + in-chunk stable ranks
+// Lane l of a token's wave holds experts [l*VPT, (l+1)*VPT).
+template <int VPT>
+__global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
+    const float* __restrict__ logits, int T, int E, int k, int tpc, int nbits,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts,
+    int32_t* __restrict__ local_rank) {
+  extern __shared__ int smem[];
+  int* sids = smem;              // [tpc * k] expert ids of the chunk's assignments
+  int* cnt = smem + tpc * k;     // [4][E] per-wave counters, then per-wave bases
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int chunk = blockIdx.x;
+  const int t0 = chunk * tpc;
+  const int ntok = min(tpc, T - t0);
+
+  for (int i = threadIdx.x; i < 4 * E; i += kRouteThreads) cnt[i] = 0;
+
+  for (int i = wv; i < ntok; i += 4) {
+    const int t = t0 + i;
+    const float* row = logits + (size_t)t * E;
+    float v[VPT];
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) {
+      const int e = lane * VPT + s;
+      v[s] = (e < E) ? row[e] : -INFINITY;
+    }
+    int my_id = 0;
+    float my_v = 0.f;
+    for (int j = 0; j < k; ++j) {
+      // best of this lane: larger value, lower slot on ties
+      float bv = v[0];
+      int bs = 0;
+#pragma unroll
+      for (int s = 1; s < VPT; ++s) {
+        if (v[s] > bv) {
+          bv = v[s];
+          bs = s;
+        }
+      }
+      const float m = wave_max_f32(bv);
+      // lowest lane holding the maximum has the lowest expert id (-0 == +0)
+      const uint64_t bal = __ballot(bv == m);
+      const int wl = bal ? (__ffsll((unsigned long long)bal) - 1) : 0;
+      const int ws = __shfl(bs, wl);
+      if (lane == wl) {
+#pragma unroll
+        for (int s = 0; s < VPT; ++s)
+          if (s == ws) v[s] = -INFINITY;
+      }
+      if (lane == j) {
+        my_id = min(wl * VPT + ws, E - 1);  // stays in range even for non-finite input
+        my_v = m;
+      }
+    }
+    const float v0 = __shfl(my_v, 0);
+    const float ex = (lane < k) ? expf(my_v - v0) : 0.f;
+    const float sum = wave_sum_f32(ex);
+    if (lane < k) {
+      ids_out[(size_t)t * k + lane] = my_id;
+      w_out[(size_t)t * k + lane] = ex / sum;
+      sids[i * k + lane] = my_id;
+    }
+  }
+  __syncthreads();
+
+  // ---- in-chunk histogram and stable ranks
+  const int na = ntok * k;
+  const int nslices = (na + 63) >> 6;
+  const int spw = (nslices + 3) >> 2;  // contiguous slices per wave
+  const uint64_t lt = lanemask_lt();
+  int rank[kMaxSlicesPerWave];
+  int eid[kMaxSlicesPerWave];
+#pragma unroll
+  for (int s = 0; s < kMaxSlicesPerWave; ++s) {
+    rank[s] = 0;
+    eid[s] = -1;
+    if (s >= spw) continue;
+    const int slice = wv * spw + s;
+    const int al = slice * 64 + lane;
+    const bool valid = slice < nslices && al < na;
+    const int e = valid ? sids[al] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      match &= bit ? bb : ~bb;
+    }
+    if (valid) {
+      const int before = __popcll(match & lt);
+      const int old = cnt[wv * E + e];
+      rank[s] = old + before;
+      eid[s] = e;
+      // the highest lane of each match group publishes the new count
+      if ((match >> lane) == 1ull) cnt[wv * E + e] = old + __popcll(match);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    const int c0 = cnt[e], c1 = cnt[E + e], c2 = cnt[2 * E + e], c3 = cnt[3 * E + e];
+    cnt[e] = 0;
+    cnt[E + e] = c0;
+    cnt[2 * E + e] = c0 + c1;
+    cnt[3 * E + e] = c0 + c1 + c2;
+    chunk_counts[(size_t)chunk * E + e] = c0 + c1 + c2 + c3;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kMaxSlicesPerWave; ++s) {
+    if (eid[s] >= 0) {
+      const int al = (wv * spw + s) * 64 + lane;
+      local_rank[(size_t)t0 * k + al] = cnt[wv * E + eid[s]] + rank[s];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Block-wide exclusive scan over kScanThreads values (one per thread).
+__device__ int block_exclusive_scan(int v, int* scratch /* >= kScanThreads/64 + 1 ints */,
+                                    int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) scratch[wv] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < kScanThreads / 64; ++i) {
+      const int x = scratch[i];
+      scratch[i] = run;
+      run += x;
+    }
+    scratch[kScanThreads / 64] = run;
+  }
+  __syncthreads();
+  const int r = scratch[wv] + incl - v;
+  *total = scratch[kScanThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
+    int32_t* __restrict__ chunk_counts, int nchunks, int E, int BM, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks) {
+  __shared__ int part[kScanThreads];
+  __shared__ int offs_s[MOEQ4_MAX_EXPERTS + 1];
+  __shared__ int boffs_s[MOEQ4_MAX_EXPERTS + 1];
+  __shared__ int scratch[kScanThreads / 64 + 1];
+  const int tid = threadIdx.x;
+
+  // ---- per expert, exclusive scan over chunks (S threads per expert)
+  const int S = kScanThreads / E;  // >= 1 since E <= 1024
+  const int e = tid % E, s = tid / E;
+  const bool act = s < S;
+  const int cpc = (nchunks + S - 1) / S;
+  const int c_lo = min(nchunks, s * cpc), c_hi = min(nchunks, (s + 1) * cpc);
+  int psum = 0;
+  if (act)
+    for (int c = c_lo; c < c_hi; ++c) psum += chunk_counts[(size_t)c * E + e];
+  part[tid] = act ? psum : 0;
+  __syncthreads();
+  int cnt_e = 0;
+  if (tid < E) {
+    int run = 0;
+    for (int i = 0; i < S; ++i) {
+      const int x = part[i * E + tid];
+      part[i * E + tid] = run;
+      run += x;
+    }
+    cnt_e = run;
+  }
+  __syncthreads();
+  if (act) {
+    int run = part[tid];
+    for (int c = c_lo; c < c_hi; ++c) {
+      const int x = chunk_counts[(size_t)c * E + e];
+      chunk_counts[(size_t)c * E + e] = run;
+      run += x;
+    }
+  }
+
+  // ---- counts, offsets, block offsets
+  int total;
+  const int off = block_exclusive_scan(tid < E ? cnt_e : 0, scratch, &total);
+  const int nb = tid < E ? (cnt_e + BM - 1) / BM : 0;
+  int nb_total;
+  const int boff = block_exclusive_scan(nb, scratch, &nb_total);
+  if (tid < E) {
+    counts[tid] = cnt_e;
+    offsets[tid] = off;
+    offs_s[tid] = off;
+    boffs_s[tid] = boff;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    offs_s[E] = total;
+    boffs_s[E] = nb_total;
+    *num_blocks = nb_total;
+  }
+  __syncthreads();
+
+  // ---- block map: entry b belongs to the expert e with boffs[e] <= b < boffs[e+1]
+  for (int b = tid; b < nb_total; b += kScanThreads) {
+    int lo = 0, hi = E;  // invariant: boffs_s[lo] <= b < boffs_s[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (boffs_s[mid] <= b) lo = mid; else hi = mid;
+    }
+    const int i = b - boffs_s[lo];
+    const int cnt = offs_s[lo + 1] - offs_s[lo];
+    blocks[4 * (size_t)b + 0] = lo;
+    blocks[4 * (size_t)b + 1] = offs_s[lo] + i * BM;
+    blocks[4 * (size_t)b + 2] = min(BM, cnt - i * BM);
+    blocks[4 * (size_t)b + 3] = i;
+  }
+}
+
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, int A, int E, int k,
+                                                 int tpc, const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ chunk_base,
+                                                 const int32_t* __restrict__ local_rank,
+                                                 int32_t* __restrict__ perm,
+                                                 int32_t* __restrict__ inv_perm) {
+  const int a = blockIdx.x * 256 + threadIdx.x;
+  if (a >= A) return;
+  const int e = ids[a];
+  const int c = (a / k) / tpc;
+  const int p = offsets[e] + chunk_base[(size_t)c * E + e] + local_rank[a];
+  if (p >= 0 && p < A) perm[p] = a;
+  inv_perm[a] = p;
+}
+
+// ----------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+RoutePlan route_plan(int T, int E, int k) {
+  RoutePlan p{};
+  int tpc = (T + 255) / 256;
+  tpc = ((tpc + 3) / 4) * 4;
+  if (tpc < 4) tpc = 4;
+  const int cap = kChunkAssignMax / k;
+  if (tpc > cap) tpc = cap;
+  if (tpc < 1) tpc = 1;
+  p.tpc = tpc;
+  p.nchunks = T > 0 ? (T + tpc - 1) / tpc : 0;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  p.nbits = nbits;
+  p.ws_chunk_counts = 0;
+  p.ws_local_rank = align256((size_t)p.nchunks * E * sizeof(int32_t));
+  p.ws_bytes = p.ws_local_rank + align256((size_t)T * k * sizeof(int32_t));
+  return p;
+}
+
+hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E, int k, int BM,
+                        int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* inv_perm, int32_t* blocks, int32_t* num_blocks, void* workspace,
+                        hipStream_t stream) {
+  int32_t* chunk_counts = (int32_t*)((char*)workspace + plan.ws_chunk_counts);
+  int32_t* local_rank = (int32_t*)((char*)workspace + plan.ws_local_rank);
+  hipError_t err = hipSuccess;
+  if (plan.nchunks > 0) {
+    const size_t shmem = sizeof(int) * ((size_t)plan.tpc * k + 4 * (size_t)E);
+    const void* fn;
+    if (E <= 64) fn = (const void*)&k_topk_rank<1>;
+    else if (E <= 128) fn = (const void*)&k_topk_rank<2>;
+    else if (E <= 256) fn = (const void*)&k_topk_rank<4>;
+    else if (E <= 512) fn = (const void*)&k_topk_rank<8>;
+    else fn = (const void*)&k_topk_rank<16>;
+    err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T, E, k,
+                 plan.tpc, plan.nbits, ids, w, chunk_counts, local_rank);
+    if (err != hipSuccess) return err;
+  }
+  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), 0, stream, chunk_counts,
+               plan.nchunks, E, BM, counts, offsets, blocks, num_blocks);
+  if (err != hipSuccess) return err;
+  const int A = T * k;
+  if (A > 0) {
+    err = launch("k_scatter", (const void*)&k_scatter, dim3((A + 255) / 256), dim3(256), 0, stream,
+                 (const int32_t*)ids, A, E, k, plan.tpc, (const int32_t*)offsets,
+                 (const int32_t*)chunk_counts, (const int32_t*)local_rank, perm, inv_perm);
+  }
+  return err;
+}
+
+}  // namespace moeq4

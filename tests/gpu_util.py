@@ -1,0 +1,55 @@
+"""Helpers for the GPU parity tests: host <-> device copies and one call of
+each library entry point through the binding (test infrastructure)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import quantized_grouped_gemm_amd as q
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor, dtype=None) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+def gpu_route(logits: np.ndarray, k: int, block_rows: int):
+    """moe_route on the GPU; returns host copies of every output."""
+    T, E = logits.shape
+    d = dev(np.ascontiguousarray(logits, np.float32)) if T > 0 else torch.empty((0, E), device="cuda")
+    b = q.alloc_route(T, E, k, block_rows)
+    # poison the outputs so that unwritten entries are visible
+    for key in ("topk_ids", "perm", "inv_perm", "blocks", "counts", "offsets", "num_blocks"):
+        b[key].fill_(-7)
+    q.moe_route(d if T > 0 else None, T, E, k, b["block_rows"], b["topk_ids"], b["topk_w"], b["counts"],
+                b["offsets"], b["perm"], b["inv_perm"], b["blocks"], b["num_blocks"], b["workspace"],
+                b["ws_bytes"])
+    torch.cuda.synchronize()
+    A = T * k
+    nb = int(host(b["num_blocks"])[0])
+    out = dict(
+        ids=host(b["topk_ids"])[:A].reshape(T, k), w=host(b["topk_w"])[:A].reshape(T, k),
+        counts=host(b["counts"]), offsets=host(b["offsets"]), perm=host(b["perm"])[:A],
+        inv_perm=host(b["inv_perm"])[:A], num_blocks=nb,
+        blocks=host(b["blocks"]).reshape(-1, 4)[:nb], dev=b, block_rows=b["block_rows"],
+        max_blocks=b["max_blocks"])
+    return out
+
+
+def gpu_gemm(X: np.ndarray, k: int, Wq, S, B, rt_dev: dict, reps: int = 1) -> np.ndarray:
+    """moe_grouped_gemm_q4 with routing tables already on the device; Y as bf16 bits [T*k, N]."""
+    Xd, Wd, Sd, Bd = dev(X), dev(Wq), dev(S), dev(B)
+    Y = None
+    for _ in range(reps):
+        Y = q.grouped_gemm_q4(Xd, k, Wd, Sd, Bd, rt_dev, Y=Y)
+    torch.cuda.synchronize()
+    return host(Y, np.uint16)

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before enqueueing
+anything.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import quantized_grouped_gemm_amd as q
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moeq4.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"moe_route", "moe_grouped_gemm_q4", "moe_strerror"} <= set(names)
+    raw = ctypes.CDLL(q.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(q.SIGNATURES), "binding and header disagree"
+
+
+def test_strerror_covers_codes():
+    for c in range(0, -7, -1):
+        assert q.strerror(c) != "unknown status"
+    assert q.strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 16, 2), (512, 256, 8), (4096, 256, 8), (16384, 256, 8), (1, 256, 8),
+                                   (0, 16, 2), (7, 1, 1), (100, 1024, 64)])
+def test_host_helpers(T, E, k):
+    bm = q.moe_default_block_rows(T, E, k)
+    assert bm in (16, 32, 64, 128)
+    for b in (16, 32, 64, 128):
+        assert q.moe_max_blocks(T, E, k, b) == oracle.max_blocks_bound(T * k, E, b)
+    assert q.moe_max_blocks(T, E, k, 0) == q.moe_max_blocks(T, E, k, bm)
+    assert q.moe_route_workspace_bytes(T, E, k, 0) >= 4 * T * k
+
+
+def test_default_block_rows_follows_expert_load():
+    assert q.moe_default_block_rows(512, 256, 8) == 32     # ~16 rows per expert
+    assert q.moe_default_block_rows(4096, 256, 8) == 128   # ~128 rows per expert
+    assert q.moe_default_block_rows(64, 16, 2) == 16       # ~8 rows per expert
+
+
+def test_invalid_shapes_rejected():
+    L = q.lib()
+    assert L.moe_max_blocks(-1, 16, 2, 16) == q.MOEQ4_ERR_SHAPE
+    assert L.moe_max_blocks(8, 16, 17, 16) == q.MOEQ4_ERR_SHAPE        # k > E
+    assert L.moe_max_blocks(8, 16, 0, 16) == q.MOEQ4_ERR_SHAPE
+    assert L.moe_max_blocks(8, 2048, 2, 16) == q.MOEQ4_ERR_SHAPE       # E > 1024
+    assert L.moe_max_blocks(8, 128, 65, 16) == q.MOEQ4_ERR_UNSUPPORTED  # k > 64
+    assert L.moe_max_blocks(8, 16, 2, 24) == q.MOEQ4_ERR_SHAPE         # block_rows
+    assert L.moe_route_workspace_bytes(8, 16, 17, 16) == 0
+
+
+FAKE = 1 << 20   # 16-B aligned host-side stand-ins: never dereferenced, the calls fail first
+
+
+def _route(**kw):
+    a = dict(logits=FAKE, T=8, E=16, k=2, block_rows=16, topk_ids=FAKE, topk_w=FAKE, counts=FAKE,
+             offsets=FAKE, perm=FAKE, inv_perm=FAKE, blocks=FAKE, num_blocks=FAKE, workspace=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return q.lib().moe_route(*a.values())
+
+
+def test_route_validation():
+    assert _route(T=-1) == q.MOEQ4_ERR_SHAPE
+    assert _route(k=0) == q.MOEQ4_ERR_SHAPE
+    assert _route(block_rows=48) == q.MOEQ4_ERR_SHAPE
+    assert _route(logits=None) == q.MOEQ4_ERR_NULL
+    assert _route(perm=None) == q.MOEQ4_ERR_NULL
+    assert _route(num_blocks=None) == q.MOEQ4_ERR_NULL
+    assert _route(ws_bytes=0) == q.MOEQ4_ERR_WORKSPACE
+    assert _route(workspace=None) == q.MOEQ4_ERR_NULL
+    assert _route(topk_w=FAKE + 4) == q.MOEQ4_ERR_ALIGN
+
+
+def _gemm(**kw):
+    a = dict(X=FAKE, T=8, K=256, N=128, E=16, k=2, Wq=FAKE, scales=FAKE, biases=FAKE, perm=FAKE,
+             blocks=FAKE, num_blocks=FAKE, max_blocks=1000, block_rows=16, Y=FAKE, stream=None)
+    a.update(kw)
+    return q.lib().moe_grouped_gemm_q4(*a.values())
+
+
+def test_gemm_validation():
+    assert _gemm(K=96) == q.MOEQ4_ERR_SHAPE
+    assert _gemm(K=0) == q.MOEQ4_ERR_SHAPE
+    assert _gemm(N=120) == q.MOEQ4_ERR_SHAPE
+    assert _gemm(max_blocks=q.moe_max_blocks(8, 16, 2, 16) - 1) == q.MOEQ4_ERR_SHAPE
+    assert _gemm(block_rows=8) == q.MOEQ4_ERR_SHAPE
+    assert _gemm(Wq=None) == q.MOEQ4_ERR_NULL
+    assert _gemm(Y=None) == q.MOEQ4_ERR_NULL
+    assert _gemm(Y=FAKE + 2) == q.MOEQ4_ERR_ALIGN
+    assert _gemm(T=0, X=None, Y=None) == q.MOEQ4_OK     # nothing to do: no launch
+
+
+def test_single_hip_runtime_in_process():
+    # torch's HIP runtime must be the one libmoeq4 binds to (streams and
+    # pointers come from torch); two copies of libamdhip64 would not share them
+    q.lib()
+    with open("/proc/self/maps") as f:
+        paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    assert len(paths) == 1, paths

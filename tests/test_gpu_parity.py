@@ -1,0 +1,169 @@
+"""GPU parity: the HIP path against the CPU oracle on identical seeded inputs.
+
+Routing tables must match bit for bit; routing weights within 1e-6; grouped
+GEMM outputs within tol = 1e-2*rms(oracle) + 1e-3 (rounding-aware, see
+tests/parity.py).  Every call goes through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import compare_bf16
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts only to be skipped
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_util import gpu_gemm, gpu_route  # noqa: E402
+
+
+def _check_route(logits, k, bm):
+    T, E = logits.shape
+    ids, w = oracle.topk_softmax(logits, k)
+    ref = oracle.route(ids, E, bm)
+    g = gpu_route(logits, k, bm)
+    np.testing.assert_array_equal(g["ids"], ids)
+    if T:
+        assert np.abs(g["w"].astype(np.float64) - w).max() <= 1e-6
+    np.testing.assert_array_equal(g["counts"], ref["counts"])
+    np.testing.assert_array_equal(g["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(g["perm"], ref["perm"])
+    np.testing.assert_array_equal(g["inv_perm"], ref["inv_perm"])
+    assert g["num_blocks"] == ref["num_blocks"]
+    np.testing.assert_array_equal(g["blocks"], ref["blocks"])
+    assert g["num_blocks"] <= g["max_blocks"]
+    return g, ids, w, ref
+
+
+def _logits(kind, T, E, seed=0):
+    r = np.random.default_rng([seed, T, E])
+    if kind == "normal":
+        return r.standard_normal((T, E)).astype(np.float32)
+    if kind == "ties":          # few distinct values: many exact ties, and both signed zeros
+        l = r.integers(-2, 3, (T, E)).astype(np.float32)
+        l[l == 0] = np.where(r.random(int((l == 0).sum())) < 0.5, -0.0, 0.0).astype(np.float32)
+        return l
+    if kind == "hot":           # expert 3 wins every token's first slot
+        l = r.standard_normal((T, E)).astype(np.float32)
+        l[:, 3] = 50.0
+        return l
+    if kind == "constant":      # all equal: selection by expert id only
+        return np.full((T, E), 0.5, np.float32)
+    raise ValueError(kind)
+
+
+ROUTE_CASES = [
+    ("normal", 64, 16, 2), ("normal", 512, 256, 8), ("normal", 4096, 256, 8), ("normal", 1, 256, 8),
+    ("ties", 300, 256, 8), ("ties", 77, 16, 4), ("hot", 1000, 256, 8), ("hot", 50, 64, 1),
+    ("constant", 40, 32, 5), ("normal", 3, 1, 1), ("normal", 33, 8, 8), ("normal", 129, 1024, 64),
+    ("normal", 200, 300, 6), ("normal", 5, 256, 8), ("normal", 1000, 128, 3), ("normal", 2500, 512, 16),
+]
+
+
+@pytest.mark.parametrize("kind,T,E,k", ROUTE_CASES)
+@pytest.mark.parametrize("bm", [16, 128])
+def test_route_bit_exact(kind, T, E, k, bm):
+    _check_route(_logits(kind, T, E), k, bm)
+
+
+def test_route_empty_prompt():
+    g = gpu_route(np.zeros((0, 16), np.float32), 2, 16)
+    assert g["num_blocks"] == 0
+    assert np.all(g["counts"] == 0) and np.all(g["offsets"] == 0)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_route_workloads(cid):
+    w = W.WORKLOADS[cid]
+    logits = W.gen_logits(cid, w.T, w.E, 0, w.skew_alpha, w.zipf_s)
+    bm = {1: 16, 2: 32, 4: 128}[cid]
+    g, *_ = _check_route(logits, w.k, bm)
+    if cid == 4:   # the skewed workload really is skewed
+        c = g["counts"]
+        assert c.max() > 10 * c.mean() and (c < 2).mean() > 0.1
+
+
+def test_route_decode_steps():
+    w = W.WORKLOADS[5]
+    for s in range(20):
+        _check_route(W.gen_logits(5, 1, w.E, s), w.k, 16)
+
+
+# ----------------------------------------------------------- grouped GEMM --
+
+def _gemm_full(w, bm, seed_logits=None):
+    p = W.make_problem(w)
+    logits = p.logits if seed_logits is None else seed_logits
+    g, ids, _, ref = _check_route(logits, w.k, bm)
+    Y = gpu_gemm(p.X, w.k, p.Wq, p.S, p.B, g["dev"])
+    Yref = oracle.grouped_gemm_q4(p.X, w.k, p.Wq, p.S, p.B, ref["perm"], ref["offsets"])
+    ok, st = compare_bf16(Y[: w.T * w.k], Yref)
+    assert ok, st
+    return Y, g, p
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_gemm_tiny_workload(bm):
+    _gemm_full(W.WORKLOADS[1], bm)
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_gemm_ragged(bm):
+    # N = 272 leaves a partial N tile; K = 320 is five K chunks; blocks end mid sub-tile
+    _gemm_full(W.custom(31, 200, 8, 3, 320, 272), bm)
+
+
+@pytest.mark.parametrize("T,E,k,K,N,bm", [
+    (40, 1, 1, 192, 48, 16),     # dense: one expert, every token
+    (1, 16, 2, 64, 16, 16),      # one token, minimum K and N
+    (6, 4, 4, 128, 32, 128),     # k = E, T*k < BM
+    (90, 3, 2, 256, 64, 32),     # few experts, many rows each
+])
+def test_gemm_edge_shapes(T, E, k, K, N, bm):
+    _gemm_full(W.custom(32, T, E, k, K, N), bm)
+
+
+def test_gemm_hot_expert():
+    w = W.custom(33, 300, 16, 2, 256, 128)
+    _gemm_full(w, 32, seed_logits=_logits("hot", 300, 16))
+
+
+def _sampled(w, bm, nsamp, seed):
+    """Full-size run; the oracle checks a sample of rows one by one."""
+    p = W.make_problem(w)
+    g, ids, _, ref = _check_route(p.logits, w.k, bm)
+    Y = gpu_gemm(p.X, w.k, p.Wq, p.S, p.B, g["dev"])
+    r = np.random.default_rng(seed)
+    blocks = ref["blocks"]
+    pick = set(r.choice(w.T * w.k, size=nsamp, replace=False).tolist())
+    for b in blocks[r.choice(len(blocks), size=min(len(blocks), nsamp // 4), replace=False)]:
+        pick.update([int(b[1]), int(b[1] + b[2] - 1)])          # first and last row of blocks
+    pos = np.array(sorted(pick), np.int32)
+    a = ref["perm"][pos]
+    Yref = oracle.expert_rows_q4(p.X, p.Wq, p.S, p.B, a // w.k, ids.reshape(-1)[a])
+    ok, st = compare_bf16(Y[pos], Yref)
+    assert ok, st
+    return Y, g
+
+
+def test_gemm_prefill_chunk_full_size():
+    _sampled(W.WORKLOADS[2], 32, 96, 1)
+
+
+def test_gemm_skewed_full_size():
+    Y, g = _sampled(W.WORKLOADS[4], 128, 96, 2)
+    assert np.isfinite(Y.view(np.int16).astype(np.float32)).all()
+
+
+def test_gemm_deterministic():
+    w = W.custom(34, 333, 32, 4, 512, 256)
+    p = W.make_problem(w)
+    g = gpu_route(p.logits, w.k, 32)
+    Y1 = gpu_gemm(p.X, w.k, p.Wq, p.S, p.B, g["dev"])
+    Y2 = gpu_gemm(p.X, w.k, p.Wq, p.S, p.B, g["dev"], reps=3)
+    np.testing.assert_array_equal(Y1, Y2)
+    g2 = gpu_route(p.logits, w.k, 32)
+    for key in ("ids", "counts", "offsets", "perm", "inv_perm", "blocks"):
+        np.testing.assert_array_equal(g[key], g2[key])
