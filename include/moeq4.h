@@ -113,16 +113,47 @@ int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t*
               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
               int32_t* blocks, int32_t* num_blocks, void* workspace, size_t ws_bytes, void* stream);
 
+/* Tiled copy of a stack of group-wise affine 4-bit matrices, the layout the
+ * grouped GEMM streams.  It holds the same bytes as the row-major format
+ * (codes E*N*K/2 bytes, scales and biases E*N*K/64 values each), re-ordered so
+ * that one wave's load of one MFMA weight fragment is 1 KB of contiguous memory
+ * (section "Dequantize weights during matrix multiplication": the weights stay
+ * packed until they are rebuilt inside the GEMM; this only re-orders them once,
+ * at load time).  With NT = N/16 row tiles, G = K/64 groups and C = ceil(G/2)
+ * chunks of 128 K values:
+ *   codes_t:  block (e, t, c) starts at byte (e*NT + t)*8*K + c*1024.  In a full
+ *             block (group 2c+1 exists), bytes [16*l, 16*l+16) belong to lane
+ *             l = 16*q + r (q in 0..3, r in 0..15): row n = 16*t + r, first the
+ *             8 bytes of K indices 128c + 16q + [0,16), then the 8 bytes of
+ *             128c + 64 + 16q + [0,16) (same nibble order as row-major).  The
+ *             last block of an odd G holds only the first 8 bytes per lane, at
+ *             [8*l, 8*l+8).
+ *   scales_t, biases_t: the value of row 16*t + r, group g (chunk c = g/2) is at
+ *             element (e*NT + t)*16*G + 32*c + 2*r + (g - 2c) in a full chunk and
+ *             (e*NT + t)*16*G + 32*c + r in the last chunk of an odd G.
+ * In:  codes [E, N, K/2], scales [E, N, K/64], biases [E, N, K/64] (row-major).
+ * Out: codes_t, scales_t, biases_t of the same sizes; must not overlap the inputs.
+ * Sizes: E >= 1, N % 16 == 0, N >= 16, K % 64 == 0, K >= 64, E*N*K/2 < 2^31. */
+int moe_prepack_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int E,
+                   int N, int K, uint8_t* codes_t, uint16_t* scales_t, uint16_t* biases_t,
+                   void* stream);
+
 /* Grouped GEMM over group-wise affine 4-bit expert weights (section
  * "Dequantize weights during matrix multiplication").
  *
  * For every block-map entry b < *num_blocks with expert e and sorted rows
  * [r0, r0 + rows):
  *   Y[p, n] = bf16( sum_kk X[perm[p] / k, kk] * weight_e(n, kk) ),  p in [r0, r0+rows)
- * with fp32 accumulation.  Weights are rebuilt in bf16 on chip, tile by tile.
+ * with fp32 accumulation.  Weights are rebuilt on chip, tile by tile, and never
+ * written back to memory.  Blocks of up to 32 rows feed the MFMA with the codes
+ * and apply each group's scale and bias to the fp32 partial sums (the weight
+ * enters as scale*code + bias exactly); taller blocks rebuild every weight as
+ * bf16(scale*code + bias) first.  Both agree with the row-major definition
+ * within fp32 rounding of the sums and the bf16 rounding of the weights.
  *
  * In:  X        uint16 (bf16) [T, K]  token activations (rows gathered via perm).
- *      Wq, scales, biases    [E, N, K/2], [E, N, K/64], [E, N, K/64]  (format above).
+ *      codes_t, scales_t, biases_t   the experts' weights [E, N, K] in the tiled
+ *                            layout written by moe_prepack_q4.
  *      perm, blocks, num_blocks  as produced by moe_route for the same T, E, k,
  *                            block_rows.
  *      max_blocks            host bound from moe_max_blocks (sizes the grid;
@@ -133,11 +164,13 @@ int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t*
  * Sizes: T >= 0, K % 64 == 0, K >= 64, N % 16 == 0, N >= 16, 1 <= k <= E,
  *        E <= MOEQ4_MAX_EXPERTS, block_rows in {0, 16, 32, 64, 128} and equal
  *        to the value given to moe_route, max_blocks >= moe_max_blocks(T, E,
- *        k, block_rows).  Y must not overlap the inputs. */
-int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wq,
-                        const uint16_t* scales, const uint16_t* biases, const int32_t* perm,
-                        const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
-                        int block_rows, uint16_t* Y, void* stream);
+ *        k, block_rows), T*K*2 and E*N*K/2 below 2^31.  Y must not overlap the
+ *        inputs. */
+int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
+                        const uint8_t* codes_t, const uint16_t* scales_t,
+                        const uint16_t* biases_t, const int32_t* perm, const int32_t* blocks,
+                        const int32_t* num_blocks, int max_blocks, int block_rows, uint16_t* Y,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,6 +40,7 @@ SIGNATURES = {
     "moe_max_blocks": (_i, [_i, _i, _i, _i]),
     "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "moe_route": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_q4": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                  _vp, _vp]),
 }
@@ -125,11 +126,17 @@ def moe_route(logits, T, E, k, block_rows, topk_ids, topk_w, counts, offsets, pe
         _stream(stream)))
 
 
-def moe_grouped_gemm_q4(X, T, K, N, E, k, Wq, scales, biases, perm, blocks, num_blocks, max_blocks,
-                        block_rows, Y, stream=None):
+def moe_prepack_q4(codes, scales, biases, E, N, K, codes_t, scales_t, biases_t, stream=None):
+    _ok("moe_prepack_q4", lib().moe_prepack_q4(
+        _p(codes), _p(scales), _p(biases), E, N, K, _p(codes_t), _p(scales_t), _p(biases_t),
+        _stream(stream)))
+
+
+def moe_grouped_gemm_q4(X, T, K, N, E, k, codes_t, scales_t, biases_t, perm, blocks, num_blocks,
+                        max_blocks, block_rows, Y, stream=None):
     _ok("moe_grouped_gemm_q4", lib().moe_grouped_gemm_q4(
-        _p(X), T, K, N, E, k, _p(Wq), _p(scales), _p(biases), _p(perm), _p(blocks), _p(num_blocks),
-        max_blocks, block_rows, _p(Y), _stream(stream)))
+        _p(X), T, K, N, E, k, _p(codes_t), _p(scales_t), _p(biases_t), _p(perm), _p(blocks),
+        _p(num_blocks), max_blocks, block_rows, _p(Y), _stream(stream)))
 
 
 # ---------------------------------------------------------------- plumbing --
@@ -162,12 +169,22 @@ def route(logits, k: int, block_rows: int = 0, bufs=None, stream=None):
     return b
 
 
-def grouped_gemm_q4(X, k, Wq, scales, biases, rt, Y=None, stream=None):
-    """Y [T*k, N] bf16 bit patterns (int16 storage) in sorted order for routing tables ``rt``."""
+def prepack(codes, scales, biases, stream=None):
+    """Tiled copies (moe_prepack_q4) of [E, N, K/2] codes and [E, N, K/64] scales/biases."""
+    E, N, K2 = codes.shape
+    out = (torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(biases))
+    moe_prepack_q4(codes, scales, biases, E, N, 2 * K2, *out, stream)
+    return out
+
+
+def grouped_gemm_q4(X, k, packed, rt, Y=None, stream=None):
+    """Y [T*k, N] bf16 bit patterns (int16 storage) in sorted order for routing tables ``rt``;
+    ``packed`` = (codes_t, scales_t, biases_t) from prepack()."""
+    codes_t, scales_t, biases_t = packed
     T, K = X.shape
-    E, N, _ = Wq.shape
+    E, N, _ = codes_t.shape
     if Y is None:
         Y = torch.empty((max(T * k, 1), N), dtype=torch.int16, device=X.device)
-    moe_grouped_gemm_q4(X, T, K, N, E, k, Wq, scales, biases, rt["perm"], rt["blocks"], rt["num_blocks"],
-                        rt["max_blocks"], rt["block_rows"], Y, stream)
+    moe_grouped_gemm_q4(X, T, K, N, E, k, codes_t, scales_t, biases_t, rt["perm"], rt["blocks"],
+                        rt["num_blocks"], rt["max_blocks"], rt["block_rows"], Y, stream)
     return Y

@@ -104,26 +104,44 @@ int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t*
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 
-int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wq,
-                        const uint16_t* scales, const uint16_t* biases, const int32_t* perm,
-                        const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
-                        int block_rows, uint16_t* Y, void* stream) {
+int moe_prepack_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int E,
+                   int N, int K, uint8_t* codes_t, uint16_t* scales_t, uint16_t* biases_t,
+                   void* stream) {
+  if (E < 1 || N < 16 || N % 16 != 0 || K < 64 || K % 64 != 0) return MOEQ4_ERR_SHAPE;
+  if ((long long)E * N * (K / 2) >= (1LL << 31)) return MOEQ4_ERR_SHAPE;
+  if (!codes || !scales || !biases || !codes_t || !scales_t || !biases_t) return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {codes, scales, biases, codes_t, scales_t, biases_t};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOEQ4_ERR_ALIGN;
+  const hipError_t err = prepack_launch(codes, scales, biases, E, N, K, codes_t, scales_t,
+                                        biases_t, (hipStream_t)stream);
+  return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
+int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
+                        const uint8_t* codes_t, const uint16_t* scales_t,
+                        const uint16_t* biases_t, const int32_t* perm, const int32_t* blocks,
+                        const int32_t* num_blocks, int max_blocks, int block_rows, uint16_t* Y,
+                        void* stream) {
   int rc = check_routing_shape(T, E, k);
   if (rc != MOEQ4_OK) return rc;
   if (K < 64 || K % 64 != 0 || N < 16 || N % 16 != 0) return MOEQ4_ERR_SHAPE;
+  if ((long long)T * K * 2 >= (1LL << 31) || (long long)E * N * (K / 2) >= (1LL << 31))
+    return MOEQ4_ERR_SHAPE;
   const int bm = resolve_block_rows(T, E, k, block_rows);
   if (bm <= 0) return bm;
   const int bound = moe_max_blocks(T, E, k, bm);
   if (bound < 0) return bound;
   if (max_blocks < bound) return MOEQ4_ERR_SHAPE;
   if (T == 0) return MOEQ4_OK;
-  if (!X || !Wq || !scales || !biases || !perm || !blocks || !num_blocks || !Y)
+  if (!X || !codes_t || !scales_t || !biases_t || !perm || !blocks || !num_blocks || !Y)
     return MOEQ4_ERR_NULL;
-  const void* ptrs[] = {X, Wq, scales, biases, perm, blocks, num_blocks, Y};
+  const void* ptrs[] = {X, codes_t, scales_t, biases_t, perm, blocks, num_blocks, Y};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOEQ4_ERR_ALIGN;
-  const hipError_t err = gemm_q4_launch(X, T, K, N, E, k, Wq, scales, biases, perm, blocks,
-                                        num_blocks, max_blocks, bm, Y, (hipStream_t)stream);
+  const hipError_t err = gemm_q4_launch(X, T, K, N, E, k, codes_t, scales_t, biases_t, perm,
+                                        blocks, num_blocks, max_blocks, bm, Y,
+                                        (hipStream_t)stream);
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 

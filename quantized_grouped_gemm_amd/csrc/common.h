@@ -70,7 +70,7 @@ inline hipError_t launch(const char* name, const void* fn, dim3 grid, dim3 block
   return err;
 }
 
-// ---- internal entry points implemented in route.hip / gemm_q4.hip
+// ---- internal entry points implemented in route.hip / gemm_q4.hip / prepack.hip
 struct RoutePlan {
   int tpc;        // tokens per chunk (one workgroup of the top-k/rank kernel)
   int nchunks;    // ceil(T / tpc)
@@ -87,9 +87,13 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
                         int32_t* perm, int32_t* inv_perm, int32_t* blocks, int32_t* num_blocks,
                         void* workspace, hipStream_t stream);
 
-hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wq,
-                          const uint16_t* S, const uint16_t* B, const int32_t* perm,
+hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wt,
+                          const uint16_t* St, const uint16_t* Bt, const int32_t* perm,
                           const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
                           int block_rows, uint16_t* Y, hipStream_t stream);
+
+hipError_t prepack_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
+                          int E, int N, int K, uint8_t* codes_t, uint16_t* scales_t,
+                          uint16_t* biases_t, hipStream_t stream);
 
 }  // namespace moeq4

@@ -46,10 +46,44 @@ def gpu_route(logits: np.ndarray, k: int, block_rows: int):
 
 
 def gpu_gemm(X: np.ndarray, k: int, Wq, S, B, rt_dev: dict, reps: int = 1) -> np.ndarray:
-    """moe_grouped_gemm_q4 with routing tables already on the device; Y as bf16 bits [T*k, N]."""
-    Xd, Wd, Sd, Bd = dev(X), dev(Wq), dev(S), dev(B)
+    """moe_prepack_q4 + moe_grouped_gemm_q4 with routing tables already on the
+    device; Y as bf16 bits [T*k, N]."""
+    Xd = dev(X)
+    packed = q.prepack(dev(Wq), dev(S), dev(B))
     Y = None
     for _ in range(reps):
-        Y = q.grouped_gemm_q4(Xd, k, Wd, Sd, Bd, rt_dev, Y=Y)
+        Y = q.grouped_gemm_q4(Xd, k, packed, rt_dev, Y=Y)
     torch.cuda.synchronize()
     return host(Y, np.uint16)
+
+
+def tiled_layout(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray):
+    """The tiled layout of moe_prepack_q4, as documented in moeq4.h, built on the host."""
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    G, NT = K // 64, N // 16
+    C = (G + 1) // 2
+    ct = np.zeros(E * N * K2, np.uint8)
+    st = np.zeros(E * N * G, np.uint16)
+    bt = np.zeros(E * N * G, np.uint16)
+    for e in range(E):
+        for t in range(NT):
+            for c in range(C):
+                full = 2 * c + 1 < G
+                base = (e * NT + t) * 8 * K + c * 1024
+                for q_ in range(4):
+                    for r in range(16):
+                        l = 16 * q_ + r
+                        row = codes[e, 16 * t + r]
+                        first = row[c * 64 + q_ * 8: c * 64 + q_ * 8 + 8]
+                        if full:
+                            ct[base + 16 * l: base + 16 * l + 8] = first
+                            ct[base + 16 * l + 8: base + 16 * l + 16] = row[c * 64 + 32 + q_ * 8: c * 64 + 40 + q_ * 8]
+                        else:
+                            ct[base + 8 * l: base + 8 * l + 8] = first
+                for r in range(16):
+                    for g in ((2 * c, 2 * c + 1) if full else (2 * c,)):
+                        dst = (e * NT + t) * 16 * G + 32 * c + (2 * r + (g - 2 * c) if full else r)
+                        st[dst] = scales[e, 16 * t + r, g]
+                        bt[dst] = biases[e, 16 * t + r, g]
+    return ct.reshape(codes.shape), st.reshape(scales.shape), bt.reshape(biases.shape)

@@ -111,3 +111,18 @@ def test_single_hip_runtime_in_process():
     with open("/proc/self/maps") as f:
         paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
     assert len(paths) == 1, paths
+
+
+def _prepack(**kw):
+    a = dict(codes=FAKE, scales=FAKE, biases=FAKE, E=2, N=32, K=128, codes_t=FAKE, scales_t=FAKE,
+             biases_t=FAKE, stream=None)
+    a.update(kw)
+    return q.lib().moe_prepack_q4(*a.values())
+
+
+def test_prepack_validation():
+    assert _prepack(N=24) == q.MOEQ4_ERR_SHAPE
+    assert _prepack(K=96) == q.MOEQ4_ERR_SHAPE
+    assert _prepack(E=0) == q.MOEQ4_ERR_SHAPE
+    assert _prepack(codes_t=None) == q.MOEQ4_ERR_NULL
+    assert _prepack(scales=FAKE + 8) == q.MOEQ4_ERR_ALIGN

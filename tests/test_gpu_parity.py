@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU hosts only to be skipped
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from gpu_util import gpu_gemm, gpu_route  # noqa: E402
+from gpu_util import dev, gpu_gemm, gpu_route, host, tiled_layout  # noqa: E402
+import quantized_grouped_gemm_amd as q  # noqa: E402
 
 
 def _check_route(logits, k, bm):
@@ -89,6 +90,20 @@ def test_route_decode_steps():
     w = W.WORKLOADS[5]
     for s in range(20):
         _check_route(W.gen_logits(5, 1, w.E, s), w.k, 16)
+
+
+# ---------------------------------------------------------------- prepack --
+
+@pytest.mark.parametrize("E,N,K", [(3, 32, 256), (2, 48, 192), (1, 16, 64), (4, 64, 320)])
+def test_prepack_layout_bit_exact(E, N, K):
+    w = W.custom(40, 1, E, 1, K, N)
+    p = W.make_problem(w)
+    ct, st, bt = q.prepack(dev(p.Wq), dev(p.S), dev(p.B))
+    torch.cuda.synchronize()
+    rc, rs, rb = tiled_layout(p.Wq, p.S, p.B)
+    np.testing.assert_array_equal(host(ct), rc)
+    np.testing.assert_array_equal(host(st, np.uint16), rs)
+    np.testing.assert_array_equal(host(bt, np.uint16), rb)
 
 
 # ----------------------------------------------------------- grouped GEMM --
