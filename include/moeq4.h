@@ -120,17 +120,20 @@ int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t*
  * (section "Dequantize weights during matrix multiplication": the weights stay
  * packed until they are rebuilt inside the GEMM; this only re-orders them once,
  * at load time).  With NT = N/16 row tiles, G = K/64 groups and C = ceil(G/2)
- * chunks of 128 K values:
- *   codes_t:  block (e, t, c) starts at byte (e*NT + t)*8*K + c*1024.  In a full
- *             block (group 2c+1 exists), bytes [16*l, 16*l+16) belong to lane
+ * chunks of 128 K values; chunk c is full when group 2c+1 exists:
+ *   codes_t:  the bytes of (expert e, chunk c, row tile t) start at
+ *             e*N*K/2 + c*NT*1024 + t*1024 (full chunk) or t*512 (the last
+ *             chunk of an odd G), so all tiles of one expert and chunk are
+ *             adjacent.  In a full chunk, bytes [16*l, 16*l+16) belong to lane
  *             l = 16*q + r (q in 0..3, r in 0..15): row n = 16*t + r, first the
  *             8 bytes of K indices 128c + 16q + [0,16), then the 8 bytes of
- *             128c + 64 + 16q + [0,16) (same nibble order as row-major).  The
- *             last block of an odd G holds only the first 8 bytes per lane, at
- *             [8*l, 8*l+8).
+ *             128c + 64 + 16q + [0,16).  Each little-endian 32-bit word holds 8
+ *             consecutive codes c0..c7 as the nibbles (bits 4p..4p+3, p = 0..7)
+ *             c0, c2, c4, c6, c1, c3, c5, c7.  The last chunk of an odd G holds
+ *             only the first 8 bytes per lane, at [8*l, 8*l+8).
  *   scales_t, biases_t: the value of row 16*t + r, group g (chunk c = g/2) is at
- *             element (e*NT + t)*16*G + 32*c + 2*r + (g - 2c) in a full chunk and
- *             (e*NT + t)*16*G + 32*c + r in the last chunk of an odd G.
+ *             element e*N*G + 32*c*NT + 32*t + 2*r + (g - 2c) in a full chunk and
+ *             e*N*G + 32*c*NT + 16*t + r in the last chunk of an odd G.
  * In:  codes [E, N, K/2], scales [E, N, K/64], biases [E, N, K/64] (row-major).
  * Out: codes_t, scales_t, biases_t of the same sizes; must not overlap the inputs.
  * Sizes: E >= 1, N % 16 == 0, N >= 16, K % 64 == 0, K >= 64, E*N*K/2 < 2^31. */

@@ -18,7 +18,7 @@ import os
 import torch  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libmoeq4.so")
+LIB_PATH = os.environ.get("MOEQ4_LIB") or os.path.join(_PKG, "_lib", "libmoeq4.so")
 
 MOEQ4_OK = 0
 MOEQ4_ERR_NULL = -1

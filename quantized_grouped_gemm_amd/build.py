@@ -38,9 +38,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoeq4)")
 
 
+# per-file code generation options (none at present; -amdgpu-mfma-vgpr-form
+# gave wrong grouped-GEMM results in a parity case and is not used)
+EXTRA: dict = {}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    extra = [] if os.environ.get("MOEQ4_NO_EXTRA_FLAGS") else EXTRA.get(os.path.basename(src), [])
+    cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

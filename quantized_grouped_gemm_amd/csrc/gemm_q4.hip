@@ -32,18 +32,21 @@
 //      exact bf16 values 128+code (one v_and_or per two codes), and the affine
 //      part is applied once per 64-K group in fp32:
 //        sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k,
-//      with the per-row group sums of the activations taken while staging
-//      them.  Rebuilding costs ~1 VALU op per weight instead of ~3, which is
-//      what a 16-row block needs to keep up with HBM.  The weight is used
-//      unrounded (s*q + b exactly), not rounded to bf16.
+//      where the per-row group sums of the activations come from two more
+//      MFMAs against an all-ones operand.  Rebuilding costs ~1 VALU op per
+//      weight instead of ~3, which is what a 16-row block needs to keep up
+//      with HBM.  The weight is used unrounded (s*q + b exactly), not rounded
+//      to bf16.
 //
 // K slot mapping inside one MFMA: lane quarter q (lanes 16q..16q+15) supplies
-// K indices g*64 + q*16 + j*8 + [0, 8) for K-step j of group g, for A and B
-// alike (in CQ mode both operands carry the slots in the order 0,4,1,5,2,6,3,7).
+// K indices g*64 + q*16 + j*8 + [0, 8) for K-step j of group g, in natural
+// order, for A and B alike.
 // The grid is sized from the host bound max_blocks; workgroups past the
 // device-side *num_blocks exit at once, so no count goes to the host.
 #include <stdlib.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -62,43 +65,32 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// A dword of the tiled layout holds 8 consecutive codes c0..c7 with nibble p
+// (bits 4p..4p+3) holding c0,c2,c4,c6,c1,c3,c5,c7 for p = 0..7, so that
+// (dword >> 4i) & 0x000F000F is the pair (c_2i, c_2i+1) in the two 16-bit halves.
+
 // exact rebuild of 8 codes: bf16(s*q + b), natural K order
 __device__ __forceinline__ bf16x8 rebuild_dq(uint32_t wd, float s, float b) {
-  const uint32_t lo = wd & 0x0F0F0F0Fu;         // codes 0,2,4,6
-  const uint32_t hi = (wd >> 4) & 0x0F0F0F0Fu;  // codes 1,3,5,7
+  const uint32_t lo = wd & 0x0F0F0F0Fu;         // bytes: c0, c4, c1, c5
+  const uint32_t hi = (wd >> 4) & 0x0F0F0F0Fu;  // bytes: c2, c6, c3, c7
   bf16x8 v;
   v[0] = (__bf16)__builtin_fmaf((float)(lo & 0xFF), s, b);
-  v[1] = (__bf16)__builtin_fmaf((float)(hi & 0xFF), s, b);
-  v[2] = (__bf16)__builtin_fmaf((float)((lo >> 8) & 0xFF), s, b);
-  v[3] = (__bf16)__builtin_fmaf((float)((hi >> 8) & 0xFF), s, b);
-  v[4] = (__bf16)__builtin_fmaf((float)((lo >> 16) & 0xFF), s, b);
-  v[5] = (__bf16)__builtin_fmaf((float)((hi >> 16) & 0xFF), s, b);
-  v[6] = (__bf16)__builtin_fmaf((float)(lo >> 24), s, b);
+  v[1] = (__bf16)__builtin_fmaf((float)((lo >> 16) & 0xFF), s, b);
+  v[2] = (__bf16)__builtin_fmaf((float)(hi & 0xFF), s, b);
+  v[3] = (__bf16)__builtin_fmaf((float)((hi >> 16) & 0xFF), s, b);
+  v[4] = (__bf16)__builtin_fmaf((float)((lo >> 8) & 0xFF), s, b);
+  v[5] = (__bf16)__builtin_fmaf((float)(lo >> 24), s, b);
+  v[6] = (__bf16)__builtin_fmaf((float)((hi >> 8) & 0xFF), s, b);
   v[7] = (__bf16)__builtin_fmaf((float)(hi >> 24), s, b);
   return v;
 }
 
-// 8 codes as the exact bf16 values 128+q, slot order 0,4,1,5,2,6,3,7
-__device__ __forceinline__ bf16x8 rebuild_cq(uint32_t wd) {
-  const uint32_t m = 0x000F000Fu, one28 = 0x43004300u;
+// 8 codes as the exact bf16 values 128+q, natural K order; `one28` holds
+// 0x43004300 (bf16 128.0 twice) in a VGPR so each pair is one v_and_or_b32
+__device__ __forceinline__ bf16x8 rebuild_cq(uint32_t wd, uint32_t one28) {
+  const uint32_t m = 0x000F000Fu;
   return as_bf16x8((wd & m) | one28, ((wd >> 4) & m) | one28, ((wd >> 8) & m) | one28,
                    ((wd >> 12) & m) | one28);
-}
-
-// 8 activations in natural order -> slot order 0,4,1,5,2,6,3,7
-__device__ __forceinline__ uint4 to_cq_order(uint4 v) {
-  return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
-                    __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
-                    __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
-                    __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
-}
-
-__device__ __forceinline__ float sum8_bf16(uint4 v) {
-  const float a = __uint_as_float(v.x << 16) + __uint_as_float(v.x & 0xFFFF0000u);
-  const float b = __uint_as_float(v.y << 16) + __uint_as_float(v.y & 0xFFFF0000u);
-  const float c = __uint_as_float(v.z << 16) + __uint_as_float(v.z & 0xFFFF0000u);
-  const float d = __uint_as_float(v.w << 16) + __uint_as_float(v.w & 0xFFFF0000u);
-  return (a + b) + (c + d);
 }
 
 template <int NF, int XP>
@@ -120,7 +112,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
   constexpr int XP = BM * (kKC / 8) / kGemmThreads;  // 16-B activation pieces per thread per stage
   static_assert(XP >= 1 && BM * (kKC / 8) % kGemmThreads == 0, "tile");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kXRow];
-  __shared__ __attribute__((aligned(16))) float xsum[CQ ? 2 : 1][2][BM];
 
   const int blk = blockIdx.x;
   if (blk >= *num_blocks) return;
@@ -135,60 +126,79 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_wave = blockIdx.y * (kGemmWaves * NF * 16) + wave * NF * 16;
   const int G = K / kGroup;
-  const int nch = (G + 1) >> 1;
-  const bool odd_tail = (G & 1) != 0;  // last chunk holds one group only
+  const int nfull = G >> 1;            // chunks holding two groups
+  const bool odd_tail = (G & 1) != 0;  // one more chunk with a single group
   const int mfa = (rows + 15) >> 4;
   const int NT = N / 16;
+  uint32_t one28;  // kept in a VGPR: see rebuild_cq
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(one28));
+  const bf16x8 ones = as_bf16x8(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
-  // ---- buffer resources: one expert's weights; the activation matrix
-  const size_t tile_bytes = (size_t)8 * K;  // codes of 16 rows
+  // ---- buffer resources: one expert's weights (chunk-major tiled layout); the activations
   const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Wt + (size_t)e * NT * tile_bytes), (short)0, (int)(NT * tile_bytes), kBufFlags);
+      (void*)(Wt + (size_t)e * N * (K / 2)), (short)0, N * (K / 2), kBufFlags);
   const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(St + (size_t)e * NT * 16 * G), (short)0, NT * 16 * G * 2, kBufFlags);
+      (void*)(St + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
   const __amdgpu_buffer_rsrc_t bsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Bt + (size_t)e * NT * 16 * G), (short)0, NT * 16 * G * 2, kBufFlags);
+      (void*)(Bt + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
   const __amdgpu_buffer_rsrc_t xsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, T * K * 2, kBufFlags);
 
-  // fragments past N load nothing (their MFMAs and stores are skipped)
+  // Fragments past N still load (from the last tile, so every address stays
+  // inside the expert's weights) and run their MFMAs, but are not stored.
   const int nf_live = min(NF, max(0, (N - n_wave) / 16));
   const int t0 = n_wave / 16;
+  int tile[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) tile[f] = min(t0 + f, NT - 1);
 
-  // per-thread activation pieces: row offset in bytes, or -1 for rows past the block
+  // per-thread activation pieces: byte offset of (token row, 16-B column);
+  // rows past the block reuse the block's first row (loaded, never stored)
   int xoff[XP];
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int p = tid + i * kGemmThreads;
     const int r = p >> 4, col = p & 15;
-    xoff[i] = (r < rows) ? (perm[row0 + r] / k) * K * 2 + col * 16 : -1;
+    xoff[i] = (perm[row0 + (r < rows ? r : 0)] / k) * K * 2 + col * 16;
   }
 
   Stage<NF, XP> st[S];
+  // full chunk c (clamped to the last full chunk): every lane loads, no branches,
+  // so the compiler's wait counts stay exact across the ring
   auto load = [&](Stage<NF, XP>& s, int c) {
-    const bool half = odd_tail && c == nch - 1;
+    const int cl = min(c, nfull - 1);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      if (f >= nf_live) break;
-      const int soff = (t0 + f) * (int)tile_bytes + c * 1024;
-      const int goff = ((t0 + f) * 16 * G + 32 * c) * 2;
-      if (!half) {
-        s.w[f] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, lane * 16, soff, 0);
-        s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, (lane & 15) * 4, goff, 0);
-        s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, (lane & 15) * 4, goff, 0);
-      } else {
-        typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wsrc, lane * 8, soff, 0);
-        s.w[f] = u32x4{v[0], v[1], 0u, 0u};
-        s.s[f] = __builtin_amdgcn_raw_buffer_load_b16(ssrc, (lane & 15) * 2, goff, 0);
-        s.b[f] = __builtin_amdgcn_raw_buffer_load_b16(bsrc, (lane & 15) * 2, goff, 0);
-      }
+      const int soff = (cl * NT + tile[f]) * 1024;
+      const int goff = (cl * NT + tile[f]) * 64;
+      s.w[f] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, lane * 16, soff, 0);
+      s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, (lane & 15) * 4, goff, 0);
+      s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, (lane & 15) * 4, goff, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[i], cl * kKC * 2, 0);
+      s.x[i] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+  };
+  // the single-group chunk that ends an odd G
+  auto load_tail = [&](Stage<NF, XP>& s) {
+    const int c = nfull;
+    typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int soff = c * NT * 1024 + tile[f] * 512;
+      const int goff = (c * NT * 32 + tile[f] * 16) * 2;
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wsrc, lane * 8, soff, 0);
+      s.w[f] = u32x4{v[0], v[1], 0u, 0u};
+      s.s[f] = __builtin_amdgcn_raw_buffer_load_b16(ssrc, (lane & 15) * 2, goff, 0);
+      s.b[f] = __builtin_amdgcn_raw_buffer_load_b16(bsrc, (lane & 15) * 2, goff, 0);
     }
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int col = (tid + i * kGemmThreads) & 15;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (xoff[i] >= 0 && (!half || col < 8)) {
+      if (col < 8) {
         const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[i], c * kKC * 2, 0);
         v = make_uint4(r[0], r[1], r[2], r[3]);
       }
@@ -200,17 +210,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
     for (int i = 0; i < XP; ++i) {
       const int p = tid + i * kGemmThreads;
       const int r = p >> 4, col = p & 15;
-      uint4 v = s.x[i];
-      if constexpr (CQ) {
-        // group sums: the 8 pieces of (row, group) sit in 8 consecutive lanes
-        float sm = sum8_bf16(v);
-        sm += __shfl_xor(sm, 1);
-        sm += __shfl_xor(sm, 2);
-        sm += __shfl_xor(sm, 4);
-        if ((col & 7) == 0) xsum[buf][col >> 3][r] = sm;
-        v = to_cq_order(v);
-      }
-      *(uint4*)(&xs[buf][r * kXRow + col * 8]) = v;
+      *(uint4*)(&xs[buf][r * kXRow + col * 8]) = s.x[i];
     }
   };
 
@@ -220,23 +220,25 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const Stage<NF, XP>& s, bool two_groups) {
+  // MFA > 0: exactly MFA row sub-tiles (straight-line code); MFA == 0: `mfa` at run time
+  auto compute = [&](auto mfa_c, int buf, const Stage<NF, XP>& s, int ngroups) {
+    constexpr int MFA = decltype(mfa_c)::value;
+    constexpr int RMAX = MFA > 0 ? MFA : MF;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-      if (gi == 1 && !two_groups) break;
+      if (gi >= ngroups) break;
       bf16x8 bfr[NF][2];
       float sc[NF], cc[NF];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        if (f >= nf_live) break;
         const float sv = gi ? __uint_as_float(s.s[f] & 0xFFFF0000u) : __uint_as_float(s.s[f] << 16);
         const float bv = gi ? __uint_as_float(s.b[f] & 0xFFFF0000u) : __uint_as_float(s.b[f] << 16);
         const uint32_t w0 = s.w[f][2 * gi], w1 = s.w[f][2 * gi + 1];
         if constexpr (CQ) {
           sc[f] = sv;
           cc[f] = __builtin_fmaf(-128.f, sv, bv);
-          bfr[f][0] = rebuild_cq(w0);
-          bfr[f][1] = rebuild_cq(w1);
+          bfr[f][0] = rebuild_cq(w0, one28);
+          bfr[f][1] = rebuild_cq(w1, one28);
         } else {
           bfr[f][0] = rebuild_dq(w0, sv, bv);
           bfr[f][1] = rebuild_dq(w1, sv, bv);
@@ -244,62 +246,79 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
       }
       const uint16_t* xb = &xs[buf][(lane & 15) * kXRow + gi * 64 + quarter * 16];
 #pragma unroll
-      for (int r = 0; r < MF; ++r) {
-        if (r >= mfa) break;
+      for (int r = 0; r < RMAX; ++r) {
+        if (MFA == 0 && r >= mfa) break;
         const bf16x8 a0 = *(const bf16x8*)(xb + r * 16 * kXRow);
         const bf16x8 a1 = *(const bf16x8*)(xb + r * 16 * kXRow + 8);
         if constexpr (CQ) {
-          const float4 xsv = *(const float4*)(&xsum[buf][gi][r * 16 + quarter * 4]);
+          // group sums of the activation rows: an MFMA against all-ones puts
+          // sum_k x[row][k] of this lane's 4 rows into every column
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          f32x4 xsv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, zero, 0, 0, 0);
+          xsv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, xsv, 0, 0, 0);
+          f32x4 p[NF];
+#pragma unroll
+          for (int f = 0; f < NF; ++f) p[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bfr[f][0], zero, 0, 0, 0);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) p[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bfr[f][1], p[f], 0, 0, 0);
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
-            if (f >= nf_live) break;
-            f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bfr[f][0], zero, 0, 0, 0);
-            p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bfr[f][1], p, 0, 0, 0);
             f32x4 t = acc[r][f];
-            t[0] = __builtin_fmaf(xsv.x, cc[f], __builtin_fmaf(p[0], sc[f], t[0]));
-            t[1] = __builtin_fmaf(xsv.y, cc[f], __builtin_fmaf(p[1], sc[f], t[1]));
-            t[2] = __builtin_fmaf(xsv.z, cc[f], __builtin_fmaf(p[2], sc[f], t[2]));
-            t[3] = __builtin_fmaf(xsv.w, cc[f], __builtin_fmaf(p[3], sc[f], t[3]));
+            t[0] = __builtin_fmaf(xsv[0], cc[f], __builtin_fmaf(p[f][0], sc[f], t[0]));
+            t[1] = __builtin_fmaf(xsv[1], cc[f], __builtin_fmaf(p[f][1], sc[f], t[1]));
+            t[2] = __builtin_fmaf(xsv[2], cc[f], __builtin_fmaf(p[f][2], sc[f], t[2]));
+            t[3] = __builtin_fmaf(xsv[3], cc[f], __builtin_fmaf(p[f][3], sc[f], t[3]));
             acc[r][f] = t;
           }
         } else {
 #pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            if (f >= nf_live) break;
+          for (int f = 0; f < NF; ++f)
             acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bfr[f][0], acc[r][f], 0, 0, 0);
-          }
 #pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            if (f >= nf_live) break;
+          for (int f = 0; f < NF; ++f)
             acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bfr[f][1], acc[r][f], 0, 0, 0);
-          }
         }
       }
     }
   };
 
-  // ---- pipeline.  Chunk c is loaded into register stage c % S at iteration
-  // c - (S-1); its activations go to LDS buffer c & 1 at iteration c - 1 and
-  // its MFMAs run at iteration c.  Loads complete in issue order, so the
-  // activation wait at iteration c - 1 only covers loads issued S-2
-  // iterations earlier, never the newer prefetches.
+  // ---- pipeline over the full chunks.  Chunk c is loaded into register
+  // stage c % S at iteration c - (S-1); its activations go to LDS buffer c & 1
+  // at iteration c - 1 and its MFMAs run at iteration c.  Loads complete in
+  // issue order, so the activation wait at iteration c - 1 only covers loads
+  // issued S-2 iterations earlier, never the newer prefetches.  Iterations past
+  // the last chunk (when S does not divide it) reload the last chunk and skip
+  // the MFMAs.
+  auto run = [&](auto mfa_c) {
+    if (nfull > 0) {
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nch) load(st[s], s);
-  store_x(st[0], 0);
-  __syncthreads();
-
-  for (int c0 = 0; c0 < nch; c0 += S) {
-#pragma unroll
-    for (int u = 0; u < S; ++u) {
-      const int c = c0 + u;
-      if (c >= nch) break;
-      if (c + S - 1 < nch) load(st[(u + S - 1) % S], c + S - 1);
-      if (c + 1 < nch) store_x(st[(u + 1) % S], (c + 1) & 1);
-      compute(c & 1, st[u], !(odd_tail && c == nch - 1));
+      for (int s = 0; s < S - 1; ++s) load(st[s], s);
+      store_x(st[0], 0);
       __syncthreads();
+      for (int c0 = 0; c0 < nfull; c0 += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+          const int c = c0 + u;
+          load(st[(u + S - 1) % S], c + S - 1);
+          store_x(st[(u + 1) % S], (c + 1) & 1);
+          if (c < nfull) compute(mfa_c, c & 1, st[u], 2);
+          __syncthreads();
+        }
+      }
     }
+    if (odd_tail) {
+      load_tail(st[0]);
+      store_x(st[0], 0);
+      __syncthreads();
+      compute(mfa_c, 0, st[0], 1);
+    }
+  };
+  // blocks of up to 32 rows: one copy of the loop per filled sub-tile count
+  if constexpr (MF <= 2) {
+    if (mfa == MF) run(std::integral_constant<int, MF>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 0>{});
   }
 
   // ---- epilogue: lane holds rows 4*quarter + i of column lane&15 of each fragment

@@ -6,9 +6,23 @@
 
 namespace moeq4 {
 
+// Row-major bytes hold codes (2i, 2i+1) in (low, high) nibble of byte i.  The
+// tiled dword of 8 codes c0..c7 holds c0,c2,c4,c6,c1,c3,c5,c7 in nibbles 0..7.
+__device__ __forceinline__ uint32_t tile_nibbles(uint32_t x) {
+  const uint32_t lo = x & 0x0F0F0F0Fu;         // bytes: c0, c2, c4, c6
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // bytes: c1, c3, c5, c7
+  const uint32_t nlo = (lo & 0xFu) | ((lo >> 4) & 0xF0u) | ((lo >> 8) & 0xF00u) | ((lo >> 12) & 0xF000u);
+  const uint32_t nhi = (hi & 0xFu) | ((hi >> 4) & 0xF0u) | ((hi >> 8) & 0xF00u) | ((hi >> 12) & 0xF000u);
+  return nlo | (nhi << 16);
+}
+
+__device__ __forceinline__ uint2 tile_nibbles2(uint2 v) {
+  return make_uint2(tile_nibbles(v.x), tile_nibbles(v.y));
+}
+
 // one thread per (matrix row, chunk, K quarter): 8 + 8 bytes of codes
 __global__ __launch_bounds__(256) void k_prepack_codes(const uint8_t* __restrict__ codes, int rows_total,
-                                                       int K, uint8_t* __restrict__ codes_t) {
+                                                       int N, int K, uint8_t* __restrict__ codes_t) {
   const int G = K / kGroup, C = (G + 1) / 2;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long total = (long long)rows_total * C * 4;
@@ -16,24 +30,27 @@ __global__ __launch_bounds__(256) void k_prepack_codes(const uint8_t* __restrict
   const int q = (int)(idx & 3);
   const int c = (int)((idx >> 2) % C);
   const long long row = (idx >> 2) / C;  // e*N + n
-  const long long tile = row >> 4;       // e*NT + t
+  const int NT = N / 16;
+  const long long e = row / N;
+  const int t = (int)((row % N) >> 4);
   const int r = (int)(row & 15);
   const int l = 16 * q + r;
   const uint8_t* src = codes + row * (K / 2) + c * 64 + q * 8;
   const bool full = 2 * c + 1 < G;
-  uint8_t* blk = codes_t + tile * 8LL * K + (long long)c * 1024;
+  // chunk-major: the NT tiles of one (expert, chunk) are adjacent
+  uint8_t* blk = codes_t + e * (long long)N * (K / 2) + (long long)c * NT * 1024 + (long long)t * (full ? 1024 : 512);
   if (full) {
-    *(uint2*)(blk + 16 * l) = *(const uint2*)src;
-    *(uint2*)(blk + 16 * l + 8) = *(const uint2*)(src + 32);
+    *(uint2*)(blk + 16 * l) = tile_nibbles2(*(const uint2*)src);
+    *(uint2*)(blk + 16 * l + 8) = tile_nibbles2(*(const uint2*)(src + 32));
   } else {
-    *(uint2*)(blk + 8 * l) = *(const uint2*)src;
+    *(uint2*)(blk + 8 * l) = tile_nibbles2(*(const uint2*)src);
   }
 }
 
 // one thread per (matrix row, group): scale and bias
 __global__ __launch_bounds__(256) void k_prepack_scales(const uint16_t* __restrict__ scales,
                                                         const uint16_t* __restrict__ biases,
-                                                        int rows_total, int K,
+                                                        int rows_total, int N, int K,
                                                         uint16_t* __restrict__ scales_t,
                                                         uint16_t* __restrict__ biases_t) {
   const int G = K / kGroup;
@@ -41,11 +58,13 @@ __global__ __launch_bounds__(256) void k_prepack_scales(const uint16_t* __restri
   if (idx >= (long long)rows_total * G) return;
   const int g = (int)(idx % G);
   const long long row = idx / G;
-  const long long tile = row >> 4;
+  const int NT = N / 16;
+  const long long e = row / N;
+  const int t = (int)((row % N) >> 4);
   const int r = (int)(row & 15);
   const int c = g >> 1;
   const bool full = 2 * c + 1 < G;
-  const long long dst = tile * 16LL * G + 32LL * c + (full ? 2 * r + (g & 1) : r);
+  const long long dst = e * (long long)N * G + 32LL * c * NT + (full ? 32LL * t + 2 * r + (g & 1) : 16LL * t + r);
   scales_t[dst] = scales[idx];
   biases_t[dst] = biases[idx];
 }
@@ -58,11 +77,11 @@ hipError_t prepack_launch(const uint8_t* codes, const uint16_t* scales, const ui
   const long long n1 = rows * C * 4, n2 = rows * G;
   hipError_t err = launch("k_prepack_codes", (const void*)&k_prepack_codes,
                           dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, stream, codes, (int)rows,
-                          K, codes_t);
+                          N, K, codes_t);
   if (err != hipSuccess) return err;
   return launch("k_prepack_scales", (const void*)&k_prepack_scales,
                 dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, stream, scales, biases, (int)rows,
-                K, scales_t, biases_t);
+                N, K, scales_t, biases_t);
 }
 
 }  // namespace moeq4

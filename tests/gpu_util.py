@@ -57,6 +57,20 @@ def gpu_gemm(X: np.ndarray, k: int, Wq, S, B, rt_dev: dict, reps: int = 1) -> np
     return host(Y, np.uint16)
 
 
+def _nibble_order(b8: np.ndarray) -> np.ndarray:
+    """8 row-major bytes (16 codes) -> the tiled word order: per 32-bit word, codes
+    c0..c7 stored as nibbles c0,c2,c4,c6,c1,c3,c5,c7."""
+    out = np.zeros(8, np.uint8)
+    for w in range(2):
+        codes = []
+        for byte in b8[4 * w: 4 * w + 4]:
+            codes += [int(byte) & 15, int(byte) >> 4]
+        nib = [codes[i] for i in (0, 2, 4, 6, 1, 3, 5, 7)]
+        for j in range(4):
+            out[4 * w + j] = nib[2 * j] | (nib[2 * j + 1] << 4)
+    return out
+
+
 def tiled_layout(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray):
     """The tiled layout of moe_prepack_q4, as documented in moeq4.h, built on the host."""
     E, N, K2 = codes.shape
@@ -70,20 +84,21 @@ def tiled_layout(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray):
         for t in range(NT):
             for c in range(C):
                 full = 2 * c + 1 < G
-                base = (e * NT + t) * 8 * K + c * 1024
+                base = e * N * K2 + c * NT * 1024 + t * (1024 if full else 512)
                 for q_ in range(4):
                     for r in range(16):
                         l = 16 * q_ + r
                         row = codes[e, 16 * t + r]
-                        first = row[c * 64 + q_ * 8: c * 64 + q_ * 8 + 8]
+                        first = _nibble_order(row[c * 64 + q_ * 8: c * 64 + q_ * 8 + 8])
                         if full:
                             ct[base + 16 * l: base + 16 * l + 8] = first
-                            ct[base + 16 * l + 8: base + 16 * l + 16] = row[c * 64 + 32 + q_ * 8: c * 64 + 40 + q_ * 8]
+                            ct[base + 16 * l + 8: base + 16 * l + 16] = _nibble_order(
+                                row[c * 64 + 32 + q_ * 8: c * 64 + 40 + q_ * 8])
                         else:
                             ct[base + 8 * l: base + 8 * l + 8] = first
                 for r in range(16):
                     for g in ((2 * c, 2 * c + 1) if full else (2 * c,)):
-                        dst = (e * NT + t) * 16 * G + 32 * c + (2 * r + (g - 2 * c) if full else r)
+                        dst = e * N * G + 32 * c * NT + (32 * t + 2 * r + (g - 2 * c) if full else 16 * t + r)
                         st[dst] = scales[e, 16 * t + r, g]
                         bt[dst] = biases[e, 16 * t + r, g]
     return ct.reshape(codes.shape), st.reshape(scales.shape), bt.reshape(biases.shape)
