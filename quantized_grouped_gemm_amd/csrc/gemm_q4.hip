@@ -101,20 +101,33 @@ struct Stage {
   uint4 x[XP];      // activation pieces
 };
 
-template <int BM, int NF, bool CQ, int S>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
+constexpr int kXcds = 8;  // MI355X: workgroup i of a launch runs on XCD i % 8
+
+template <int BM, int NF, bool CQ, int S, int WAUX, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(
     const uint16_t* __restrict__ X, int T, int K, int N, int E, int A, int k,
     const uint8_t* __restrict__ Wt, const uint16_t* __restrict__ St,
     const uint16_t* __restrict__ Bt, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ num_blocks,
     uint16_t* __restrict__ Y) {
   constexpr int MF = BM / 16;
-  constexpr int XP = BM * (kKC / 8) / kGemmThreads;  // 16-B activation pieces per thread per stage
-  static_assert(XP >= 1 && BM * (kKC / 8) % kGemmThreads == 0, "tile");
+  constexpr int NTHR = WAVES * 64;
+  constexpr int XP = (BM * (kKC / 8) + NTHR - 1) / NTHR;  // 16-B activation pieces per thread per stage
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kXRow];
 
-  const int blk = blockIdx.x;
-  if (blk >= *num_blocks) return;
+  // XCD-aware task order: the workgroups of one XCD take consecutive tasks
+  // (block, N tile), so the N tiles of a block -- which gather the same
+  // activation rows -- and the blocks of one expert -- which stream the same
+  // weights -- share that XCD's L2.  Tasks past the device-side block count exit.
+  const int ntiles = (N + WAVES * NF * 16 - 1) / (WAVES * NF * 16);
+  const int total = *num_blocks * ntiles;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int task = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (task >= total) return;
+  const int blk = task / ntiles;
+  const int ntile = task - blk * ntiles;
   const int e = blocks[4 * blk + 0];
   const int row0 = blocks[4 * blk + 1];
   const int rows = min(blocks[4 * blk + 2], BM);
@@ -124,7 +137,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
   const int lane = tid & 63;
   const int quarter = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_wave = blockIdx.y * (kGemmWaves * NF * 16) + wave * NF * 16;
+  const int n_wave = ntile * (WAVES * NF * 16) + wave * NF * 16;
   const int G = K / kGroup;
   const int nfull = G >> 1;            // chunks holding two groups
   const bool odd_tail = (G & 1) != 0;  // one more chunk with a single group
@@ -152,14 +165,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
 #pragma unroll
   for (int f = 0; f < NF; ++f) tile[f] = min(t0 + f, NT - 1);
 
-  // per-thread activation pieces: byte offset of (token row, 16-B column);
-  // rows past the block reuse the block's first row (loaded, never stored)
+  // per-thread activation pieces: byte offset of (token row, 16-B column).
+  // Rows past the block get an offset past the buffer: the buffer load returns
+  // zeros without touching memory.
+  const int x_oob = T * K * 2;
   int xoff[XP];
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
-    const int p = tid + i * kGemmThreads;
+    const int p = tid + i * NTHR;
     const int r = p >> 4, col = p & 15;
-    xoff[i] = (perm[row0 + (r < rows ? r : 0)] / k) * K * 2 + col * 16;
+    xoff[i] = (r < rows && p < BM * 16) ? (perm[row0 + r] / k) * K * 2 + col * 16 : x_oob;
   }
 
   Stage<NF, XP> st[S];
@@ -171,9 +186,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
     for (int f = 0; f < NF; ++f) {
       const int soff = (cl * NT + tile[f]) * 1024;
       const int goff = (cl * NT + tile[f]) * 64;
-      s.w[f] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, lane * 16, soff, 0);
-      s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, (lane & 15) * 4, goff, 0);
-      s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, (lane & 15) * 4, goff, 0);
+      s.w[f] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, lane * 16, soff, WAUX);
+      s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, (lane & 15) * 4, goff, WAUX);
+      s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, (lane & 15) * 4, goff, WAUX);
     }
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -196,7 +211,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
     }
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      const int col = (tid + i * kGemmThreads) & 15;
+      const int col = (tid + i * NTHR) & 15;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (col < 8) {
         const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[i], c * kKC * 2, 0);
@@ -208,9 +223,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
   auto store_x = [&](const Stage<NF, XP>& s, int buf) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
-      const int p = tid + i * kGemmThreads;
+      const int p = tid + i * NTHR;
       const int r = p >> 4, col = p & 15;
-      *(uint4*)(&xs[buf][r * kXRow + col * 8]) = s.x[i];
+      if (XP * NTHR == BM * 16 || p < BM * 16) *(uint4*)(&xs[buf][r * kXRow + col * 8]) = s.x[i];
     }
   };
 
@@ -338,36 +353,253 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tall blocks (64/128 rows): bf16 MFMA 32x32x16, exact bf16 rebuild (DQ).
+//
+// One wave covers every row of the block (BM/32 row tiles) and NF32 tiles of
+// 32 columns, so each rebuilt weight feeds BM/32 MFMAs, and the 32x32x16 MFMA
+// keeps the matrix cores busy with only a few independent accumulators.  The
+// weights come from the same tiled layout: for 32-column tile u, lane
+// l = 32h + n (h in 0..1, n in 0..31) loads the two 16-byte quarter slices
+// q = 2h and 2h+1 of column n%16 of 16-row tile 2u + n/16, i.e. 32 codes of
+// K indices 32h + [0,32) in each of the chunk's two groups.  K-step s4 of group
+// g then takes K indices g*64 + 32h + 8*s4 + [0,8) from lane half h, for both
+// operands, so every K-step stays inside one scale group.
+template <int BM, int NF32, int S, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(
+    const uint16_t* __restrict__ X, int T, int K, int N, int E, int A, int k,
+    const uint8_t* __restrict__ Wt, const uint16_t* __restrict__ St,
+    const uint16_t* __restrict__ Bt, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ num_blocks,
+    uint16_t* __restrict__ Y) {
+  constexpr int MF32 = BM / 32;
+  constexpr int NTHR = WAVES * 64;
+  constexpr int XP = (BM * (kKC / 8) + NTHR - 1) / NTHR;
+  constexpr int TILE_N = WAVES * NF32 * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kXRow];
+
+  const int ntiles = (N + TILE_N - 1) / TILE_N;
+  const int total = *num_blocks * ntiles;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int task = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (task >= total) return;
+  const int blk = task / ntiles;
+  const int ntile = task - blk * ntiles;
+  const int e = blocks[4 * blk + 0];
+  const int row0 = blocks[4 * blk + 1];
+  const int rows = min(blocks[4 * blk + 2], BM);
+  if (e < 0 || e >= E || row0 < 0 || rows <= 0 || row0 + rows > A) return;  // malformed entry
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;   // K half inside a K-step
+  const int col = lane & 31;    // column inside a 32-column tile
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_wave = ntile * TILE_N + wave * NF32 * 32;
+  const int G = K / kGroup;
+  const int nfull = G >> 1;
+  const bool odd_tail = (G & 1) != 0;
+  const int mfa = (rows + 31) >> 5;  // row tiles holding rows
+  const int NT = N / 16;
+
+  const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Wt + (size_t)e * N * (K / 2)), (short)0, N * (K / 2), kBufFlags);
+  const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(St + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t bsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Bt + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t xsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, T * K * 2, kBufFlags);
+
+  // this lane's 16-row tile per 32-column tile (clamped inside the expert: columns
+  // past N load the last tile and are never stored) and its row inside that tile
+  int tile16[NF32];
+#pragma unroll
+  for (int f = 0; f < NF32; ++f) tile16[f] = min((n_wave + f * 32 + col) >> 4, NT - 1);
+  const int r16 = col & 15;
+  const int nf_live = min(NF32, max(0, (N - n_wave + 31) / 32));
+
+  const int x_oob = T * K * 2;  // rows past the block: the load returns zeros, no traffic
+  int xoff[XP];
+#pragma unroll
+  for (int i = 0; i < XP; ++i) {
+    const int p = tid + i * NTHR;
+    const int r = p >> 4, c16 = p & 15;
+    xoff[i] = (r < rows && p < BM * 16) ? (perm[row0 + r] / k) * K * 2 + c16 * 16 : x_oob;
+  }
+
+  struct St32 {
+    u32x4 w[NF32][2];   // quarter slices 2h and 2h+1
+    uint32_t s[NF32], b[NF32];
+    uint4 x[XP];
+  };
+  St32 st[S];
+  auto load = [&](St32& s, int c) {
+    const int cl = min(c, nfull - 1);
+#pragma unroll
+    for (int f = 0; f < NF32; ++f) {
+      const int base = (cl * NT + tile16[f]) * 1024 + r16 * 16;
+      s.w[f][0] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, base + (2 * half) * 256, 0, 0);
+      s.w[f][1] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, base + (2 * half + 1) * 256, 0, 0);
+      const int gbase = ((cl * NT + tile16[f]) * 32 + 2 * r16) * 2;
+      s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, gbase, 0, 0);
+      s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, gbase, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[i], cl * kKC * 2, 0);
+      s.x[i] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+  };
+  auto load_tail = [&](St32& s) {
+    const int c = nfull;
+    typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+#pragma unroll
+    for (int f = 0; f < NF32; ++f) {
+      const int base = c * NT * 1024 + tile16[f] * 512 + r16 * 8;
+      const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(wsrc, base + (2 * half) * 128, 0, 0);
+      const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(wsrc, base + (2 * half + 1) * 128, 0, 0);
+      s.w[f][0] = u32x4{v0[0], v0[1], 0u, 0u};
+      s.w[f][1] = u32x4{v1[0], v1[1], 0u, 0u};
+      const int gbase = (c * NT * 32 + tile16[f] * 16 + r16) * 2;
+      s.s[f] = __builtin_amdgcn_raw_buffer_load_b16(ssrc, gbase, 0, 0);
+      s.b[f] = __builtin_amdgcn_raw_buffer_load_b16(bsrc, gbase, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int c16 = (tid + i * NTHR) & 15;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (c16 < 8) {
+        const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[i], c * kKC * 2, 0);
+        v = make_uint4(r[0], r[1], r[2], r[3]);
+      }
+      s.x[i] = v;
+    }
+  };
+  auto store_x = [&](const St32& s, int buf) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int p = tid + i * NTHR;
+      if (XP * NTHR == BM * 16 || p < BM * 16) *(uint4*)(&xs[buf][(p >> 4) * kXRow + (p & 15) * 8]) = s.x[i];
+    }
+  };
+
+  f32x16 acc[MF32][NF32];
+#pragma unroll
+  for (int r = 0; r < MF32; ++r)
+#pragma unroll
+    for (int f = 0; f < NF32; ++f)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][f][i] = 0.f;
+
+  auto compute = [&](int buf, const St32& s, int ngroups) {
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      if (gi >= ngroups) break;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        // K indices gi*64 + 32*half + 8*s4 + [0,8): slice (2*half + s4/2), dword 2*gi + s4%2
+        bf16x8 bfr[NF32];
+#pragma unroll
+        for (int f = 0; f < NF32; ++f) {
+          const float sv = gi ? __uint_as_float(s.s[f] & 0xFFFF0000u) : __uint_as_float(s.s[f] << 16);
+          const float bv = gi ? __uint_as_float(s.b[f] & 0xFFFF0000u) : __uint_as_float(s.b[f] << 16);
+          bfr[f] = rebuild_dq(s.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
+        }
+        const uint16_t* xb = &xs[buf][col * kXRow + gi * 64 + half * 32 + s4 * 8];
+#pragma unroll
+        for (int r = 0; r < MF32; ++r) {
+          if (r >= mfa) break;
+          const bf16x8 a = *(const bf16x8*)(xb + r * 32 * kXRow);
+#pragma unroll
+          for (int f = 0; f < NF32; ++f)
+            acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[f], acc[r][f], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nfull > 0) {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) load(st[s], s);
+    store_x(st[0], 0);
+    __syncthreads();
+    for (int c0 = 0; c0 < nfull; c0 += S) {
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        const int c = c0 + u;
+        load(st[(u + S - 1) % S], c + S - 1);
+        store_x(st[(u + 1) % S], (c + 1) & 1);
+        if (c < nfull) compute(c & 1, st[u], 2);
+        __syncthreads();
+      }
+    }
+  }
+  if (odd_tail) {
+    load_tail(st[0]);
+    store_x(st[0], 0);
+    __syncthreads();
+    compute(0, st[0], 1);
+  }
+
+  // epilogue: 32x32 accumulator layout -- lane holds column lane&31 and rows
+  // 8*(i/4) + 4*half + i%4 (i = 0..15) of each tile
+#pragma unroll
+  for (int r = 0; r < MF32; ++r) {
+    if (r >= mfa) break;
+#pragma unroll
+    for (int f = 0; f < NF32; ++f) {
+      if (f >= nf_live) break;
+      const int n = n_wave + f * 32 + col;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = r * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (row < rows) Y[(size_t)(row0 + row) * N + n] = f32_to_bf16_bits(acc[r][f][i]);
+      }
+    }
+  }
+}
+
 namespace {
 
 struct GemmVariant {
   const char* name;
-  int bm, nf;
+  int bm;
+  int tile_n;  // columns per workgroup
+  int waves;   // waves per workgroup
   const void* fn;
 };
 
-#define MOEQ4_GEMM_VARIANT(BM, NF, CQ, S) \
-  {"bm" #BM "_nf" #NF "_" #CQ "_s" #S, BM, NF, (const void*)&k_gemm_q4<BM, NF, CQ, S>}
+#define MOEQ4_GEMM_VARIANT(BM, NF, CQ, S, WAUX, WAVES)                          \
+  {"bm" #BM "_nf" #NF "_" #CQ "_s" #S "_a" #WAUX "_w" #WAVES, BM, WAVES * NF * 16, WAVES, \
+   (const void*)&k_gemm_q4<BM, NF, CQ, S, WAUX, WAVES>}
+#define MOEQ4_GEMM_W32(BM, NF32, S, WAVES)                                      \
+  {"w32_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, WAVES * NF32 * 32, WAVES,   \
+   (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES>}
 
-// The first entry of each block height is its default.
+// The first entry of each block height is its default.  WAUX is the cache
+// policy of the weight loads (2 = non-temporal: streamed weights do not
+// evict the activation rows from L2).
 const GemmVariant kVariants[] = {
-    MOEQ4_GEMM_VARIANT(16, 2, true, 4),
-    MOEQ4_GEMM_VARIANT(32, 2, true, 4),
-    MOEQ4_GEMM_VARIANT(64, 4, false, 3),
-    MOEQ4_GEMM_VARIANT(128, 4, false, 2),
-    MOEQ4_GEMM_VARIANT(16, 4, true, 4),
-    MOEQ4_GEMM_VARIANT(16, 1, true, 4),
-    MOEQ4_GEMM_VARIANT(32, 4, true, 3),
-    MOEQ4_GEMM_VARIANT(32, 4, true, 4),
-    MOEQ4_GEMM_VARIANT(32, 1, true, 4),
-    MOEQ4_GEMM_VARIANT(32, 2, true, 3),
-    MOEQ4_GEMM_VARIANT(32, 2, false, 4),
-    MOEQ4_GEMM_VARIANT(64, 2, true, 3),
-    MOEQ4_GEMM_VARIANT(64, 4, false, 2),
-    MOEQ4_GEMM_VARIANT(128, 4, false, 3),
-    MOEQ4_GEMM_VARIANT(128, 2, false, 3),
+    // defaults (first entry of each block height), from sweeps on MI355X
+    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 8),
+    MOEQ4_GEMM_VARIANT(32, 2, true, 3, 0, 8),
+    MOEQ4_GEMM_W32(64, 2, 2, 4),
+    MOEQ4_GEMM_W32(128, 1, 2, 8),
+    // alternatives for tuning sweeps
+    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 4),
+    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 4),
+    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 8),
+    MOEQ4_GEMM_VARIANT(32, 2, true, 4, 0, 8),
+    MOEQ4_GEMM_W32(128, 2, 2, 8),
+    MOEQ4_GEMM_W32(128, 2, 2, 4),
+    MOEQ4_GEMM_W32(64, 2, 2, 8),
 };
 #undef MOEQ4_GEMM_VARIANT
+#undef MOEQ4_GEMM_W32
 
 // Tile choice by block height; MOEQ4_GEMM_VARIANT=<name> (same block height)
 // overrides it for tuning sweeps.
@@ -390,9 +622,10 @@ hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, 
   if (max_blocks <= 0) return hipSuccess;
   const GemmVariant* v = pick_variant(BM);
   if (!v) return hipErrorInvalidValue;
-  const int ntile = kGemmWaves * v->nf * 16;
-  const dim3 grid(max_blocks, (N + ntile - 1) / ntile);
-  return launch("k_gemm_q4", v->fn, grid, dim3(kGemmThreads), 0, stream, X, T, K, N, E, T * k, k,
+  const int tile_n = v->tile_n;
+  const long long tasks = (long long)max_blocks * ((N + tile_n - 1) / tile_n);
+  const dim3 grid((unsigned)((tasks + kXcds - 1) / kXcds * kXcds));
+  return launch("k_gemm_q4", v->fn, grid, dim3(v->waves * 64), 0, stream, X, T, K, N, E, T * k, k,
                 Wt, St, Bt, perm, blocks, num_blocks, Y);
 }
 
