@@ -44,6 +44,22 @@ __device__ __forceinline__ float wave_max_f32(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// wave-wide maximum of a signed int; the result is uniform (SGPR)
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, dpp_i32<0xB1>(x));
+  x = max(x, dpp_i32<0x4E>(x));
+  x = max(x, dpp_i32<0x141>(x));
+  x = max(x, dpp_i32<0x140>(x));
+  x = max(x, dpp_i32<0x142, 0xA>(x));
+  x = max(x, dpp_i32<0x143, 0xC>(x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 __device__ __forceinline__ float wave_sum_f32(float x) {
   x += dpp_f32<0xB1>(x);
   x += dpp_f32<0x4E>(x);
@@ -73,6 +89,7 @@ inline hipError_t launch(const char* name, const void* fn, dim3 grid, dim3 block
 
 // ---- internal entry points implemented in route.hip / gemm_q4.hip / prepack.hip
 struct RoutePlan {
+  int waves;      // waves per workgroup of the top-k/rank kernel
   int tpc;        // tokens per chunk (one workgroup of the top-k/rank kernel)
   int nchunks;    // ceil(T / tpc)
   int nbits;      // bits that distinguish expert ids: ceil(log2(E))

@@ -18,70 +18,99 @@
 //                    counts, offsets, block counts and their scan, block map.
 //   k_scatter        one thread per assignment: perm / inv_perm.
 // Only integer adds decide positions, so every output is deterministic.
+#include <limits.h>
+
 #include "common.h"
 
 namespace moeq4 {
 
-constexpr int kRouteThreads = 256;         // 4 waves per chunk workgroup
+constexpr int kRouteMaxThreads = 1024;     // up to 16 waves per chunk workgroup
 constexpr int kChunkAssignMax = 2048;      // assignments per chunk (LDS bound)
-constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / 4;
+constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / 4;  // with at least 4 waves
 constexpr int kScanThreads = 1024;
+constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 
 // ----------------------------------------------------------------------------
-// top-k + softmax + chunk histogram + in-chunk stable ranks
-// Lane l of a token's wave holds experts [l*VPT, (l+1)*VPT).
+// top-k + softmax + chunk histogram + in-chunk stable ranks.
+// A workgroup of NW waves handles one chunk of tpc tokens; wave w takes tokens
+// w, w+NW, ...  Lane l of a token's wave holds experts [l*VPT, (l+1)*VPT).
+// Selection compares order-preserving integer keys of the logits (with -0
+// folded into +0, so equal logits give equal keys): the wave maximum is a
+// DPP max over ints, and the lowest lane holding it has the lowest expert id.
+__device__ __forceinline__ int order_key(float v) {
+  const int u = __float_as_int(v + 0.0f);  // -0 + 0 = +0
+  return u ^ ((u >> 31) & 0x7FFFFFFF);     // monotone in v for non-NaN floats
+}
+
 template <int VPT>
-__global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
+__global__ __launch_bounds__(kRouteMaxThreads) void k_topk_rank(
     const float* __restrict__ logits, int T, int E, int k, int tpc, int nbits,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts,
     int32_t* __restrict__ local_rank) {
   extern __shared__ int smem[];
+  const int NW = blockDim.x >> 6;
   int* sids = smem;              // [tpc * k] expert ids of the chunk's assignments
-  int* cnt = smem + tpc * k;     // [4][E] per-wave counters, then per-wave bases
+  int* cnt = smem + tpc * k;     // [NW][E] per-wave counters, then per-wave bases
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int chunk = blockIdx.x;
   const int t0 = chunk * tpc;
   const int ntok = min(tpc, T - t0);
+  constexpr int kTaken = INT_MIN;  // below every finite logit's key
 
-  for (int i = threadIdx.x; i < 4 * E; i += kRouteThreads) cnt[i] = 0;
+  for (int i = threadIdx.x; i < NW * E; i += blockDim.x) cnt[i] = 0;
 
-  for (int i = wv; i < ntok; i += 4) {
-    const int t = t0 + i;
-    const float* row = logits + (size_t)t * E;
-    float v[VPT];
+  // the next token's logits are in flight while the current one is selected
+  int kn[VPT];
+  float vn[VPT];
+  auto fetch = [&](int i) {
 #pragma unroll
     for (int s = 0; s < VPT; ++s) {
       const int e = lane * VPT + s;
-      v[s] = (e < E) ? row[e] : -INFINITY;
+      vn[s] = (i < ntok && e < E) ? logits[(size_t)(t0 + i) * E + e] : 0.f;
+      kn[s] = (i < ntok && e < E) ? 0 : kTaken;
     }
+  };
+  fetch(wv);
+  for (int i = wv; i < ntok; i += NW) {
+    const int t = t0 + i;
+    int key[VPT];
+    float v[VPT];
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) {
+      v[s] = vn[s];
+      key[s] = kn[s] == kTaken ? kTaken : order_key(vn[s]);
+    }
+    fetch(i + NW);
     int my_id = 0;
     float my_v = 0.f;
     for (int j = 0; j < k; ++j) {
-      // best of this lane: larger value, lower slot on ties
-      float bv = v[0];
-      int bs = 0;
+      // best of this lane: larger key, lower slot on ties
+      int bk = key[0], bs = 0;
 #pragma unroll
       for (int s = 1; s < VPT; ++s) {
-        if (v[s] > bv) {
-          bv = v[s];
+        if (key[s] > bk) {
+          bk = key[s];
           bs = s;
         }
       }
-      const float m = wave_max_f32(bv);
-      // lowest lane holding the maximum has the lowest expert id (-0 == +0)
-      const uint64_t bal = __ballot(bv == m);
+      const int m = wave_max_i32(bk);
+      const uint64_t bal = __ballot(bk == m);
       const int wl = bal ? (__ffsll((unsigned long long)bal) - 1) : 0;
       const int ws = __shfl(bs, wl);
+      float sel_v = 0.f;
+#pragma unroll
+      for (int s = 0; s < VPT; ++s) sel_v = (s == ws) ? v[s] : sel_v;
+      sel_v = __shfl(sel_v, wl);
       if (lane == wl) {
 #pragma unroll
         for (int s = 0; s < VPT; ++s)
-          if (s == ws) v[s] = -INFINITY;
+          if (s == ws) key[s] = kTaken;
       }
       if (lane == j) {
         my_id = min(wl * VPT + ws, E - 1);  // stays in range even for non-finite input
-        my_v = m;
+        my_v = sel_v;
       }
     }
     const float v0 = __shfl(my_v, 0);
@@ -98,7 +127,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
   // ---- in-chunk histogram and stable ranks
   const int na = ntok * k;
   const int nslices = (na + 63) >> 6;
-  const int spw = (nslices + 3) >> 2;  // contiguous slices per wave
+  const int spw = (nslices + NW - 1) / NW;  // contiguous slices per wave (<= kMaxSlicesPerWave)
   const uint64_t lt = lanemask_lt();
   int rank[kMaxSlicesPerWave];
   int eid[kMaxSlicesPerWave];
@@ -127,13 +156,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    const int c0 = cnt[e], c1 = cnt[E + e], c2 = cnt[2 * E + e], c3 = cnt[3 * E + e];
-    cnt[e] = 0;
-    cnt[E + e] = c0;
-    cnt[2 * E + e] = c0 + c1;
-    cnt[3 * E + e] = c0 + c1 + c2;
-    chunk_counts[(size_t)chunk * E + e] = c0 + c1 + c2 + c3;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+    chunk_counts[(size_t)chunk * E + e] = run;
   }
   __syncthreads();
 #pragma unroll
@@ -183,15 +213,27 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
   __shared__ int scratch[kScanThreads / 64 + 1];
   const int tid = threadIdx.x;
 
-  // ---- per expert, exclusive scan over chunks (S threads per expert)
+  // ---- per expert, exclusive scan over chunks (S threads per expert).  Each
+  // thread holds its chunk counts in registers, fetched with independent loads.
   const int S = kScanThreads / E;  // >= 1 since E <= 1024
   const int e = tid % E, s = tid / E;
   const bool act = s < S;
   const int cpc = (nchunks + S - 1) / S;
   const int c_lo = min(nchunks, s * cpc), c_hi = min(nchunks, (s + 1) * cpc);
+  int vals[kScanRegs];
   int psum = 0;
-  if (act)
+  const bool in_regs = cpc <= kScanRegs;
+  if (act && in_regs) {
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) {
+      const int c = c_lo + i;
+      vals[i] = (c < c_hi) ? chunk_counts[(size_t)c * E + e] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) psum += vals[i];
+  } else if (act) {
     for (int c = c_lo; c < c_hi; ++c) psum += chunk_counts[(size_t)c * E + e];
+  }
   part[tid] = act ? psum : 0;
   __syncthreads();
   int cnt_e = 0;
@@ -205,7 +247,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
     cnt_e = run;
   }
   __syncthreads();
-  if (act) {
+  if (act && in_regs) {
+    int run = part[tid];
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) {
+      const int c = c_lo + i;
+      if (c < c_hi) chunk_counts[(size_t)c * E + e] = run;
+      run += vals[i];
+    }
+  } else if (act) {
     int run = part[tid];
     for (int c = c_lo; c < c_hi; ++c) {
       const int x = chunk_counts[(size_t)c * E + e];
@@ -271,9 +321,14 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 RoutePlan route_plan(int T, int E, int k) {
   RoutePlan p{};
+  // waves per chunk workgroup: as many as the per-wave counters [NW][E] allow in 16 KB
+  int nw = 16;
+  while (nw > 4 && nw * E > 4096) nw >>= 1;
+  p.waves = nw;
+  // about 256 chunks for long prompts; at least one token per wave
   int tpc = (T + 255) / 256;
-  tpc = ((tpc + 3) / 4) * 4;
-  if (tpc < 4) tpc = 4;
+  tpc = ((tpc + nw - 1) / nw) * nw;
+  if (tpc < nw) tpc = nw;
   const int cap = kChunkAssignMax / k;
   if (tpc > cap) tpc = cap;
   if (tpc < 1) tpc = 1;
@@ -296,14 +351,14 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
   int32_t* local_rank = (int32_t*)((char*)workspace + plan.ws_local_rank);
   hipError_t err = hipSuccess;
   if (plan.nchunks > 0) {
-    const size_t shmem = sizeof(int) * ((size_t)plan.tpc * k + 4 * (size_t)E);
+    const size_t shmem = sizeof(int) * ((size_t)plan.tpc * k + (size_t)plan.waves * E);
     const void* fn;
     if (E <= 64) fn = (const void*)&k_topk_rank<1>;
     else if (E <= 128) fn = (const void*)&k_topk_rank<2>;
     else if (E <= 256) fn = (const void*)&k_topk_rank<4>;
     else if (E <= 512) fn = (const void*)&k_topk_rank<8>;
     else fn = (const void*)&k_topk_rank<16>;
-    err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T, E, k,
+    err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(plan.waves * 64), shmem, stream, logits, T, E, k,
                  plan.tpc, plan.nbits, ids, w, chunk_counts, local_rank);
     if (err != hipSuccess) return err;
   }
