@@ -6,16 +6,21 @@ moe_grouped_gemm_q4 over the routed rows, on the prefill-chunk workload
 weights).  Inputs are seeded synthetic arrays already resident in HBM when
 the timed region starts.
 
-Prints one JSON line with the throughput of the whole step, the roofline of
-the grouped-GEMM kernel (timed with HIP events on its own stream) and the CPU
-oracle timed on the host cores.
+Cold weights: consecutive steps use different resident copies of the layer's
+weights (like consecutive MoE layers), at least 1 GiB in all, so every GEMM
+reads its weights from HBM rather than from the 256 MB Infinity Cache.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+Prints one JSON line with the throughput of the whole step, the roofline of
+the grouped-GEMM kernel (timed with HIP events on its launch stream; HBM
+traffic from the committed rocprofv3 counter summary when it matches the
+kernel source) and the CPU oracle timed on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 2|4|1]
+                    [--block-rows BM] [--layers L] [--no-cpu-baseline] [--cpu-reps R]
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -36,17 +41,10 @@ def q4_bytes(N: int, K: int) -> int:
     return N * K // 2 + (N * K // 64) * 4
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("gemm_q4.hip", "common.h"):
-        with open(os.path.join(ROOT, "quantized_grouped_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source."""
+    was taken on the current kernel source (else None)."""
+    from quantized_grouped_gemm_amd.profiling import kernel_source_hash
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -83,8 +81,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--block-rows", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0, help="resident weight copies used in turn (0: >= 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--cpu-reps", type=int, default=40)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path is single-GPU "
@@ -108,57 +107,47 @@ def main():
             a = a.view(np.int16)
         return torch.from_numpy(a).to(dev)
 
-    logits, X = d(p.logits), d(p.X)
-    packed = q.prepack(d(p.Wq), d(p.S), d(p.B))     # one-time re-tiling at load time
     T, E, k, K, N = w.T, w.E, w.k, w.K, w.N
+    # Cold weights, as in a model: consecutive MoE layers each read their own
+    # weights.  `layers` resident copies (>= 1 GiB in all, four times the
+    # 256 MB Infinity Cache) are used in turn, so a step's weights were last
+    # touched a whole rotation earlier and come from HBM.
+    w_layer = E * q4_bytes(N, K)
+    layers = args.layers or max(2, -(-(1 << 30) // w_layer))
+    packed0 = q.prepack(d(p.Wq), d(p.S), d(p.B))     # one-time re-tiling at load time
+    packs = [packed0] + [tuple(t.clone() for t in packed0) for _ in range(layers - 1)]
+    logits, X = d(p.logits), d(p.X)
     rt = q.alloc_route(T, E, k, args.block_rows, device=dev)
     Y = torch.empty((T * k, N), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
         q.route(logits, k, bufs=rt, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        q.grouped_gemm_q4(X, k, packed, rt, Y=Y, stream=stream)
+        q.grouped_gemm_q4(X, k, packs[i % layers], rt, Y=Y, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
-    # Cold caches: the weights of one layer are not in the 256 MB Infinity Cache
-    # or the L2s when its turn comes, so every timed step starts after reading
-    # a 1 GiB buffer (a read, so no dirty lines are written back meanwhile).
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-
-    def flush():
-        flush_buf.sum()
-
-    for _ in range(args.warmup):
-        flush()
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # (1) cold: flush, then one step, each step timed with HIP events on its stream
-    ev_cold = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        flush()
-        step(ev_cold[i])
-    torch.cuda.synchronize()
-    step_ms = np.array([a.elapsed_time(c) for a, b, c in ev_cold])
-    gemm_ms_all = np.array([b.elapsed_time(c) for a, b, c in ev_cold])
-    ms_per_step = float(step_ms.mean())
-    gemm_ms = float(gemm_ms_all.mean())
-
-    # (2) warm: K back-to-back steps between two synchronisations, wall clock
-    ev_warm = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    # timed: exactly `steps` steps back to back between two synchronisations;
+    # HIP events on the launch stream split each step into route and GEMM
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev_warm[i])
+        step(args.warmup + i, ev[i])
     torch.cuda.synchronize()
-    warm_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    warm_gemm_ms = float(np.mean([b.elapsed_time(c) for a, b, c in ev_warm]))
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_step_ms = float(np.mean([a.elapsed_time(c) for a, b, c in ev]))
+    route_ms = float(np.mean([a.elapsed_time(b) for a, b, c in ev]))
+    gemm_all = np.array([b.elapsed_time(c) for a, b, c in ev])
+    gemm_ms = float(gemm_all.mean())
 
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
@@ -176,7 +165,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": gemm_tflops / BF16_PEAK_TFLOPS}
-    roof["traffic"] = load_traffic("k_gemm_q4", f"workload{args.workload}")
+    roof["traffic"] = load_traffic("k_gemm_q4", w.name)
     roof["kernel"] = "k_gemm_q4"
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["algorithmic_flops_per_launch"] = flops
@@ -193,19 +182,21 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded numpy PCG64; logits N(0,1), activations bf16 N(0,1), uniform 4-bit "
-                "codes, bf16 scale |N(0,0.02)|, bias -8*scale + N(0,0.002))",
+        "data": "synthetic (seeded numpy PCG64; logits N(0,1)" + (f" + Zipf expert bias, alpha {w.skew_alpha}"
+                if w.skew_alpha else "") + ", activations bf16 N(0,1), uniform 4-bit codes, bf16 scale "
+                "|N(0,0.02)|, bias -8*scale + N(0,0.002))",
         "config": {"workload": w.name, "T": T, "E": E, "top_k": k, "K": K, "N": N,
                    "block_rows": rt["block_rows"], "group": 64, "parallelism": "single GPU"},
         "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
         "gemm": {"us": gemm_ms * 1e3, "TFLOP/s": gemm_tflops, "weight_GB/s": w_bytes / (gemm_ms * 1e-3) / 1e9,
-                 "experts_touched": touched},
-        "route_us": (ms_per_step - gemm_ms) * 1e3,
-        "timing": "cold caches: 1 GiB read between steps; each step timed with HIP events on its stream "
-                  "(route start to GEMM end)",
-        "warm": {"ms_per_step_wall": warm_ms_per_step, "gemm_us": warm_gemm_ms * 1e3,
-                 "value": flops / (warm_ms_per_step * 1e-3) / 1e12,
-                 "note": "steps back to back; weights served from the Infinity Cache"},
+                 "experts_touched": touched, "rows_max_over_mean": float(counts.max() / counts.mean()),
+                 "experts_below_2_rows": float((counts < 2).mean())},
+        "route_us": route_ms * 1e3,
+        "event_ms_per_step": ev_step_ms,
+        "timing": f"steps back to back, wall clock between two synchronisations; weights rotate over {layers} "
+                  f"resident copies ({layers * w_layer / 2**30:.2f} GiB) so each GEMM reads them from HBM; "
+                  "route and GEMM split by HIP events on the launch stream",
+        "gemm_us_p10_p90": [float(np.percentile(gemm_all, 10)) * 1e3, float(np.percentile(gemm_all, 90)) * 1e3],
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -7,16 +7,18 @@
 // and a block map lists the fixed-size blocks the grouped GEMM processes.  The
 // whole sequence stays on the GPU: the block count never goes to the host.
 //
-// Three kernels, all on the caller's stream:
-//   k_topk_rank      one wave per token: top-k by k rounds of a wave-wide
-//                    argmax (DPP max + ballot), softmax over the k selected
-//                    logits; then, per workgroup "chunk" of tokens, the
-//                    histogram of its assignments and each assignment's stable
-//                    rank among same-expert assignments of the chunk (ballot
-//                    match masks over the expert-id bits + mbcnt popcounts).
+// Two or three kernels, all on the caller's stream:
+//   k_topk_rank      one workgroup of 16 waves per "chunk" of tokens, one wave
+//                    per token: top-k by k rounds of a wave-wide argmax over
+//                    order-preserving integer keys (DPP max + ballot), softmax
+//                    over the k selected logits; then the chunk's histogram
+//                    and each assignment's stable rank among same-expert
+//                    assignments of the chunk (ballot match masks over the
+//                    expert-id bits + popcounts).
 //   k_scan_blockmap  one workgroup: per-expert exclusive scan over chunks,
-//                    counts, offsets, block counts and their scan, block map.
-//   k_scatter        one thread per assignment: perm / inv_perm.
+//                    counts, offsets, block counts and their scan, block map;
+//                    for up to kFusedScatterMax assignments also the scatter.
+//   k_scatter        (larger inputs) one thread per assignment: perm, inv_perm.
 // Only integer adds decide positions, so every output is deterministic.
 #include <limits.h>
 
@@ -24,9 +26,11 @@
 
 namespace moeq4 {
 
-constexpr int kRouteMaxThreads = 1024;     // up to 16 waves per chunk workgroup
+constexpr int kRouteWaves = 16;            // waves per chunk workgroup
+constexpr int kRouteThreads = kRouteWaves * 64;
 constexpr int kChunkAssignMax = 2048;      // assignments per chunk (LDS bound)
-constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / 4;  // with at least 4 waves
+constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / kRouteWaves;
+constexpr int kFusedScatterMax = 8192;     // assignments the scan workgroup also scatters
 constexpr int kScanThreads = 1024;
 constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 
@@ -43,14 +47,14 @@ __device__ __forceinline__ int order_key(float v) {
 }
 
 template <int VPT>
-__global__ __launch_bounds__(kRouteMaxThreads) void k_topk_rank(
+__global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
     const float* __restrict__ logits, int T, int E, int k, int tpc, int nbits,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts,
     int32_t* __restrict__ local_rank) {
   extern __shared__ int smem[];
-  const int NW = blockDim.x >> 6;
-  int* sids = smem;              // [tpc * k] expert ids of the chunk's assignments
-  int* cnt = smem + tpc * k;     // [NW][E] per-wave counters, then per-wave bases
+  constexpr int NW = kRouteWaves;
+  int* sids = smem;                                  // [tpc * k] expert ids of the chunk
+  uint16_t* cnt = (uint16_t*)(smem + tpc * k);       // [NW][E] per-wave counters, then bases
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -62,29 +66,23 @@ __global__ __launch_bounds__(kRouteMaxThreads) void k_topk_rank(
   for (int i = threadIdx.x; i < NW * E; i += blockDim.x) cnt[i] = 0;
 
   // the next token's logits are in flight while the current one is selected
-  int kn[VPT];
   float vn[VPT];
   auto fetch = [&](int i) {
 #pragma unroll
     for (int s = 0; s < VPT; ++s) {
       const int e = lane * VPT + s;
       vn[s] = (i < ntok && e < E) ? logits[(size_t)(t0 + i) * E + e] : 0.f;
-      kn[s] = (i < ntok && e < E) ? 0 : kTaken;
     }
   };
   fetch(wv);
   for (int i = wv; i < ntok; i += NW) {
     const int t = t0 + i;
     int key[VPT];
-    float v[VPT];
 #pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-      v[s] = vn[s];
-      key[s] = kn[s] == kTaken ? kTaken : order_key(vn[s]);
-    }
+    for (int s = 0; s < VPT; ++s) key[s] = (lane * VPT + s < E) ? order_key(vn[s]) : kTaken;
     fetch(i + NW);
     int my_id = 0;
-    float my_v = 0.f;
+    float my_v = 0.f, v0 = 0.f;
     for (int j = 0; j < k; ++j) {
       // best of this lane: larger key, lower slot on ties
       int bk = key[0], bs = 0;
@@ -95,25 +93,21 @@ __global__ __launch_bounds__(kRouteMaxThreads) void k_topk_rank(
           bs = s;
         }
       }
-      const int m = wave_max_i32(bk);
+      const int m = wave_max_i32(bk);  // uniform
       const uint64_t bal = __ballot(bk == m);
-      const int wl = bal ? (__ffsll((unsigned long long)bal) - 1) : 0;
-      const int ws = __shfl(bs, wl);
-      float sel_v = 0.f;
+      const int wl = __builtin_amdgcn_readfirstlane(bal ? (__ffsll((unsigned long long)bal) - 1) : 0);
+      const int ws = __builtin_amdgcn_readlane(bs, wl);
+      // the key is an involution of the logit's bits: the selected logit
+      const float sel_v = __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
+      if (j == 0) v0 = sel_v;
 #pragma unroll
-      for (int s = 0; s < VPT; ++s) sel_v = (s == ws) ? v[s] : sel_v;
-      sel_v = __shfl(sel_v, wl);
-      if (lane == wl) {
-#pragma unroll
-        for (int s = 0; s < VPT; ++s)
-          if (s == ws) key[s] = kTaken;
-      }
+      for (int s = 0; s < VPT; ++s)
+        if (lane == wl && s == ws) key[s] = kTaken;
       if (lane == j) {
         my_id = min(wl * VPT + ws, E - 1);  // stays in range even for non-finite input
         my_v = sel_v;
       }
     }
-    const float v0 = __shfl(my_v, 0);
     const float ex = (lane < k) ? expf(my_v - v0) : 0.f;
     const float sum = wave_sum_f32(ex);
     if (lane < k) {
@@ -128,6 +122,7 @@ __global__ __launch_bounds__(kRouteMaxThreads) void k_topk_rank(
   const int na = ntok * k;
   const int nslices = (na + 63) >> 6;
   const int spw = (nslices + NW - 1) / NW;  // contiguous slices per wave (<= kMaxSlicesPerWave)
+  static_assert(kMaxSlicesPerWave * 64 * NW >= kChunkAssignMax, "slices per wave");
   const uint64_t lt = lanemask_lt();
   int rank[kMaxSlicesPerWave];
   int eid[kMaxSlicesPerWave];
@@ -152,7 +147,7 @@ __global__ __launch_bounds__(kRouteMaxThreads) void k_topk_rank(
       rank[s] = old + before;
       eid[s] = e;
       // the highest lane of each match group publishes the new count
-      if ((match >> lane) == 1ull) cnt[wv * E + e] = old + __popcll(match);
+      if ((match >> lane) == 1ull) cnt[wv * E + e] = (uint16_t)(old + __popcll(match));
     }
   }
   __syncthreads();
@@ -160,7 +155,7 @@ __global__ __launch_bounds__(kRouteMaxThreads) void k_topk_rank(
     int run = 0;
     for (int w = 0; w < NW; ++w) {
       const int c = cnt[w * E + e];
-      cnt[w * E + e] = run;
+      cnt[w * E + e] = (uint16_t)run;
       run += c;
     }
     chunk_counts[(size_t)chunk * E + e] = run;
@@ -206,7 +201,9 @@ __device__ int block_exclusive_scan(int v, int* scratch /* >= kScanThreads/64 + 
 
 __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
     int32_t* __restrict__ chunk_counts, int nchunks, int E, int BM, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks,
+    int fuse_scatter, const int32_t* __restrict__ ids, int A, int k, int tpc,
+    const int32_t* __restrict__ local_rank, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
   __shared__ int part[kScanThreads];
   __shared__ int offs_s[MOEQ4_MAX_EXPERTS + 1];
   __shared__ int boffs_s[MOEQ4_MAX_EXPERTS + 1];
@@ -298,6 +295,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
     blocks[4 * (size_t)b + 2] = min(BM, cnt - i * BM);
     blocks[4 * (size_t)b + 3] = i;
   }
+
+  // ---- small inputs: the scatter too (chunk bases were written above, before
+  // the barriers of the scans)
+  if (fuse_scatter) {
+    for (int a = tid; a < A; a += kScanThreads) {
+      const int e = ids[a];
+      const int c = (a / k) / tpc;
+      const int p = offs_s[e] + chunk_counts[(size_t)c * E + e] + local_rank[a];
+      if (p >= 0 && p < A) perm[p] = a;
+      inv_perm[a] = p;
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -321,9 +330,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 RoutePlan route_plan(int T, int E, int k) {
   RoutePlan p{};
-  // waves per chunk workgroup: as many as the per-wave counters [NW][E] allow in 16 KB
-  int nw = 16;
-  while (nw > 4 && nw * E > 4096) nw >>= 1;
+  const int nw = kRouteWaves;
   p.waves = nw;
   // about 256 chunks for long prompts; at least one token per wave
   int tpc = (T + 255) / 256;
@@ -351,22 +358,24 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
   int32_t* local_rank = (int32_t*)((char*)workspace + plan.ws_local_rank);
   hipError_t err = hipSuccess;
   if (plan.nchunks > 0) {
-    const size_t shmem = sizeof(int) * ((size_t)plan.tpc * k + (size_t)plan.waves * E);
+    const size_t shmem = sizeof(int) * (size_t)plan.tpc * k + sizeof(uint16_t) * (size_t)kRouteWaves * E;
     const void* fn;
     if (E <= 64) fn = (const void*)&k_topk_rank<1>;
     else if (E <= 128) fn = (const void*)&k_topk_rank<2>;
     else if (E <= 256) fn = (const void*)&k_topk_rank<4>;
     else if (E <= 512) fn = (const void*)&k_topk_rank<8>;
     else fn = (const void*)&k_topk_rank<16>;
-    err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(plan.waves * 64), shmem, stream, logits, T, E, k,
+    err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T, E, k,
                  plan.tpc, plan.nbits, ids, w, chunk_counts, local_rank);
     if (err != hipSuccess) return err;
   }
-  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), 0, stream, chunk_counts,
-               plan.nchunks, E, BM, counts, offsets, blocks, num_blocks);
-  if (err != hipSuccess) return err;
   const int A = T * k;
-  if (A > 0) {
+  const int fuse = A <= kFusedScatterMax;
+  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), 0, stream, chunk_counts,
+               plan.nchunks, E, BM, counts, offsets, blocks, num_blocks, fuse, (const int32_t*)ids, A, k,
+               plan.tpc, (const int32_t*)local_rank, perm, inv_perm);
+  if (err != hipSuccess) return err;
+  if (A > 0 && !fuse) {
     err = launch("k_scatter", (const void*)&k_scatter, dim3((A + 255) / 256), dim3(256), 0, stream,
                  (const int32_t*)ids, A, E, k, plan.tpc, (const int32_t*)offsets,
                  (const int32_t*)chunk_counts, (const int32_t*)local_rank, perm, inv_perm);
