@@ -175,6 +175,53 @@ int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
                         const int32_t* num_blocks, int max_blocks, int block_rows, uint16_t* Y,
                         void* stream);
 
+/* Bytes of device scratch moe_decode_ffn_q4 needs (0 on invalid sizes).
+ * shared: 1 when a shared expert is given, else 0. */
+size_t moe_decode_workspace_bytes(int E, int k, int H, int I, int shared);
+
+/* One batch-1 decode step of the MoE layer: routing, the selected experts'
+ * FFNs and the shared expert, fused into two kernels (sections "Decode is a
+ * bandwidth problem" and "Reduce intermediate and state traffic": the step is
+ * bound by the weight bytes it reads; the two input projections run with their
+ * gated activation, the output projection with the routing scores and the
+ * shared expert's result).
+ *
+ *   ids, w   = top-k of logits and softmax over the k selected (as moe_route)
+ *   h_j      = bf16( silu(G_j x) * (U_j x) ),  G_j / U_j = rows [0, I) / [I, 2I)
+ *              of expert ids[j]'s gate+up matrix [2I, H]
+ *   out      = bf16( sum_j w_j * D_j h_j  +  D_sh h_sh )
+ * where D_j is expert ids[j]'s down matrix [H, I] and the shared expert's terms
+ * (weight 1, no routing) are present when its matrices are given.  silu(z) =
+ * z / (1 + exp(-z)) in fp32 from the fp32 projections.  Every weight is
+ * rebuilt exactly as bf16(scale * code + bias) before it is multiplied (fp32
+ * accumulation).  The result is the same for the same inputs, run after run.
+ *
+ * In:  logits  float  [E]           the token's router logits (finite).
+ *      x       uint16 (bf16) [H]    the token's activations.
+ *      gu_codes_t, gu_scales_t, gu_biases_t   [E, 2I, H] gate+up weights in the
+ *                                   tiled layout of moe_prepack_q4 (N = 2I, K = H).
+ *      dn_codes_t, dn_scales_t, dn_biases_t   [E, H, I] down weights, tiled
+ *                                   (N = H, K = I).
+ *      sh_*    the shared expert's two matrices ([1, 2I, H] and [1, H, I],
+ *              tiled), all six given or all six NULL.
+ *      workspace  device scratch of moe_decode_workspace_bytes(E, k, H, I,
+ *              shared) bytes, 16-byte aligned; no initial contents needed.
+ * Out: out     uint16 (bf16) [H].
+ *      topk_ids int32 [k], topk_w float [k]   the routing (each may be NULL).
+ * Sizes: 1 <= k <= min(E, MOEQ4_MAX_TOPK), E <= MOEQ4_MAX_EXPERTS, H and I
+ *        multiples of 64 and at least 128, H <= 16384, ceil((k + shared) / 2) * I * 2 bytes
+ *        <= 64 KiB, E*2I*H/2 below 2^31.  Returns MOEQ4_ERR_UNSUPPORTED when
+ *        the sizes exceed the kernels' LDS budget. */
+int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int H, int I,
+                      const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                      const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                      const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                      const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                      const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                      const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                      int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
+                      size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,6 +43,8 @@ SIGNATURES = {
     "moe_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_q4": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                  _vp, _vp]),
+    "moe_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "moe_decode_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -139,6 +141,21 @@ def moe_grouped_gemm_q4(X, T, K, N, E, k, codes_t, scales_t, biases_t, perm, blo
         _p(num_blocks), max_blocks, block_rows, _p(Y), _stream(stream)))
 
 
+def moe_decode_workspace_bytes(E: int, k: int, H: int, I: int, shared: bool) -> int:
+    return int(lib().moe_decode_workspace_bytes(E, k, H, I, int(bool(shared))))
+
+
+def moe_decode_ffn_q4(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t,
+                      dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                      sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, topk_ids, topk_w, out, workspace,
+                      ws_bytes, stream=None):
+    _ok("moe_decode_ffn_q4", lib().moe_decode_ffn_q4(
+        _p(logits), _p(x), E, k, H, I, _p(gu_codes_t), _p(gu_scales_t), _p(gu_biases_t), _p(dn_codes_t),
+        _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
+        _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), _p(topk_ids), _p(topk_w), _p(out),
+        _p(workspace), int(ws_bytes), _stream(stream)))
+
+
 # ---------------------------------------------------------------- plumbing --
 # Device buffers come from torch (memory and streams only).
 
@@ -188,3 +205,32 @@ def grouped_gemm_q4(X, k, packed, rt, Y=None, stream=None):
     moe_grouped_gemm_q4(X, T, K, N, E, k, codes_t, scales_t, biases_t, rt["perm"], rt["blocks"],
                         rt["num_blocks"], rt["max_blocks"], rt["block_rows"], Y, stream)
     return Y
+
+
+def alloc_decode(E: int, k: int, H: int, I: int, shared: bool = True, device="cuda"):
+    """Output and workspace tensors for moe_decode_ffn_q4."""
+    ws = moe_decode_workspace_bytes(E, k, H, I, shared)
+    if ws == 0:
+        raise MoeQ4Error("moe_decode_workspace_bytes", MOEQ4_ERR_SHAPE)
+    return dict(
+        out=torch.empty(H, dtype=torch.int16, device=device),
+        topk_ids=torch.empty(k, dtype=torch.int32, device=device),
+        topk_w=torch.empty(k, dtype=torch.float32, device=device),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=device), ws_bytes=ws)
+
+
+def decode_ffn(logits, x, k: int, gu, dn, sh_gu=None, sh_dn=None, bufs=None, stream=None):
+    """One batch-1 decode step (moe_decode_ffn_q4).  ``logits`` float32 [E],
+    ``x`` bf16 bits [H]; ``gu`` / ``dn`` = prepack() tuples of the [E, 2I, H] and
+    [E, H, I] matrices; ``sh_gu`` / ``sh_dn`` the shared expert's ([1, ...]) or
+    None.  Returns the buffer dict (``out`` holds bf16 bits [H])."""
+    E = logits.shape[-1]
+    H = x.shape[-1]
+    I = gu[0].shape[1] // 2
+    shared = sh_gu is not None
+    b = bufs or alloc_decode(E, k, H, I, shared, device=x.device)
+    sg = sh_gu if shared else (None, None, None)
+    sd = sh_dn if shared else (None, None, None)
+    moe_decode_ffn_q4(logits, x, E, k, H, I, *gu, *dn, *sg, *sd, b["topk_ids"], b["topk_w"], b["out"],
+                      b["workspace"], b["ws_bytes"], stream)
+    return b

@@ -70,6 +70,60 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
+// Order-preserving integer image of a float (monotone for non-NaN values;
+// -0 is folded into +0 so equal logits get equal keys).  It is an involution on
+// the folded bits: applying it again returns the float's bits.
+__device__ __forceinline__ int order_key(float v) {
+  const int u = __float_as_int(v + 0.0f);  // -0 + 0 = +0
+  return u ^ ((u >> 31) & 0x7FFFFFFF);
+}
+
+__device__ __forceinline__ float key_value(int key) {
+  return __int_as_float(key ^ ((key >> 31) & 0x7FFFFFFF));
+}
+
+constexpr int kKeyTaken = (int)0x80000000;  // below every finite logit's key
+
+// Top-k of one token's logits held by one wave: lane l holds the keys of
+// experts l*VPT + s (kKeyTaken where there is no expert).  k rounds of a
+// wave-wide maximum select the largest key, the lowest expert id among equal
+// keys (Perplexity Engineering, "Optimizing on-device inference for Apple
+// Silicon", section "Qwen creates three workload shapes": the router keeps the
+// best-scoring experts of each token).  Lane j < k receives the j-th selected
+// expert id and logit; v0 (uniform) is the largest logit.  Consumes `key`.
+template <int VPT>
+__device__ __forceinline__ void wave_topk(int (&key)[VPT], int E, int k, int& my_id, float& my_v,
+                                          float& v0) {
+  const int lane = threadIdx.x & 63;
+  my_id = 0;
+  my_v = 0.f;
+  v0 = 0.f;
+  for (int j = 0; j < k; ++j) {
+    // best of this lane: larger key, lower slot on ties
+    int bk = key[0], bs = 0;
+#pragma unroll
+    for (int s = 1; s < VPT; ++s) {
+      if (key[s] > bk) {
+        bk = key[s];
+        bs = s;
+      }
+    }
+    const int m = wave_max_i32(bk);  // uniform
+    const uint64_t bal = __ballot(bk == m);
+    const int wl = __builtin_amdgcn_readfirstlane(bal ? (__ffsll((unsigned long long)bal) - 1) : 0);
+    const int ws = __builtin_amdgcn_readlane(bs, wl);
+    const float sel_v = key_value(m);
+    if (j == 0) v0 = sel_v;
+#pragma unroll
+    for (int s = 0; s < VPT; ++s)
+      if (lane == wl && s == ws) key[s] = kKeyTaken;
+    if (lane == j) {
+      my_id = min(wl * VPT + ws, E - 1);  // stays in range even for non-finite input
+      my_v = sel_v;
+    }
+  }
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = __lane_id();
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -109,6 +163,21 @@ hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, 
                           const uint16_t* St, const uint16_t* Bt, const int32_t* perm,
                           const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
                           int block_rows, uint16_t* Y, hipStream_t stream);
+
+struct DecodePlan {
+  int J;               // experts per step: k routed + the shared one if given
+  size_t ws_ids, ws_w, ws_h, ws_tickets, ws_part, ws_bytes;  // workspace byte offsets / total
+  size_t lds_gateup, lds_down;                               // dynamic LDS bytes per kernel
+};
+
+DecodePlan decode_plan(int E, int k, int H, int I, bool shared);
+
+hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_t* x, int E, int k, int H, int I,
+                         const uint8_t* gu_q, const uint16_t* gu_s, const uint16_t* gu_b, const uint8_t* dn_q,
+                         const uint16_t* dn_s, const uint16_t* dn_b, const uint8_t* sh_gu_q,
+                         const uint16_t* sh_gu_s, const uint16_t* sh_gu_b, const uint8_t* sh_dn_q,
+                         const uint16_t* sh_dn_s, const uint16_t* sh_dn_b, int32_t* ids_out, float* w_out,
+                         uint16_t* out, void* workspace, hipStream_t stream);
 
 hipError_t prepack_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
                           int E, int N, int K, uint8_t* codes_t, uint16_t* scales_t,

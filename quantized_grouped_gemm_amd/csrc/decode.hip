@@ -1,0 +1,408 @@
+// decode.hip -- batch-1 decode step of the MoE layer (one token), gfx950.
+//
+// Perplexity Engineering, "Optimizing on-device inference for Apple Silicon":
+//   section "Decode is a bandwidth problem": with one token per step each
+//   expert GEMV reads every selected weight once, so the step is bound by the
+//   weight bytes, and matrix-vector work suits the vector ALUs;
+//   section "Reduce intermediate and state traffic": the two input projections
+//   run together with their gated activation, and the output projection
+//   together with the routing score and the shared expert's result;
+//   section "Qwen creates three workload shapes": 8 of 256 experts per token
+//   plus one shared expert that sees every token.
+//
+// Two kernels on the caller's stream, reading the same tiled weights as the
+// grouped GEMM (moe_prepack_q4), so one copy of the weights serves both:
+//   k_decode_gateup  one workgroup per (selected expert j, 16-row tile t of the
+//                    intermediate dimension I).  Each workgroup routes the
+//                    token itself (wave_topk over the E logits: no separate
+//                    routing launch, no host round trip), reads gate tile t and
+//                    up tile t + I/16 of expert e_j and writes
+//                    h_j[16t..16t+16) = bf16(silu(g) * u).  Workgroup 0 also
+//                    writes the k ids and softmax weights and clears the
+//                    tickets of the down kernel.
+//   k_decode_down    one workgroup per (16-row tile of H, half of the experts):
+//                    sum over its experts of w_j * (Wd[e_j] h_j), with w = 1 for
+//                    the shared expert.  Of the two workgroups of a tile, the
+//                    one that finishes second adds the two fp32 halves (always
+//                    half 0 + half 1) and writes bf16 out, so the result does not
+//                    depend on which finished first.
+//
+// GEMV inner loop: a wave reads one 1 KB block of the tiled layout (16 rows x
+// 128 K values; lane 16q+r holds 32 codes of row r) and rebuilds every weight
+// exactly as bf16(scale * code + bias) (section "Dequantize weights during
+// matrix multiplication": bf16 weights are rebuilt on chip before the
+// multiply); v_dot2c_f32_bf16 multiplies the rebuilt pairs with bf16
+// activation pairs from LDS and accumulates in fp32.  All of a lane's block
+// loads are issued before any math, behind the activation loads, so the waits
+// are exact (loads complete in issue order).
+#include "common.h"
+
+namespace moeq4 {
+
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = kDecWaves * 64;
+constexpr int kDecBatch = 8;      // weight blocks a wave keeps in flight
+
+typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16v2, a), __builtin_bit_cast(bf16v2, b), c,
+                                         false);
+}
+
+// bf16(s*q0 + b) and bf16(s*q1 + b) packed low / high
+__device__ __forceinline__ uint32_t rebuild_pair(uint32_t q0, uint32_t q1, float s, float b) {
+  const __bf16 w0 = (__bf16)__builtin_fmaf((float)q0, s, b);  // s*q + b is exact in fp32
+  const __bf16 w1 = (__bf16)__builtin_fmaf((float)q1, s, b);
+  return (uint32_t)__builtin_bit_cast(uint16_t, w0) | ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+}
+
+// sum over 16 consecutive K values of x * bf16(s*q + b): codes in tiled dwords
+// d0 (K +0..7) and d1 (K +8..15), x pairs in xa (K +0..7) and xb (K +8..15).
+// A tiled dword holds c0..c7 as nibbles c0,c2,c4,c6,c1,c3,c5,c7, so its bytes
+// masked with 0x0F0F0F0F are (c0,c4,c1,c5) and shifted by 4 are (c2,c6,c3,c7).
+__device__ __forceinline__ float dot16(uint32_t d0, uint32_t d1, uint4 xa, uint4 xb, float s, float b) {
+  float p = 0.f, q = 0.f;
+  {
+    const uint32_t lo = d0 & 0x0F0F0F0Fu, hi = (d0 >> 4) & 0x0F0F0F0Fu;
+    p = dot2(rebuild_pair(lo & 0xFF, (lo >> 16) & 0xFF, s, b), xa.x, p);  // c0, c1
+    q = dot2(rebuild_pair(hi & 0xFF, (hi >> 16) & 0xFF, s, b), xa.y, q);  // c2, c3
+    p = dot2(rebuild_pair((lo >> 8) & 0xFF, lo >> 24, s, b), xa.z, p);    // c4, c5
+    q = dot2(rebuild_pair((hi >> 8) & 0xFF, hi >> 24, s, b), xa.w, q);    // c6, c7
+  }
+  {
+    const uint32_t lo = d1 & 0x0F0F0F0Fu, hi = (d1 >> 4) & 0x0F0F0F0Fu;
+    p = dot2(rebuild_pair(lo & 0xFF, (lo >> 16) & 0xFF, s, b), xb.x, p);
+    q = dot2(rebuild_pair(hi & 0xFF, (hi >> 16) & 0xFF, s, b), xb.y, q);
+    p = dot2(rebuild_pair((lo >> 8) & 0xFF, lo >> 24, s, b), xb.z, p);
+    q = dot2(rebuild_pair((hi >> 8) & 0xFF, hi >> 24, s, b), xb.w, q);
+  }
+  return p + q;
+}
+
+// One matrix [N][K] of the tiled layout, seen by one GEMV.
+struct TiledMat {
+  const uint8_t* q;    // codes of this matrix
+  const uint16_t* s;   // scales
+  const uint16_t* b;   // biases
+  int NT;              // N / 16
+};
+
+// Partial GEMV of column r = lane % 16 of tile `tile` over full chunk c; x and
+// its 16-value slice sums live in LDS.
+struct FullBlock {
+  uint4 codes;
+  uint32_t s2, b2;  // bf16 scale / bias of groups 2c (low half) and 2c+1 (high half)
+};
+
+__device__ __forceinline__ FullBlock load_full(const TiledMat& m, int tile, int c, int lane) {
+  FullBlock f;
+  f.codes = *(const uint4*)(m.q + ((size_t)c * m.NT + tile) * 1024 + 16 * lane);
+  const size_t g = 32 * ((size_t)c * m.NT + tile) + 2 * (lane & 15);
+  f.s2 = *(const uint32_t*)(m.s + g);
+  f.b2 = *(const uint32_t*)(m.b + g);
+  return f;
+}
+
+__device__ __forceinline__ float gemv_full(const FullBlock& f, int c, int lane, const uint4* xl) {
+  const int k0 = 128 * c + 16 * (lane >> 4);  // first K value of the lane's first 16
+  const float s0 = bf16_bits_to_f32(f.s2 & 0xFFFFu), s1 = bf16_bits_to_f32(f.s2 >> 16);
+  const float b0 = bf16_bits_to_f32(f.b2 & 0xFFFFu), b1 = bf16_bits_to_f32(f.b2 >> 16);
+  return dot16(f.codes.x, f.codes.y, xl[k0 / 8], xl[k0 / 8 + 1], s0, b0) +
+         dot16(f.codes.z, f.codes.w, xl[(k0 + 64) / 8], xl[(k0 + 64) / 8 + 1], s1, b1);
+}
+
+// the half-size last chunk of an odd group count: lane 16q+r holds 16 codes
+__device__ __forceinline__ float gemv_tail(const TiledMat& m, int tile, int c, int lane, const uint4* xl) {
+  const uint2 cd = *(const uint2*)(m.q + (size_t)c * m.NT * 1024 + (size_t)tile * 512 + 8 * lane);
+  const size_t g = 32 * (size_t)c * m.NT + 16 * (size_t)tile + (lane & 15);
+  const float s0 = bf16_bits_to_f32(m.s[g]), b0 = bf16_bits_to_f32(m.b[g]);
+  const int k0 = 128 * c + 16 * (lane >> 4);
+  return dot16(cd.x, cd.y, xl[k0 / 8], xl[k0 / 8 + 1], s0, b0);
+}
+
+// Sum over the chunks c = c_first, c_first + c_step, ... of the full chunks
+// (nfull of them), batched so that a wave keeps kDecBatch block loads in flight.
+__device__ __forceinline__ float gemv_chunks(const TiledMat& m, int tile, int nfull, int c_first, int c_step,
+                                             int lane, const uint4* xl) {
+  float acc = 0.f;
+  for (int c0 = c_first; c0 < nfull; c0 += kDecBatch * c_step) {
+    FullBlock f[kDecBatch];
+#pragma unroll
+    for (int i = 0; i < kDecBatch; ++i) f[i] = load_full(m, tile, min(c0 + i * c_step, nfull - 1), lane);
+#pragma unroll
+    for (int i = 0; i < kDecBatch; ++i) {
+      const int c = c0 + i * c_step;
+      if (c < nfull) acc += gemv_full(f[i], c, lane, xl);
+    }
+  }
+  return acc;
+}
+
+// sum of the partials of lanes r, r+16, r+32, r+48 (the four K quarters)
+__device__ __forceinline__ float sum_quarters(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Staging of bf16 vectors (n values each, n % 8 == 0) in LDS.  The first
+// 16-byte piece of each thread is loaded into registers (stage_load) before
+// the weight loads are issued, so that the wait for it does not also wait for
+// the weights (loads complete in issue order); stage_store writes it to LDS,
+// then any further pieces are staged directly.
+__device__ __forceinline__ uint4 stage_load(const uint16_t* __restrict__ src, int npieces) {
+  const int i = min((int)threadIdx.x, npieces - 1);
+  return *(const uint4*)(src + 8 * (size_t)i);
+}
+
+__device__ __forceinline__ void stage_store(uint4 first, const uint16_t* __restrict__ src, int npieces,
+                                            uint4* xl) {
+  if ((int)threadIdx.x < npieces) xl[threadIdx.x] = first;
+  for (int i = threadIdx.x + kDecThreads; i < npieces; i += kDecThreads) xl[i] = *(const uint4*)(src + 8 * (size_t)i);
+}
+
+// ----------------------------------------------------------------------------
+template <int VPT>
+__global__ __launch_bounds__(kDecThreads) void k_decode_gateup(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, int H, int I,
+    const uint8_t* __restrict__ gu_q, const uint16_t* __restrict__ gu_s, const uint16_t* __restrict__ gu_b,
+    const uint8_t* __restrict__ sh_q, const uint16_t* __restrict__ sh_s, const uint16_t* __restrict__ sh_b,
+    int32_t* __restrict__ ids_ws, float* __restrict__ w_ws, uint16_t* __restrict__ h_ws,
+    int32_t* __restrict__ tickets, int ntickets, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+  extern __shared__ uint4 dsm[];
+  uint4* xl = dsm;  // x as bf16, H values
+  __shared__ float red[kDecWaves][16];
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int IT = I / 16;
+  const int j = blockIdx.x / IT, t = blockIdx.x % IT;
+
+  const uint4 xr = stage_load(x, H / 8);  // x is needed by every workgroup: its load goes first
+  // ---- which expert: the token's j-th choice (every wave selects on its own)
+  int e = 0;
+  if (j < k) {
+    float lg[VPT];
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) lg[s] = logits[min(lane * VPT + s, E - 1)];
+    int key[VPT];
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) key[s] = lane * VPT + s < E ? order_key(lg[s]) : kKeyTaken;
+    int my_id;
+    float my_v, v0;
+    wave_topk<VPT>(key, E, k, my_id, my_v, v0);
+    e = __builtin_amdgcn_readlane(my_id, j);
+    if (blockIdx.x == 0 && wv == 0) {
+      const float ex = (lane < k) ? expf(my_v - v0) : 0.f;
+      const float sum = wave_sum_f32(ex);
+      if (lane < k) {
+        ids_ws[lane] = my_id;
+        w_ws[lane] = ex / sum;
+        if (ids_out) ids_out[lane] = my_id;
+        if (w_out) w_out[lane] = ex / sum;
+      }
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < ntickets; i += kDecThreads) tickets[i] = 0;
+
+  const size_t mat_codes = (size_t)I * H;  // bytes of one [2I][H] code matrix
+  const size_t mat_groups = (size_t)2 * I * (H / kGroup);
+  TiledMat m;
+  m.q = j < k ? gu_q + e * mat_codes : sh_q;
+  m.s = j < k ? gu_s + e * mat_groups : sh_s;
+  m.b = j < k ? gu_b + e * mat_groups : sh_b;
+  m.NT = 2 * IT;
+  const int G = H / kGroup, nfull = G / 2;
+
+  // waves 0..3: gate tile t, waves 4..7: up tile t + I/16; wave w & 3 takes
+  // chunks w&3, (w&3)+4, ...  Loads are unconditional (chunk index clamped,
+  // surplus results unused) so the wait for x below is exact.
+  constexpr int WPT = kDecWaves / 2;  // waves per tile
+  const int tile = (wv < WPT) ? t : t + IT;
+  const int c_first = wv % WPT;
+  FullBlock f[kDecBatch];
+#pragma unroll
+  for (int i = 0; i < kDecBatch; ++i) f[i] = load_full(m, tile, min(c_first + WPT * i, nfull - 1), lane);
+  stage_store(xr, x, H / 8, xl);
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDecBatch; ++i) {
+    const int c = c_first + WPT * i;
+    if (c < nfull) acc += gemv_full(f[i], c, lane, xl);
+  }
+  acc += gemv_chunks(m, tile, nfull, c_first + WPT * kDecBatch, WPT, lane, xl);
+  if ((G & 1) && c_first == nfull % WPT) acc += gemv_tail(m, tile, nfull, lane, xl);
+  acc = sum_quarters(acc);
+  if (lane < 16) red[wv][lane] = acc;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int r = threadIdx.x;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) {
+      g += red[w][r];
+      u += red[WPT + w][r];
+    }
+    const float silu = g / (1.f + expf(-g));
+    h_ws[(size_t)j * I + 16 * t + r] = f32_to_bf16_bits(silu * u);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Ends a down-projection workgroup: reduces the waves' partials of the tile's 16
+// outputs, publishes them, and if the other half of the tile is already done,
+// adds the two halves (half 0 + half 1) and writes bf16 out.
+__device__ __forceinline__ void finish_tile(float acc, int t, int half, float (*red)[16],
+                                            int32_t* __restrict__ tickets, float* __restrict__ part,
+                                            uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane < 16) red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    const int r = lane & 15;
+    float p = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) p += red[w][r];
+    if (lane < 16)
+      __hip_atomic_store(part + ((size_t)t * 2 + half) * 16 + r, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(tickets + t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old == 1 && lane < 16) {  // the other half is complete: combine in a fixed order
+      const float other = __hip_atomic_load(part + ((size_t)t * 2 + (1 - half)) * 16 + r, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+      const float total = half == 0 ? p + other : other + p;
+      out[16 * t + r] = f32_to_bf16_bits(total);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kDecThreads) void k_decode_down(
+    int k, int H, int I, int J, const uint8_t* __restrict__ dn_q, const uint16_t* __restrict__ dn_s,
+    const uint16_t* __restrict__ dn_b, const uint8_t* __restrict__ sh_q, const uint16_t* __restrict__ sh_s,
+    const uint16_t* __restrict__ sh_b, const int32_t* __restrict__ ids_ws, const float* __restrict__ w_ws,
+    const uint16_t* __restrict__ h_ws, int32_t* __restrict__ tickets, float* __restrict__ part,
+    uint16_t* __restrict__ out) {
+  extern __shared__ uint4 dsm[];
+  __shared__ float red[kDecWaves][16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int J0 = (J + 1) / 2;
+  const int j_lo = half ? J0 : 0, j_hi = half ? J : J0;
+  const int nj = j_hi - j_lo;
+  if (nj == 0) {  // a single expert in all: this half has nothing to add
+    finish_tile(0.f, t, half, red, tickets, part, out);
+    return;
+  }
+  const uint4 hr = stage_load(h_ws + (size_t)j_lo * I, nj * (I / 8));
+  uint4* hl = dsm;  // [nj][I] bf16: h of this half's experts
+
+  const size_t mat_codes = (size_t)H * I / 2;
+  const size_t mat_groups = (size_t)H * (I / kGroup);
+  const int G = I / kGroup, nfull = G / 2;
+  const int nb = nj * nfull;  // full blocks of this workgroup: (expert, chunk); wave w takes w, w+8, ...
+  auto mat = [&](int j, size_t e) {
+    TiledMat m1;
+    m1.q = j < k ? dn_q + e * mat_codes : sh_q;
+    m1.s = j < k ? dn_s + e * mat_groups : sh_s;
+    m1.b = j < k ? dn_b + e * mat_groups : sh_b;
+    m1.NT = H / 16;
+    return m1;
+  };
+  float acc = 0.f;
+  FullBlock f[kDecBatch];
+  float wb[kDecBatch];
+  // loads are unconditional (indices clamped, surplus results unused), so the
+  // expert ids arrive with one wait and the wait for h below is exact
+  auto load_batch = [&](int b0) {
+    int eb[kDecBatch];
+#pragma unroll
+    for (int i = 0; i < kDecBatch; ++i) {
+      const int b = min(b0 + kDecWaves * i, nb - 1);
+      const int j = j_lo + b / nfull, jc = min(j, k - 1);
+      eb[i] = ids_ws[jc];
+      const float wl = w_ws[jc];
+      wb[i] = j < k ? wl : 1.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kDecBatch; ++i) {
+      const int b = min(b0 + kDecWaves * i, nb - 1);
+      f[i] = load_full(mat(j_lo + b / nfull, (size_t)eb[i]), t, b % nfull, lane);
+    }
+  };
+  auto compute_batch = [&](int b0) {
+#pragma unroll
+    for (int i = 0; i < kDecBatch; ++i) {
+      const int b = b0 + kDecWaves * i;
+      if (b < nb) acc = __builtin_fmaf(wb[i], gemv_full(f[i], b % nfull, lane, hl + (size_t)(b / nfull) * I / 8), acc);
+    }
+  };
+  load_batch(wv);  // in flight while h is staged
+  stage_store(hr, h_ws + (size_t)j_lo * I, nj * (I / 8), hl);
+  __syncthreads();
+  compute_batch(wv);
+  for (int b0 = wv + kDecWaves * kDecBatch; b0 < nb; b0 += kDecWaves * kDecBatch) {
+    load_batch(b0);
+    compute_batch(b0);
+  }
+  if (G & 1) {  // half-size last chunk of every expert of this half
+    for (int jj = wv; jj < nj; jj += kDecWaves) {
+      const int j = j_lo + jj;
+      const float wj = j < k ? w_ws[j] : 1.f;
+      acc = __builtin_fmaf(wj, gemv_tail(mat(j, j < k ? (size_t)ids_ws[j] : 0), t, nfull, lane, hl + (size_t)jj * I / 8),
+                           acc);
+    }
+  }
+  acc = sum_quarters(acc);
+  finish_tile(acc, t, half, red, tickets, part, out);
+}
+
+// ----------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodePlan decode_plan(int E, int k, int H, int I, bool shared) {
+  DecodePlan p{};
+  p.J = k + (shared ? 1 : 0);
+  p.ws_ids = 0;
+  p.ws_w = align256(sizeof(int32_t) * (size_t)k);
+  p.ws_h = p.ws_w + align256(sizeof(float) * (size_t)k);
+  p.ws_tickets = p.ws_h + align256(sizeof(uint16_t) * (size_t)p.J * I);
+  p.ws_part = p.ws_tickets + align256(sizeof(int32_t) * (size_t)(H / 16));
+  p.ws_bytes = p.ws_part + align256(sizeof(float) * (size_t)(H / 16) * 2 * 16);
+  p.lds_gateup = (size_t)H * 2;
+  const int J0 = (p.J + 1) / 2;
+  p.lds_down = (size_t)J0 * I * 2;
+  (void)E;
+  return p;
+}
+
+hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_t* x, int E, int k, int H, int I,
+                         const uint8_t* gu_q, const uint16_t* gu_s, const uint16_t* gu_b, const uint8_t* dn_q,
+                         const uint16_t* dn_s, const uint16_t* dn_b, const uint8_t* sh_gu_q,
+                         const uint16_t* sh_gu_s, const uint16_t* sh_gu_b, const uint8_t* sh_dn_q,
+                         const uint16_t* sh_dn_s, const uint16_t* sh_dn_b, int32_t* ids_out, float* w_out,
+                         uint16_t* out, void* workspace, hipStream_t stream) {
+  char* ws = (char*)workspace;
+  int32_t* ids_ws = (int32_t*)(ws + p.ws_ids);
+  float* w_ws = (float*)(ws + p.ws_w);
+  uint16_t* h_ws = (uint16_t*)(ws + p.ws_h);
+  int32_t* tickets = (int32_t*)(ws + p.ws_tickets);
+  float* part = (float*)(ws + p.ws_part);
+  const void* fn;
+  if (E <= 64) fn = (const void*)&k_decode_gateup<1>;
+  else if (E <= 128) fn = (const void*)&k_decode_gateup<2>;
+  else if (E <= 256) fn = (const void*)&k_decode_gateup<4>;
+  else if (E <= 512) fn = (const void*)&k_decode_gateup<8>;
+  else fn = (const void*)&k_decode_gateup<16>;
+  hipError_t err = launch("k_decode_gateup", fn, dim3(p.J * (I / 16)), dim3(kDecThreads), p.lds_gateup, stream,
+                          logits, x, E, k, H, I, gu_q, gu_s, gu_b, sh_gu_q, sh_gu_s, sh_gu_b, ids_ws, w_ws, h_ws,
+                          tickets, H / 16, ids_out, w_out);
+  if (err != hipSuccess) return err;
+  return launch("k_decode_down", (const void*)&k_decode_down, dim3(2 * (H / 16)), dim3(kDecThreads), p.lds_down,
+                stream, k, H, I, p.J, dn_q, dn_s, dn_b, sh_dn_q, sh_dn_s, sh_dn_b, (const int32_t*)ids_ws,
+                (const float*)w_ws, (const uint16_t*)h_ws, tickets, part, out);
+}
+
+}  // namespace moeq4

@@ -20,8 +20,6 @@
 //                    for up to kFusedScatterMax assignments also the scatter.
 //   k_scatter        (larger inputs) one thread per assignment: perm, inv_perm.
 // Only integer adds decide positions, so every output is deterministic.
-#include <limits.h>
-
 #include "common.h"
 
 namespace moeq4 {
@@ -38,14 +36,7 @@ constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 // top-k + softmax + chunk histogram + in-chunk stable ranks.
 // A workgroup of NW waves handles one chunk of tpc tokens; wave w takes tokens
 // w, w+NW, ...  Lane l of a token's wave holds experts [l*VPT, (l+1)*VPT).
-// Selection compares order-preserving integer keys of the logits (with -0
-// folded into +0, so equal logits give equal keys): the wave maximum is a
-// DPP max over ints, and the lowest lane holding it has the lowest expert id.
-__device__ __forceinline__ int order_key(float v) {
-  const int u = __float_as_int(v + 0.0f);  // -0 + 0 = +0
-  return u ^ ((u >> 31) & 0x7FFFFFFF);     // monotone in v for non-NaN floats
-}
-
+// Selection compares order-preserving integer keys of the logits (wave_topk).
 template <int VPT>
 __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
     const float* __restrict__ logits, int T, int E, int k, int tpc, int nbits,
@@ -61,7 +52,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
   const int chunk = blockIdx.x;
   const int t0 = chunk * tpc;
   const int ntok = min(tpc, T - t0);
-  constexpr int kTaken = INT_MIN;  // below every finite logit's key
 
   for (int i = threadIdx.x; i < NW * E; i += blockDim.x) cnt[i] = 0;
 
@@ -71,7 +61,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
 #pragma unroll
     for (int s = 0; s < VPT; ++s) {
       const int e = lane * VPT + s;
-      vn[s] = (i < ntok && e < E) ? logits[(size_t)(t0 + i) * E + e] : 0.f;
+      // clamped indices: the loads are unconditional, so they overlap
+      vn[s] = logits[(size_t)(t0 + min(i, ntok - 1)) * E + min(e, E - 1)];
     }
   };
   fetch(wv);
@@ -79,35 +70,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
     const int t = t0 + i;
     int key[VPT];
 #pragma unroll
-    for (int s = 0; s < VPT; ++s) key[s] = (lane * VPT + s < E) ? order_key(vn[s]) : kTaken;
+    for (int s = 0; s < VPT; ++s) key[s] = (lane * VPT + s < E) ? order_key(vn[s]) : kKeyTaken;
     fetch(i + NW);
-    int my_id = 0;
-    float my_v = 0.f, v0 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      // best of this lane: larger key, lower slot on ties
-      int bk = key[0], bs = 0;
-#pragma unroll
-      for (int s = 1; s < VPT; ++s) {
-        if (key[s] > bk) {
-          bk = key[s];
-          bs = s;
-        }
-      }
-      const int m = wave_max_i32(bk);  // uniform
-      const uint64_t bal = __ballot(bk == m);
-      const int wl = __builtin_amdgcn_readfirstlane(bal ? (__ffsll((unsigned long long)bal) - 1) : 0);
-      const int ws = __builtin_amdgcn_readlane(bs, wl);
-      // the key is an involution of the logit's bits: the selected logit
-      const float sel_v = __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
-      if (j == 0) v0 = sel_v;
-#pragma unroll
-      for (int s = 0; s < VPT; ++s)
-        if (lane == wl && s == ws) key[s] = kTaken;
-      if (lane == j) {
-        my_id = min(wl * VPT + ws, E - 1);  // stays in range even for non-finite input
-        my_v = sel_v;
-      }
-    }
+    int my_id;
+    float my_v, v0;
+    wave_topk<VPT>(key, E, k, my_id, my_v, v0);
     const float ex = (lane < k) ? expf(my_v - v0) : 0.f;
     const float sum = wave_sum_f32(ex);
     if (lane < k) {

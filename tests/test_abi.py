@@ -126,3 +126,27 @@ def test_prepack_validation():
     assert _prepack(E=0) == q.MOEQ4_ERR_SHAPE
     assert _prepack(codes_t=None) == q.MOEQ4_ERR_NULL
     assert _prepack(scales=FAKE + 8) == q.MOEQ4_ERR_ALIGN
+
+
+def _decode(**kw):
+    a = dict(logits=FAKE, x=FAKE, E=16, k=2, H=256, I=128, gu_q=FAKE, gu_s=FAKE, gu_b=FAKE, dn_q=FAKE,
+             dn_s=FAKE, dn_b=FAKE, sh_gu_q=None, sh_gu_s=None, sh_gu_b=None, sh_dn_q=None, sh_dn_s=None,
+             sh_dn_b=None, topk_ids=None, topk_w=None, out=FAKE, workspace=FAKE,
+             ws_bytes=q.moe_decode_workspace_bytes(16, 2, 256, 128, False), stream=None)
+    a.update(kw)
+    return q.lib().moe_decode_ffn_q4(*a.values())
+
+
+def test_decode_validation():
+    assert q.moe_decode_workspace_bytes(256, 8, 2048, 512, True) > 0
+    assert q.moe_decode_workspace_bytes(256, 8, 64, 512, True) == 0     # H below 128
+    assert q.moe_decode_workspace_bytes(256, 8, 2048, 96, True) == 0    # I not a multiple of 64
+    assert _decode(H=192 + 8) == q.MOEQ4_ERR_SHAPE
+    assert _decode(k=17) == q.MOEQ4_ERR_SHAPE                           # k > E
+    assert _decode(E=128, k=65) == q.MOEQ4_ERR_UNSUPPORTED               # k > 64
+    assert _decode(logits=None) == q.MOEQ4_ERR_NULL
+    assert _decode(out=None) == q.MOEQ4_ERR_NULL
+    assert _decode(sh_gu_q=FAKE) == q.MOEQ4_ERR_NULL                    # shared: all six or none
+    assert _decode(x=FAKE + 4) == q.MOEQ4_ERR_ALIGN
+    assert _decode(ws_bytes=16) == q.MOEQ4_ERR_WORKSPACE
+    assert _decode(E=128, k=64, I=1088) == q.MOEQ4_ERR_UNSUPPORTED      # h of 32 experts: beyond LDS
