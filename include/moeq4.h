@@ -175,6 +175,50 @@ int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
                         const int32_t* num_blocks, int max_blocks, int block_rows, uint16_t* Y,
                         void* stream);
 
+/* Bytes of device scratch moe_expert_ffn_q4 needs (0 on invalid sizes):
+ * 2*T*k*(I + H) bytes, plus 2*T*I with a shared expert, rounded up.
+ * shared: 1 when a shared expert is given, else 0. */
+size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int shared);
+
+/* The MoE layer's expert FFNs over a batch of T tokens, after moe_route
+ * (section "Reduce intermediate and state traffic": the two input projections
+ * run with their gated activation, the output projection with the routing
+ * score and the shared expert's result; section "Qwen creates three workload
+ * shapes": one shared expert sees every token):
+ *   for each assignment a = t*k + j routed to expert e (rows grouped by expert
+ *   through perm / blocks, as for moe_grouped_gemm_q4):
+ *     h_a = bf16( silu(G_e x_t) * (U_e x_t) ),  G_e / U_e = rows [0, I) / [I, 2I)
+ *                                               of e's gate+up matrix [2I, H]
+ *   and with a shared expert (no routing, weight 1) h_t likewise;
+ *     out[t] = bf16( D_sh h_t + sum_j w_a * D_e h_a )
+ * silu(z) = z / (1 + exp(-z)) in fp32 from the fp32 projections; every weight
+ * is rebuilt exactly as bf16(scale * code + bias); fp32 accumulation.  Each
+ * weighted routed term is held once in the workspace as fp16 of term * 2^-8
+ * (11-bit significand, |term| up to ~1.6e7) before the combine, which adds in
+ * a fixed order (shared term, then j ascending): the result is the same run
+ * after run.
+ *
+ * In:  X        uint16 (bf16) [T, H]   token activations.
+ *      gu_*     [E, 2I, H] gate+up weights, dn_* [E, H, I] down weights, both
+ *               in the tiled layout of moe_prepack_q4.
+ *      sh_*     the shared expert's [1, 2I, H] and [1, H, I] matrices (tiled):
+ *               all six given or all six NULL.
+ *      topk_w, perm, blocks, num_blocks   from moe_route(T, E, k, block_rows).
+ *      max_blocks   >= moe_max_blocks(T, E, k, block_rows).
+ *      workspace    moe_expert_ffn_workspace_bytes(...) bytes, 16-byte
+ *               aligned; no initial contents needed.
+ * Out: out      uint16 (bf16) [T, H]; must not overlap the inputs.
+ * Sizes: as moe_grouped_gemm_q4 for both matrices; H and I multiples of 64;
+ *        T*k*I*2, T*H*2 and the weight arrays below 2^31 bytes. */
+int moe_expert_ffn_q4(const uint16_t* X, int T, int H, int I, int E, int k, const uint8_t* gu_codes_t,
+                      const uint16_t* gu_scales_t, const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                      const uint16_t* dn_scales_t, const uint16_t* dn_biases_t, const uint8_t* sh_gu_codes_t,
+                      const uint16_t* sh_gu_scales_t, const uint16_t* sh_gu_biases_t,
+                      const uint8_t* sh_dn_codes_t, const uint16_t* sh_dn_scales_t,
+                      const uint16_t* sh_dn_biases_t, const float* topk_w, const int32_t* perm,
+                      const int32_t* blocks, const int32_t* num_blocks, int max_blocks, int block_rows,
+                      uint16_t* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of device scratch moe_decode_ffn_q4 needs (0 on invalid sizes).
  * shared: 1 when a shared expert is given, else 0. */
 size_t moe_decode_workspace_bytes(int E, int k, int H, int I, int shared);

@@ -43,6 +43,9 @@ SIGNATURES = {
     "moe_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_q4": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                  _vp, _vp]),
+    "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "moe_expert_ffn_q4": (_i, [_vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz,
+                                                                       _vp]),
     "moe_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_decode_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -141,6 +144,21 @@ def moe_grouped_gemm_q4(X, T, K, N, E, k, codes_t, scales_t, biases_t, perm, blo
         _p(num_blocks), max_blocks, block_rows, _p(Y), _stream(stream)))
 
 
+def moe_expert_ffn_workspace_bytes(T: int, H: int, I: int, E: int, k: int, shared: bool) -> int:
+    return int(lib().moe_expert_ffn_workspace_bytes(T, H, I, E, k, int(bool(shared))))
+
+
+def moe_expert_ffn_q4(X, T, H, I, E, k, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
+                      dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t, sh_dn_codes_t, sh_dn_scales_t,
+                      sh_dn_biases_t, topk_w, perm, blocks, num_blocks, max_blocks, block_rows, out, workspace,
+                      ws_bytes, stream=None):
+    _ok("moe_expert_ffn_q4", lib().moe_expert_ffn_q4(
+        _p(X), T, H, I, E, k, _p(gu_codes_t), _p(gu_scales_t), _p(gu_biases_t), _p(dn_codes_t), _p(dn_scales_t),
+        _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t), _p(sh_dn_codes_t),
+        _p(sh_dn_scales_t), _p(sh_dn_biases_t), _p(topk_w), _p(perm), _p(blocks), _p(num_blocks), max_blocks,
+        block_rows, _p(out), _p(workspace), int(ws_bytes), _stream(stream)))
+
+
 def moe_decode_workspace_bytes(E: int, k: int, H: int, I: int, shared: bool) -> int:
     return int(lib().moe_decode_workspace_bytes(E, k, H, I, int(bool(shared))))
 
@@ -233,4 +251,29 @@ def decode_ffn(logits, x, k: int, gu, dn, sh_gu=None, sh_dn=None, bufs=None, str
     sd = sh_dn if shared else (None, None, None)
     moe_decode_ffn_q4(logits, x, E, k, H, I, *gu, *dn, *sg, *sd, b["topk_ids"], b["topk_w"], b["out"],
                       b["workspace"], b["ws_bytes"], stream)
+    return b
+
+
+def alloc_ffn(T: int, H: int, I: int, E: int, k: int, shared: bool = True, device="cuda"):
+    """Output and workspace tensors for moe_expert_ffn_q4."""
+    ws = moe_expert_ffn_workspace_bytes(T, H, I, E, k, shared)
+    return dict(out=torch.empty((max(T, 1), H), dtype=torch.int16, device=device),
+                workspace=torch.empty(max(ws, 1), dtype=torch.uint8, device=device), ws_bytes=ws)
+
+
+def expert_ffn(X, k: int, rt, gu, dn, sh_gu=None, sh_dn=None, bufs=None, stream=None):
+    """The expert FFNs of a batch (moe_expert_ffn_q4).  ``X`` bf16 bits [T, H];
+    ``rt`` the routing buffers of route(); ``gu`` / ``dn`` = prepack() tuples of
+    the [E, 2I, H] and [E, H, I] matrices; ``sh_gu`` / ``sh_dn`` the shared
+    expert's or None.  Returns the buffer dict (``out`` holds bf16 bits [T, H])."""
+    T, H = X.shape
+    E, I2, _ = gu[0].shape
+    I = I2 // 2
+    shared = sh_gu is not None
+    b = bufs or alloc_ffn(T, H, I, E, k, shared, device=X.device)
+    sg = sh_gu if shared else (None, None, None)
+    sd = sh_dn if shared else (None, None, None)
+    moe_expert_ffn_q4(X, T, H, I, E, k, *gu, *dn, *sg, *sd, rt["topk_w"], rt["perm"], rt["blocks"],
+                      rt["num_blocks"], rt["max_blocks"], rt["block_rows"], b["out"], b["workspace"],
+                      b["ws_bytes"], stream)
     return b

@@ -196,4 +196,60 @@ int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int 
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 
+static int check_ffn_shape(int T, int H, int I, int E, int k) {
+  const int rc = check_routing_shape(T, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOEQ4_ERR_SHAPE;
+  const long long A = (long long)T * k;
+  if ((long long)T * H * 2 >= (1LL << 31) || A * I * 2 >= (1LL << 31) ||
+      (long long)E * 2 * I * (H / 2) >= (1LL << 31) || (long long)E * H * (I / 2) >= (1LL << 31))
+    return MOEQ4_ERR_SHAPE;
+  return MOEQ4_OK;
+}
+
+size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int shared) {
+  if (check_ffn_shape(T, H, I, E, k) != MOEQ4_OK) return 0;
+  return ffn_plan(T, H, I, k, shared != 0).ws_bytes;
+}
+
+int moe_expert_ffn_q4(const uint16_t* X, int T, int H, int I, int E, int k, const uint8_t* gu_codes_t,
+                      const uint16_t* gu_scales_t, const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                      const uint16_t* dn_scales_t, const uint16_t* dn_biases_t, const uint8_t* sh_gu_codes_t,
+                      const uint16_t* sh_gu_scales_t, const uint16_t* sh_gu_biases_t,
+                      const uint8_t* sh_dn_codes_t, const uint16_t* sh_dn_scales_t,
+                      const uint16_t* sh_dn_biases_t, const float* topk_w, const int32_t* perm,
+                      const int32_t* blocks, const int32_t* num_blocks, int max_blocks, int block_rows,
+                      uint16_t* out, void* workspace, size_t ws_bytes, void* stream) {
+  const void* sh[] = {sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                      sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t};
+  int nsh = 0;
+  for (const void* p : sh) nsh += p != nullptr;
+  if (nsh != 0 && nsh != 6) return MOEQ4_ERR_NULL;
+  const int shared = nsh == 6;
+  int rc = check_ffn_shape(T, H, I, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  const int bm = resolve_block_rows(T, E, k, block_rows);
+  if (bm <= 0) return bm;
+  const int bound = moe_max_blocks(T, E, k, bm);
+  if (bound < 0) return bound;
+  if (max_blocks < bound) return MOEQ4_ERR_SHAPE;
+  if (T == 0) return MOEQ4_OK;
+  if (!X || !gu_codes_t || !gu_scales_t || !gu_biases_t || !dn_codes_t || !dn_scales_t || !dn_biases_t ||
+      !topk_w || !perm || !blocks || !num_blocks || !out || !workspace)
+    return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {X, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t, dn_biases_t,
+                        topk_w, perm, blocks, num_blocks, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOEQ4_ERR_ALIGN;
+  for (const void* p : sh)
+    if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
+  const FfnPlan plan = ffn_plan(T, H, I, k, shared);
+  if (ws_bytes < plan.ws_bytes) return MOEQ4_ERR_WORKSPACE;
+  const hipError_t err = ffn_launch(plan, X, T, H, I, E, k, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t,
+                                    dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                                    sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, topk_w, perm, blocks,
+                                    num_blocks, max_blocks, bm, out, workspace, (hipStream_t)stream);
+  return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
 }  // extern "C"

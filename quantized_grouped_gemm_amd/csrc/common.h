@@ -26,6 +26,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
+// The FFN keeps the weighted routed terms between its two projections as fp16
+// holding value * 2^-8 (11-bit significand, range to ~1.7e7): the combine then
+// adds terms rounded 8x finer than bf16 at the same bytes.
+constexpr float kTermScale = 1.f / 256.f;
+
+__device__ __forceinline__ uint16_t term_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)(v * kTermScale));  // round to nearest even
+}
+
+__device__ __forceinline__ float term_value(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16) * (1.f / kTermScale);
+}
+
 // ---- wave64 reductions through DPP; the full result lands in lane 63 and is
 // ---- broadcast with readlane (uniform, lives in an SGPR).
 template <int CTRL, int ROW_MASK = 0xF>
@@ -159,6 +172,33 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
                         int32_t* perm, int32_t* inv_perm, int32_t* blocks, int32_t* num_blocks,
                         void* workspace, hipStream_t stream);
 
+// One grouped-GEMM launch over tiled group-wise affine 4-bit weights.
+enum GemmEpi {
+  kEpiPlain = 0,    // Y[p][n] = bf16(acc)                         (sorted row p)
+  kEpiSwiglu = 1,   // Y[p][n] = bf16(silu(acc_n) * acc_{n+N/2})    (N/2 output columns)
+  kEpiScale = 2,    // Y[perm[p]][n] = term_bits(topk_w[perm[p]] * acc)  (assignment order)
+  kEpiCombine = 3,  // Y[p][n] = bf16(acc + sum_j term_value(Dw[p*k + j][n]))  (dense rows = tokens)
+};
+
+struct GemmArgs {
+  const uint16_t* X;  // activations: xrows rows of K bf16
+  int xrows;
+  int K, N, E, A, k;  // N weight rows per expert; A rows in the block-map space
+  const uint8_t* Wt;  // tiled weights of E experts
+  const uint16_t* St;
+  const uint16_t* Bt;
+  const int32_t* gather;      // non-null: row p reads X[gather[p] / k]; null: X[p]
+  const int32_t* blocks;      // block map; null: dense BM-row blocks over A rows of expert 0
+  const int32_t* num_blocks;  // device count of block-map entries
+  uint16_t* Y;                // output, row stride ldy
+  int ldy;
+  const int32_t* perm;        // kEpiScale
+  const float* topk_w;        // kEpiScale
+  const uint16_t* Dw;         // kEpiCombine: [rows * k][ldy]
+};
+
+hipError_t gemm_launch(const GemmArgs& a, int epi, int block_rows, int max_blocks, hipStream_t stream);
+
 hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wt,
                           const uint16_t* St, const uint16_t* Bt, const int32_t* perm,
                           const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
@@ -178,6 +218,21 @@ hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_
                          const uint16_t* sh_gu_s, const uint16_t* sh_gu_b, const uint8_t* sh_dn_q,
                          const uint16_t* sh_dn_s, const uint16_t* sh_dn_b, int32_t* ids_out, float* w_out,
                          uint16_t* out, void* workspace, hipStream_t stream);
+
+struct FfnPlan {
+  size_t ws_h, ws_hs, ws_dw, ws_bytes;  // workspace: routed h [T*k][I], shared h [T][I], Dw [T*k][H]
+  int bm_shared;                        // dense block height of the shared expert
+};
+
+FfnPlan ffn_plan(int T, int H, int I, int k, bool shared);
+
+hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, int E, int k,
+                      const uint8_t* gu_q, const uint16_t* gu_s, const uint16_t* gu_b, const uint8_t* dn_q,
+                      const uint16_t* dn_s, const uint16_t* dn_b, const uint8_t* sh_gu_q, const uint16_t* sh_gu_s,
+                      const uint16_t* sh_gu_b, const uint8_t* sh_dn_q, const uint16_t* sh_dn_s,
+                      const uint16_t* sh_dn_b, const float* topk_w, const int32_t* perm, const int32_t* blocks,
+                      const int32_t* num_blocks, int max_blocks, int BM, uint16_t* out, void* workspace,
+                      hipStream_t stream);
 
 hipError_t prepack_launch(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases,
                           int E, int N, int K, uint8_t* codes_t, uint16_t* scales_t,

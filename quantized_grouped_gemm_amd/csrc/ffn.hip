@@ -1,0 +1,167 @@
+// ffn.hip -- the routed experts' FFN plus the shared expert over a prefill
+// batch, as four grouped-GEMM launches on the caller's stream.
+//
+// Perplexity Engineering, "Optimizing on-device inference for Apple Silicon":
+//   section "Reduce intermediate and state traffic": the two input projections
+//   run with their gated activation fused, and the output projection with its
+//   routing score and the shared expert's result;
+//   section "Qwen creates three workload shapes": the shared expert processes
+//   every token next to the routed ones;
+//   section "Dequantize weights during matrix multiplication": all four
+//   products rebuild the 4-bit weights on chip.
+//
+//   1. routed gate+up   h[p]  = bf16(silu(G x) * (U x))   rows p in expert-sorted order,
+//                                                      x = X[perm[p] / k]
+//   2. shared gate+up   hs[t] = bf16(silu(Gs x_t) * (Us x_t))   dense, all T tokens
+//   3. routed down      Dw[a] = w_a * (D h[p]),  a = perm[p]: rows back in
+//                                                      assignment order t*k + j,
+//                                                      kept as fp16 of value*2^-8
+//   4. shared down      out[t] = bf16(Ds hs[t] + sum_j Dw[t*k + j])   (the combine
+//                        runs in the epilogue; without a shared expert a small
+//                        kernel sums the k rows)
+// The combine adds in a fixed order (the shared term, then j ascending), so the
+// result does not depend on scheduling.
+#include "common.h"
+
+namespace moeq4 {
+
+constexpr int kCombineThreads = 256;
+
+// out[t][n] = bf16(sum_j term_value(Dw[t*k + j][n])), 8 columns per thread
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t* __restrict__ Dw, int T, int H, int k,
+                                                             uint16_t* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * kCombineThreads + threadIdx.x;  // 8-column piece
+  const int pieces = H / 8;
+  if (i >= (long long)T * pieces) return;
+  const int t = (int)(i / pieces), c8 = (int)(i % pieces) * 8;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const uint4 v = *(const uint4*)(Dw + ((size_t)t * k + j) * H + c8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s[2 * q] += term_value(w[q] & 0xFFFFu);
+      s[2 * q + 1] += term_value(w[q] >> 16);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = (uint32_t)f32_to_bf16_bits(s[2 * q]) | ((uint32_t)f32_to_bf16_bits(s[2 * q + 1]) << 16);
+  *(uint4*)(out + (size_t)t * H + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+FfnPlan ffn_plan(int T, int H, int I, int k, bool shared) {
+  FfnPlan p{};
+  const size_t A = (size_t)T * k;
+  p.ws_h = 0;
+  p.ws_hs = align256(A * I * 2);
+  p.ws_dw = p.ws_hs + (shared ? align256((size_t)T * I * 2) : 0);
+  p.ws_bytes = p.ws_dw + align256(A * H * 2);
+  // dense block height of the shared expert: as for one expert holding all T rows
+  int bm = 16;
+  while (bm < 128 && bm < (5LL * T + 3) / 4) bm <<= 1;
+  p.bm_shared = bm;
+  return p;
+}
+
+hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, int E, int k,
+                      const uint8_t* gu_q, const uint16_t* gu_s, const uint16_t* gu_b, const uint8_t* dn_q,
+                      const uint16_t* dn_s, const uint16_t* dn_b, const uint8_t* sh_gu_q, const uint16_t* sh_gu_s,
+                      const uint16_t* sh_gu_b, const uint8_t* sh_dn_q, const uint16_t* sh_dn_s,
+                      const uint16_t* sh_dn_b, const float* topk_w, const int32_t* perm, const int32_t* blocks,
+                      const int32_t* num_blocks, int max_blocks, int BM, uint16_t* out, void* workspace,
+                      hipStream_t stream) {
+  const bool shared = sh_gu_q != nullptr;
+  const int A = T * k;
+  char* ws = (char*)workspace;
+  uint16_t* h = (uint16_t*)(ws + p.ws_h);
+  uint16_t* hs = (uint16_t*)(ws + p.ws_hs);
+  uint16_t* Dw = (uint16_t*)(ws + p.ws_dw);
+  const int sh_blocks = (T + p.bm_shared - 1) / p.bm_shared;
+
+  // 1. routed gate+up with SwiGLU
+  GemmArgs g{};
+  g.X = X;
+  g.xrows = T;
+  g.K = H;
+  g.N = 2 * I;
+  g.E = E;
+  g.A = A;
+  g.k = k;
+  g.Wt = gu_q;
+  g.St = gu_s;
+  g.Bt = gu_b;
+  g.gather = perm;
+  g.blocks = blocks;
+  g.num_blocks = num_blocks;
+  g.Y = h;
+  g.ldy = I;
+  hipError_t err = gemm_launch(g, kEpiSwiglu, BM, max_blocks, stream);
+  if (err != hipSuccess) return err;
+
+  // 2. shared gate+up, dense over the tokens
+  if (shared) {
+    GemmArgs s = g;
+    s.E = 1;
+    s.A = T;
+    s.k = 1;
+    s.Wt = sh_gu_q;
+    s.St = sh_gu_s;
+    s.Bt = sh_gu_b;
+    s.gather = nullptr;
+    s.blocks = nullptr;
+    s.num_blocks = nullptr;
+    s.Y = hs;
+    err = gemm_launch(s, kEpiSwiglu, p.bm_shared, sh_blocks, stream);
+    if (err != hipSuccess) return err;
+  }
+
+  // 3. routed down, scaled by the routing weight, rows back in assignment order
+  GemmArgs d{};
+  d.X = h;
+  d.xrows = A;
+  d.K = I;
+  d.N = H;
+  d.E = E;
+  d.A = A;
+  d.k = k;
+  d.Wt = dn_q;
+  d.St = dn_s;
+  d.Bt = dn_b;
+  d.gather = nullptr;
+  d.blocks = blocks;
+  d.num_blocks = num_blocks;
+  d.Y = Dw;
+  d.ldy = H;
+  d.perm = perm;
+  d.topk_w = topk_w;
+  err = gemm_launch(d, kEpiScale, BM, max_blocks, stream);
+  if (err != hipSuccess) return err;
+
+  // 4. shared down + combine, or the combine alone
+  if (shared) {
+    GemmArgs s{};
+    s.X = hs;
+    s.xrows = T;
+    s.K = I;
+    s.N = H;
+    s.E = 1;
+    s.A = T;
+    s.k = k;  // fan-in of the combine
+    s.Wt = sh_dn_q;
+    s.St = sh_dn_s;
+    s.Bt = sh_dn_b;
+    s.Y = out;
+    s.ldy = H;
+    s.Dw = Dw;
+    return gemm_launch(s, kEpiCombine, p.bm_shared, sh_blocks, stream);
+  }
+  const long long pieces = (long long)T * (H / 8);
+  return launch("k_combine", (const void*)&k_combine, dim3((unsigned)((pieces + kCombineThreads - 1) / kCombineThreads)),
+                dim3(kCombineThreads), 0, stream, (const uint16_t*)Dw, T, H, k, out);
+}
+
+}  // namespace moeq4

@@ -103,14 +103,73 @@ struct Stage {
 
 constexpr int kXcds = 8;  // MI355X: workgroup i of a launch runs on XCD i % 8
 
-template <int BM, int NF, bool CQ, int S, int WAUX, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(
-    const uint16_t* __restrict__ X, int T, int K, int N, int E, int A, int k,
-    const uint8_t* __restrict__ Wt, const uint16_t* __restrict__ St,
-    const uint16_t* __restrict__ Bt, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ blocks, const int32_t* __restrict__ num_blocks,
-    uint16_t* __restrict__ Y) {
+// Decoded block-map entry of one workgroup; false for a malformed entry.
+__device__ __forceinline__ bool gemm_block(const GemmArgs& a, int BM, int blk, int& e, int& row0, int& rows) {
+  if (a.blocks) {
+    e = a.blocks[4 * blk + 0];
+    row0 = a.blocks[4 * blk + 1];
+    rows = min(a.blocks[4 * blk + 2], BM);
+  } else {  // dense: BM-row blocks over all A rows of expert 0
+    e = 0;
+    row0 = blk * BM;
+    rows = min(BM, a.A - row0);
+  }
+  return !(e < 0 || e >= a.E || row0 < 0 || rows <= 0 || row0 + rows > a.A);
+}
+
+__device__ __forceinline__ int gemm_nblocks(const GemmArgs& a, int BM) {
+  return a.blocks ? *a.num_blocks : (a.A + BM - 1) / BM;
+}
+
+// byte offset of sorted row p's activations in X
+__device__ __forceinline__ int gemm_xrow(const GemmArgs& a, int p) {
+  return (a.gather ? a.gather[p] / a.k : p) * a.K * 2;
+}
+
+// Epilogue of one output row (sorted row p): per-row values are read once.
+template <int EPI>
+struct EpiRow {
+  uint16_t* y;    // output row
+  float w;        // kEpiScale: routing weight of the row's assignment
+  const uint16_t* dw;  // kEpiCombine: the token's first weighted expert row
+  __device__ __forceinline__ EpiRow(const GemmArgs& a, int p) {
+    if constexpr (EPI == kEpiScale) {
+      const int as = a.perm[p];
+      y = a.Y + (size_t)as * a.ldy;
+      w = a.topk_w[as];
+    } else {
+      y = a.Y + (size_t)p * a.ldy;
+      w = 1.f;
+    }
+    if constexpr (EPI == kEpiCombine) dw = a.Dw + (size_t)p * a.k * a.ldy;
+    else dw = nullptr;
+  }
+  // value v of output column n (g, u for kEpiSwiglu)
+  __device__ __forceinline__ void store(const GemmArgs& a, int n, float v, float u = 0.f) const {
+    if constexpr (EPI == kEpiSwiglu) {
+      y[n] = f32_to_bf16_bits(v / (1.f + expf(-v)) * u);
+    } else if constexpr (EPI == kEpiScale) {
+      y[n] = term_bits(w * v);
+    } else if constexpr (EPI == kEpiCombine) {
+      float s = v;
+      for (int j = 0; j < a.k; ++j) s += term_value(dw[(size_t)j * a.ldy + n]);
+      y[n] = f32_to_bf16_bits(s);
+    } else {
+      y[n] = f32_to_bf16_bits(v);
+    }
+  }
+};
+
+template <int BM, int NF, bool CQ, int S, int WAUX, int WAVES, int EPI>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
+  static_assert(EPI != kEpiSwiglu || NF % 2 == 0, "SwiGLU pairs gate and up fragments");
   constexpr int MF = BM / 16;
+  constexpr int NFO = EPI == kEpiSwiglu ? NF / 2 : NF;  // output fragments per wave
+  const int K = a.K, N = a.N, E = a.E;
+  const uint8_t* __restrict__ Wt = a.Wt;
+  const uint16_t* __restrict__ St = a.St;
+  const uint16_t* __restrict__ Bt = a.Bt;
+  const int NOUT = EPI == kEpiSwiglu ? N / 2 : N;  // output columns
   constexpr int NTHR = WAVES * 64;
   constexpr int XP = (BM * (kKC / 8) + NTHR - 1) / NTHR;  // 16-B activation pieces per thread per stage
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kXRow];
@@ -119,8 +178,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(
   // (block, N tile), so the N tiles of a block -- which gather the same
   // activation rows -- and the blocks of one expert -- which stream the same
   // weights -- share that XCD's L2.  Tasks past the device-side block count exit.
-  const int ntiles = (N + WAVES * NF * 16 - 1) / (WAVES * NF * 16);
-  const int total = *num_blocks * ntiles;
+  const int ntiles = (NOUT + WAVES * NFO * 16 - 1) / (WAVES * NFO * 16);
+  const int total = gemm_nblocks(a, BM) * ntiles;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
   if (slot >= per_xcd) return;
@@ -128,16 +187,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(
   if (task >= total) return;
   const int blk = task / ntiles;
   const int ntile = task - blk * ntiles;
-  const int e = blocks[4 * blk + 0];
-  const int row0 = blocks[4 * blk + 1];
-  const int rows = min(blocks[4 * blk + 2], BM);
-  if (e < 0 || e >= E || row0 < 0 || rows <= 0 || row0 + rows > A) return;  // malformed entry
+  int e, row0, rows;
+  if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int quarter = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_wave = ntile * (WAVES * NF * 16) + wave * NF * 16;
+  const int n_wave = ntile * (WAVES * NFO * 16) + wave * NFO * 16;  // first output column of the wave
   const int G = K / kGroup;
   const int nfull = G >> 1;            // chunks holding two groups
   const bool odd_tail = (G & 1) != 0;  // one more chunk with a single group
@@ -155,26 +212,30 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(
   const __amdgpu_buffer_rsrc_t bsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Bt + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
   const __amdgpu_buffer_rsrc_t xsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, T * K * 2, kBufFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, a.xrows * K * 2, kBufFlags);
 
-  // Fragments past N still load (from the last tile, so every address stays
-  // inside the expert's weights) and run their MFMAs, but are not stored.
-  const int nf_live = min(NF, max(0, (N - n_wave) / 16));
-  const int t0 = n_wave / 16;
+  // Fragments past the output columns still load (from the last tile, so every
+  // address stays inside the expert's weights) and run their MFMAs, but are not
+  // stored.  SwiGLU: fragment f < NF/2 holds gate columns, f + NF/2 the up
+  // columns NOUT further on.
+  const int nf_live = min(NFO, max(0, (NOUT - n_wave) / 16));
   int tile[NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) tile[f] = min(t0 + f, NT - 1);
+  for (int f = 0; f < NF; ++f) {
+    const int n = f < NFO ? n_wave + f * 16 : NOUT + n_wave + (f - NFO) * 16;
+    tile[f] = min(n / 16, NT - 1);
+  }
 
-  // per-thread activation pieces: byte offset of (token row, 16-B column).
+  // per-thread activation pieces: byte offset of (activation row, 16-B column).
   // Rows past the block get an offset past the buffer: the buffer load returns
   // zeros without touching memory.
-  const int x_oob = T * K * 2;
+  const int x_oob = a.xrows * K * 2;
   int xoff[XP];
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int p = tid + i * NTHR;
     const int r = p >> 4, col = p & 15;
-    xoff[i] = (r < rows && p < BM * 16) ? (perm[row0 + r] / k) * K * 2 + col * 16 : x_oob;
+    xoff[i] = (r < rows && p < BM * 16) ? gemm_xrow(a, row0 + r) + col * 16 : x_oob;
   }
 
   Stage<NF, XP> st[S];
@@ -341,13 +402,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(
   for (int r = 0; r < MF; ++r) {
     if (r >= mfa) break;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f >= nf_live) break;
-      const int n = n_wave + f * 16 + (lane & 15);
+    for (int i = 0; i < 4; ++i) {
+      const int row = r * 16 + quarter * 4 + i;
+      if (row >= rows) continue;
+      const EpiRow<EPI> er(a, row0 + row);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = r * 16 + quarter * 4 + i;
-        if (row < rows) Y[(size_t)(row0 + row) * N + n] = f32_to_bf16_bits(acc[r][f][i]);
+      for (int f = 0; f < NFO; ++f) {
+        if (f >= nf_live) break;
+        const int n = n_wave + f * 16 + (lane & 15);
+        if constexpr (EPI == kEpiSwiglu) er.store(a, n, acc[r][f][i], acc[r][f + NFO][i]);
+        else er.store(a, n, acc[r][f][i]);
       }
     }
   }
@@ -365,21 +429,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(
 // K indices 32h + [0,32) in each of the chunk's two groups.  K-step s4 of group
 // g then takes K indices g*64 + 32h + 8*s4 + [0,8) from lane half h, for both
 // operands, so every K-step stays inside one scale group.
-template <int BM, int NF32, int S, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(
-    const uint16_t* __restrict__ X, int T, int K, int N, int E, int A, int k,
-    const uint8_t* __restrict__ Wt, const uint16_t* __restrict__ St,
-    const uint16_t* __restrict__ Bt, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ blocks, const int32_t* __restrict__ num_blocks,
-    uint16_t* __restrict__ Y) {
+template <int BM, int NF32, int S, int WAVES, int EPI>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
+  static_assert(EPI != kEpiSwiglu || NF32 % 2 == 0, "SwiGLU pairs gate and up fragments");
   constexpr int MF32 = BM / 32;
   constexpr int NTHR = WAVES * 64;
   constexpr int XP = (BM * (kKC / 8) + NTHR - 1) / NTHR;
-  constexpr int TILE_N = WAVES * NF32 * 32;
+  constexpr int NFO = EPI == kEpiSwiglu ? NF32 / 2 : NF32;  // output fragments per wave
+  constexpr int TILE_N = WAVES * NFO * 32;                  // output columns per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kXRow];
+  const int K = a.K, N = a.N;
+  const uint8_t* __restrict__ Wt = a.Wt;
+  const uint16_t* __restrict__ St = a.St;
+  const uint16_t* __restrict__ Bt = a.Bt;
+  const int NOUT = EPI == kEpiSwiglu ? N / 2 : N;
 
-  const int ntiles = (N + TILE_N - 1) / TILE_N;
-  const int total = *num_blocks * ntiles;
+  const int ntiles = (NOUT + TILE_N - 1) / TILE_N;
+  const int total = gemm_nblocks(a, BM) * ntiles;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
   if (slot >= per_xcd) return;
@@ -387,17 +453,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(
   if (task >= total) return;
   const int blk = task / ntiles;
   const int ntile = task - blk * ntiles;
-  const int e = blocks[4 * blk + 0];
-  const int row0 = blocks[4 * blk + 1];
-  const int rows = min(blocks[4 * blk + 2], BM);
-  if (e < 0 || e >= E || row0 < 0 || rows <= 0 || row0 + rows > A) return;  // malformed entry
+  int e, row0, rows;
+  if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int half = lane >> 5;   // K half inside a K-step
   const int col = lane & 31;    // column inside a 32-column tile
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_wave = ntile * TILE_N + wave * NF32 * 32;
+  const int n_wave = ntile * TILE_N + wave * NFO * 32;  // first output column of the wave
   const int G = K / kGroup;
   const int nfull = G >> 1;
   const bool odd_tail = (G & 1) != 0;
@@ -411,23 +475,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(
   const __amdgpu_buffer_rsrc_t bsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Bt + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
   const __amdgpu_buffer_rsrc_t xsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, T * K * 2, kBufFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, a.xrows * K * 2, kBufFlags);
 
   // this lane's 16-row tile per 32-column tile (clamped inside the expert: columns
-  // past N load the last tile and are never stored) and its row inside that tile
+  // past the output load the last tile and are never stored) and its row inside
+  // that tile.  SwiGLU: fragment f < NF32/2 holds gate columns, f + NF32/2 the up
+  // columns NOUT further on.
   int tile16[NF32];
 #pragma unroll
-  for (int f = 0; f < NF32; ++f) tile16[f] = min((n_wave + f * 32 + col) >> 4, NT - 1);
+  for (int f = 0; f < NF32; ++f) {
+    const int n = f < NFO ? n_wave + f * 32 + col : NOUT + n_wave + (f - NFO) * 32 + col;
+    tile16[f] = min(n >> 4, NT - 1);
+  }
   const int r16 = col & 15;
-  const int nf_live = min(NF32, max(0, (N - n_wave + 31) / 32));
+  const int nf_live = min(NFO, max(0, (NOUT - n_wave + 31) / 32));
 
-  const int x_oob = T * K * 2;  // rows past the block: the load returns zeros, no traffic
+  const int x_oob = a.xrows * K * 2;  // rows past the block: the load returns zeros, no traffic
   int xoff[XP];
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int p = tid + i * NTHR;
     const int r = p >> 4, c16 = p & 15;
-    xoff[i] = (r < rows && p < BM * 16) ? (perm[row0 + r] / k) * K * 2 + c16 * 16 : x_oob;
+    xoff[i] = (r < rows && p < BM * 16) ? gemm_xrow(a, row0 + r) + c16 * 16 : x_oob;
   }
 
   struct St32 {
@@ -550,14 +619,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(
   for (int r = 0; r < MF32; ++r) {
     if (r >= mfa) break;
 #pragma unroll
-    for (int f = 0; f < NF32; ++f) {
-      if (f >= nf_live) break;
-      const int n = n_wave + f * 32 + col;
-      if (n >= N) continue;
+    for (int i = 0; i < 16; ++i) {
+      const int row = r * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+      if (row >= rows) continue;
+      const EpiRow<EPI> er(a, row0 + row);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = r * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (row < rows) Y[(size_t)(row0 + row) * N + n] = f32_to_bf16_bits(acc[r][f][i]);
+      for (int f = 0; f < NFO; ++f) {
+        if (f >= nf_live) break;
+        const int n = n_wave + f * 32 + col;
+        if (n >= NOUT) continue;
+        if constexpr (EPI == kEpiSwiglu) er.store(a, n, acc[r][f][i], acc[r][f + NFO][i]);
+        else er.store(a, n, acc[r][f][i]);
       }
     }
   }
@@ -568,65 +640,99 @@ namespace {
 struct GemmVariant {
   const char* name;
   int bm;
-  int tile_n;  // columns per workgroup
+  int epi;
+  int tile_n;  // output columns per workgroup
   int waves;   // waves per workgroup
   const void* fn;
 };
 
-#define MOEQ4_GEMM_VARIANT(BM, NF, CQ, S, WAUX, WAVES)                          \
-  {"bm" #BM "_nf" #NF "_" #CQ "_s" #S "_a" #WAUX "_w" #WAVES, BM, WAVES * NF * 16, WAVES, \
-   (const void*)&k_gemm_q4<BM, NF, CQ, S, WAUX, WAVES>}
-#define MOEQ4_GEMM_W32(BM, NF32, S, WAVES)                                      \
-  {"w32_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, WAVES * NF32 * 32, WAVES,   \
-   (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES>}
+#define MOEQ4_GEMM_VARIANT(BM, NF, CQ, S, WAUX, WAVES, EPI)                                      \
+  {"bm" #BM "_nf" #NF "_" #CQ "_s" #S "_a" #WAUX "_w" #WAVES, BM, EPI,                         \
+   WAVES * NF * 16 / (EPI == kEpiSwiglu ? 2 : 1), WAVES, (const void*)&k_gemm_q4<BM, NF, CQ, S, WAUX, WAVES, EPI>}
+#define MOEQ4_GEMM_W32(BM, NF32, S, WAVES, EPI)                                                  \
+  {"w32_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, EPI, WAVES * NF32 * 32 / (EPI == kEpiSwiglu ? 2 : 1), \
+   WAVES, (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES, EPI>}
 
-// The first entry of each block height is its default.  WAUX is the cache
-// policy of the weight loads (2 = non-temporal: streamed weights do not
-// evict the activation rows from L2).
+// The first entry of each (block height, epilogue) is its default, from sweeps
+// on MI355X.  WAUX is the cache policy of the weight loads.  The single
+// projection (kEpiPlain) feeds short blocks with the codes (CQ); the FFN
+// epilogues rebuild every weight exactly (DQ), as the FFN chains two
+// projections and the rebuilt weights' bf16 rounding then matters.
 const GemmVariant kVariants[] = {
-    // defaults (first entry of each block height), from sweeps on MI355X
-    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 8),
-    MOEQ4_GEMM_VARIANT(32, 2, true, 3, 0, 8),
-    MOEQ4_GEMM_W32(64, 2, 2, 4),
-    MOEQ4_GEMM_W32(128, 1, 2, 8),
+    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 8, kEpiPlain),
+    MOEQ4_GEMM_VARIANT(32, 2, true, 3, 0, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiPlain),
+    // FFN: gate+up with SwiGLU, down scaled by the routing weight, shared down + combine
+    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiSwiglu),
+    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiSwiglu),
+    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiSwiglu),
+    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiSwiglu),
+    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiScale),
+    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiScale),
+    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiScale),
+    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiScale),
+    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiCombine),
+    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiCombine),
+    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiCombine),
+    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiCombine),
     // alternatives for tuning sweeps
-    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 4),
-    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 4),
-    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 8),
-    MOEQ4_GEMM_VARIANT(32, 2, true, 4, 0, 8),
-    MOEQ4_GEMM_W32(128, 2, 2, 8),
-    MOEQ4_GEMM_W32(128, 2, 2, 4),
-    MOEQ4_GEMM_W32(64, 2, 2, 8),
+    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 4, kEpiPlain),
+    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 4, kEpiPlain),
+    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 8, kEpiPlain),
+    MOEQ4_GEMM_VARIANT(32, 2, true, 4, 0, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiPlain),
+    MOEQ4_GEMM_W32(64, 2, 2, 8, kEpiPlain),
 };
 #undef MOEQ4_GEMM_VARIANT
 #undef MOEQ4_GEMM_W32
 
-// Tile choice by block height; MOEQ4_GEMM_VARIANT=<name> (same block height)
-// overrides it for tuning sweeps.
-const GemmVariant* pick_variant(int bm) {
+// Tile choice by block height and epilogue; MOEQ4_GEMM_VARIANT=<name> (same
+// block height and epilogue) overrides it for tuning sweeps.
+const GemmVariant* pick_variant(int bm, int epi) {
   static const char* forced = getenv("MOEQ4_GEMM_VARIANT");
   if (forced)
     for (const GemmVariant& v : kVariants)
-      if (v.bm == bm && strcmp(v.name, forced) == 0) return &v;
+      if (v.bm == bm && v.epi == epi && strcmp(v.name, forced) == 0) return &v;
   for (const GemmVariant& v : kVariants)
-    if (v.bm == bm) return &v;
+    if (v.bm == bm && v.epi == epi) return &v;
   return nullptr;
 }
 
 }  // namespace
 
+hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipStream_t stream) {
+  if (max_blocks <= 0) return hipSuccess;
+  const GemmVariant* v = pick_variant(BM, epi);
+  if (!v) return hipErrorInvalidValue;
+  const int nout = epi == kEpiSwiglu ? a.N / 2 : a.N;
+  const long long tasks = (long long)max_blocks * ((nout + v->tile_n - 1) / v->tile_n);
+  const dim3 grid((unsigned)((tasks + kXcds - 1) / kXcds * kXcds));
+  return launch("k_gemm_q4", v->fn, grid, dim3(v->waves * 64), 0, stream, a);
+}
+
 hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wt,
                           const uint16_t* St, const uint16_t* Bt, const int32_t* perm,
                           const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
                           int BM, uint16_t* Y, hipStream_t stream) {
-  if (max_blocks <= 0) return hipSuccess;
-  const GemmVariant* v = pick_variant(BM);
-  if (!v) return hipErrorInvalidValue;
-  const int tile_n = v->tile_n;
-  const long long tasks = (long long)max_blocks * ((N + tile_n - 1) / tile_n);
-  const dim3 grid((unsigned)((tasks + kXcds - 1) / kXcds * kXcds));
-  return launch("k_gemm_q4", v->fn, grid, dim3(v->waves * 64), 0, stream, X, T, K, N, E, T * k, k,
-                Wt, St, Bt, perm, blocks, num_blocks, Y);
+  GemmArgs a{};
+  a.X = X;
+  a.xrows = T;
+  a.K = K;
+  a.N = N;
+  a.E = E;
+  a.A = T * k;
+  a.k = k;
+  a.Wt = Wt;
+  a.St = St;
+  a.Bt = Bt;
+  a.gather = perm;
+  a.blocks = blocks;
+  a.num_blocks = num_blocks;
+  a.Y = Y;
+  a.ldy = N;
+  return gemm_launch(a, kEpiPlain, BM, max_blocks, stream);
 }
 
 }  // namespace moeq4

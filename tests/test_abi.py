@@ -150,3 +150,26 @@ def test_decode_validation():
     assert _decode(x=FAKE + 4) == q.MOEQ4_ERR_ALIGN
     assert _decode(ws_bytes=16) == q.MOEQ4_ERR_WORKSPACE
     assert _decode(E=128, k=64, I=1088) == q.MOEQ4_ERR_UNSUPPORTED      # h of 32 experts: beyond LDS
+
+
+def _ffn(**kw):
+    a = dict(X=FAKE, T=8, H=256, I=128, E=16, k=2, gu_q=FAKE, gu_s=FAKE, gu_b=FAKE, dn_q=FAKE, dn_s=FAKE,
+             dn_b=FAKE, sh_gu_q=None, sh_gu_s=None, sh_gu_b=None, sh_dn_q=None, sh_dn_s=None, sh_dn_b=None,
+             topk_w=FAKE, perm=FAKE, blocks=FAKE, num_blocks=FAKE, max_blocks=1000, block_rows=16, out=FAKE,
+             workspace=FAKE, ws_bytes=q.moe_expert_ffn_workspace_bytes(8, 256, 128, 16, 2, False), stream=None)
+    a.update(kw)
+    return q.lib().moe_expert_ffn_q4(*a.values())
+
+
+def test_ffn_validation():
+    assert q.moe_expert_ffn_workspace_bytes(4096, 2048, 512, 256, 8, True) >= 2 * 4096 * 8 * (512 + 2048)
+    assert q.moe_expert_ffn_workspace_bytes(8, 100, 128, 16, 2, True) == 0   # H not a multiple of 64
+    assert _ffn(I=96) == q.MOEQ4_ERR_SHAPE
+    assert _ffn(k=17) == q.MOEQ4_ERR_SHAPE
+    assert _ffn(block_rows=24) == q.MOEQ4_ERR_SHAPE
+    assert _ffn(max_blocks=1) == q.MOEQ4_ERR_SHAPE
+    assert _ffn(perm=None) == q.MOEQ4_ERR_NULL
+    assert _ffn(sh_dn_b=FAKE) == q.MOEQ4_ERR_NULL                            # shared: all six or none
+    assert _ffn(out=FAKE + 2) == q.MOEQ4_ERR_ALIGN
+    assert _ffn(ws_bytes=64) == q.MOEQ4_ERR_WORKSPACE
+    assert _ffn(T=0, X=None, out=None) == q.MOEQ4_OK                         # nothing to do: no launch
