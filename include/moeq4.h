@@ -176,7 +176,7 @@ int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
                         void* stream);
 
 /* Bytes of device scratch moe_expert_ffn_q4 needs (0 on invalid sizes):
- * 2*T*k*(I + H) bytes, plus 2*T*I with a shared expert, rounded up.
+ * 2*T*k*(I + H) bytes, plus 2*T*(I + H) with a shared expert, rounded up.
  * shared: 1 when a shared expert is given, else 0. */
 size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int shared);
 
@@ -193,10 +193,10 @@ size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int sha
  *     out[t] = bf16( D_sh h_t + sum_j w_a * D_e h_a )
  * silu(z) = z / (1 + exp(-z)) in fp32 from the fp32 projections; every weight
  * is rebuilt exactly as bf16(scale * code + bias); fp32 accumulation.  Each
- * weighted routed term is held once in the workspace as fp16 of term * 2^-8
- * (11-bit significand, |term| up to ~1.6e7) before the combine, which adds in
- * a fixed order (shared term, then j ascending): the result is the same run
- * after run.
+ * weighted routed term and the shared term are held once in the workspace as
+ * fp16 of term * 2^-8 (11-bit significand, |term| up to ~1.6e7) before the
+ * combine, which adds in a fixed order (shared term, then j ascending): the
+ * result is the same run after run.
  *
  * In:  X        uint16 (bf16) [T, H]   token activations.
  *      gu_*     [E, 2I, H] gate+up weights, dn_* [E, H, I] down weights, both

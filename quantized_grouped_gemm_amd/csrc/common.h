@@ -177,7 +177,7 @@ enum GemmEpi {
   kEpiPlain = 0,    // Y[p][n] = bf16(acc)                         (sorted row p)
   kEpiSwiglu = 1,   // Y[p][n] = bf16(silu(acc_n) * acc_{n+N/2})    (N/2 output columns)
   kEpiScale = 2,    // Y[perm[p]][n] = term_bits(topk_w[perm[p]] * acc)  (assignment order)
-  kEpiCombine = 3,  // Y[p][n] = bf16(acc + sum_j term_value(Dw[p*k + j][n]))  (dense rows = tokens)
+  kEpiTerm = 3,     // Y[p][n] = term_bits(acc)
 };
 
 struct GemmArgs {
@@ -194,7 +194,6 @@ struct GemmArgs {
   int ldy;
   const int32_t* perm;        // kEpiScale
   const float* topk_w;        // kEpiScale
-  const uint16_t* Dw;         // kEpiCombine: [rows * k][ldy]
 };
 
 hipError_t gemm_launch(const GemmArgs& a, int epi, int block_rows, int max_blocks, hipStream_t stream);
@@ -220,7 +219,8 @@ hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_
                          uint16_t* out, void* workspace, hipStream_t stream);
 
 struct FfnPlan {
-  size_t ws_h, ws_hs, ws_dw, ws_bytes;  // workspace: routed h [T*k][I], shared h [T][I], Dw [T*k][H]
+  // workspace: routed h [T*k][I], shared h [T][I], routed terms [T*k][H], shared term [T][H]
+  size_t ws_h, ws_hs, ws_dw, ws_dsh, ws_bytes;
   int bm_shared;                        // dense block height of the shared expert
 };
 

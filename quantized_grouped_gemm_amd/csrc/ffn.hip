@@ -16,34 +16,38 @@
 //   3. routed down      Dw[a] = w_a * (D h[p]),  a = perm[p]: rows back in
 //                                                      assignment order t*k + j,
 //                                                      kept as fp16 of value*2^-8
-//   4. shared down      out[t] = bf16(Ds hs[t] + sum_j Dw[t*k + j])   (the combine
-//                        runs in the epilogue; without a shared expert a small
-//                        kernel sums the k rows)
-// The combine adds in a fixed order (the shared term, then j ascending), so the
-// result does not depend on scheduling.
+//   4. shared down      Dsh[t] = Ds hs[t], kept like Dw
+//   5. combine          out[t] = bf16(Dsh[t] + sum_j Dw[t*k + j]): 16-byte reads of
+//                        every term, added in a fixed order (the shared term,
+//                        then j ascending), so the result does not depend on
+//                        scheduling.
 #include "common.h"
 
 namespace moeq4 {
 
 constexpr int kCombineThreads = 256;
 
-// out[t][n] = bf16(sum_j term_value(Dw[t*k + j][n])), 8 columns per thread
-__global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t* __restrict__ Dw, int T, int H, int k,
+// out[t][n] = bf16(Dsh[t][n] + sum_j Dw[t*k + j][n]) over the stored terms
+// (Dsh may be null), 8 columns per thread
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t* __restrict__ Dw,
+                                                             const uint16_t* __restrict__ Dsh, int T, int H, int k,
                                                              uint16_t* __restrict__ out) {
   const long long i = (long long)blockIdx.x * kCombineThreads + threadIdx.x;  // 8-column piece
   const int pieces = H / 8;
   if (i >= (long long)T * pieces) return;
   const int t = (int)(i / pieces), c8 = (int)(i % pieces) * 8;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const uint4 v = *(const uint4*)(Dw + ((size_t)t * k + j) * H + c8);
+  auto add = [&](const uint16_t* src) {
+    const uint4 v = *(const uint4*)src;
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       s[2 * q] += term_value(w[q] & 0xFFFFu);
       s[2 * q + 1] += term_value(w[q] >> 16);
     }
-  }
+  };
+  if (Dsh) add(Dsh + (size_t)t * H + c8);
+  for (int j = 0; j < k; ++j) add(Dw + ((size_t)t * k + j) * H + c8);
   uint32_t o[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -59,7 +63,8 @@ FfnPlan ffn_plan(int T, int H, int I, int k, bool shared) {
   p.ws_h = 0;
   p.ws_hs = align256(A * I * 2);
   p.ws_dw = p.ws_hs + (shared ? align256((size_t)T * I * 2) : 0);
-  p.ws_bytes = p.ws_dw + align256(A * H * 2);
+  p.ws_dsh = p.ws_dw + align256(A * H * 2);
+  p.ws_bytes = p.ws_dsh + (shared ? align256((size_t)T * H * 2) : 0);
   // dense block height of the shared expert: as for one expert holding all T rows
   int bm = 16;
   while (bm < 128 && bm < (5LL * T + 3) / 4) bm <<= 1;
@@ -80,6 +85,7 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   uint16_t* h = (uint16_t*)(ws + p.ws_h);
   uint16_t* hs = (uint16_t*)(ws + p.ws_hs);
   uint16_t* Dw = (uint16_t*)(ws + p.ws_dw);
+  uint16_t* Dsh = shared ? (uint16_t*)(ws + p.ws_dsh) : nullptr;
   const int sh_blocks = (T + p.bm_shared - 1) / p.bm_shared;
 
   // 1. routed gate+up with SwiGLU
@@ -141,7 +147,7 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   err = gemm_launch(d, kEpiScale, BM, max_blocks, stream);
   if (err != hipSuccess) return err;
 
-  // 4. shared down + combine, or the combine alone
+  // 4. shared down, dense over the tokens
   if (shared) {
     GemmArgs s{};
     s.X = hs;
@@ -150,18 +156,20 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
     s.N = H;
     s.E = 1;
     s.A = T;
-    s.k = k;  // fan-in of the combine
+    s.k = 1;
     s.Wt = sh_dn_q;
     s.St = sh_dn_s;
     s.Bt = sh_dn_b;
-    s.Y = out;
+    s.Y = Dsh;
     s.ldy = H;
-    s.Dw = Dw;
-    return gemm_launch(s, kEpiCombine, p.bm_shared, sh_blocks, stream);
+    err = gemm_launch(s, kEpiTerm, p.bm_shared, sh_blocks, stream);
+    if (err != hipSuccess) return err;
   }
+
+  // 5. combine
   const long long pieces = (long long)T * (H / 8);
   return launch("k_combine", (const void*)&k_combine, dim3((unsigned)((pieces + kCombineThreads - 1) / kCombineThreads)),
-                dim3(kCombineThreads), 0, stream, (const uint16_t*)Dw, T, H, k, out);
+                dim3(kCombineThreads), 0, stream, (const uint16_t*)Dw, (const uint16_t*)Dsh, T, H, k, out);
 }
 
 }  // namespace moeq4

@@ -69,20 +69,30 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
 // (bits 4p..4p+3) holding c0,c2,c4,c6,c1,c3,c5,c7 for p = 0..7, so that
 // (dword >> 4i) & 0x000F000F is the pair (c_2i, c_2i+1) in the two 16-bit halves.
 
-// exact rebuild of 8 codes: bf16(s*q + b), natural K order
+// two fp32 values as one packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
+}
+
+// exact rebuild of 8 codes: bf16(s*q + b), natural K order.  The two masked
+// words are made opaque to the compiler so that each code converts with one
+// v_cvt_f32_ubyteN of its byte (the compiler would otherwise re-extract every
+// nibble with its own shift and mask).
 __device__ __forceinline__ bf16x8 rebuild_dq(uint32_t wd, float s, float b) {
-  const uint32_t lo = wd & 0x0F0F0F0Fu;         // bytes: c0, c4, c1, c5
-  const uint32_t hi = (wd >> 4) & 0x0F0F0F0Fu;  // bytes: c2, c6, c3, c7
-  bf16x8 v;
-  v[0] = (__bf16)__builtin_fmaf((float)(lo & 0xFF), s, b);
-  v[1] = (__bf16)__builtin_fmaf((float)((lo >> 16) & 0xFF), s, b);
-  v[2] = (__bf16)__builtin_fmaf((float)(hi & 0xFF), s, b);
-  v[3] = (__bf16)__builtin_fmaf((float)((hi >> 16) & 0xFF), s, b);
-  v[4] = (__bf16)__builtin_fmaf((float)((lo >> 8) & 0xFF), s, b);
-  v[5] = (__bf16)__builtin_fmaf((float)(lo >> 24), s, b);
-  v[6] = (__bf16)__builtin_fmaf((float)((hi >> 8) & 0xFF), s, b);
-  v[7] = (__bf16)__builtin_fmaf((float)(hi >> 24), s, b);
-  return v;
+  uint32_t lo = wd & 0x0F0F0F0Fu;         // bytes: c0, c4, c1, c5
+  uint32_t hi = (wd >> 4) & 0x0F0F0F0Fu;  // bytes: c2, c6, c3, c7
+  asm("" : "+v"(lo), "+v"(hi));
+  const float c0 = __builtin_fmaf((float)(lo & 0xFF), s, b);
+  const float c4 = __builtin_fmaf((float)((lo >> 8) & 0xFF), s, b);
+  const float c1 = __builtin_fmaf((float)((lo >> 16) & 0xFF), s, b);
+  const float c5 = __builtin_fmaf((float)(lo >> 24), s, b);
+  const float c2 = __builtin_fmaf((float)(hi & 0xFF), s, b);
+  const float c6 = __builtin_fmaf((float)((hi >> 8) & 0xFF), s, b);
+  const float c3 = __builtin_fmaf((float)((hi >> 16) & 0xFF), s, b);
+  const float c7 = __builtin_fmaf((float)(hi >> 24), s, b);
+  return as_bf16x8(pk_bf16(c0, c1), pk_bf16(c2, c3), pk_bf16(c4, c5), pk_bf16(c6, c7));
 }
 
 // 8 codes as the exact bf16 values 128+q, natural K order; `one28` holds
@@ -131,7 +141,6 @@ template <int EPI>
 struct EpiRow {
   uint16_t* y;    // output row
   float w;        // kEpiScale: routing weight of the row's assignment
-  const uint16_t* dw;  // kEpiCombine: the token's first weighted expert row
   __device__ __forceinline__ EpiRow(const GemmArgs& a, int p) {
     if constexpr (EPI == kEpiScale) {
       const int as = a.perm[p];
@@ -141,19 +150,15 @@ struct EpiRow {
       y = a.Y + (size_t)p * a.ldy;
       w = 1.f;
     }
-    if constexpr (EPI == kEpiCombine) dw = a.Dw + (size_t)p * a.k * a.ldy;
-    else dw = nullptr;
   }
   // value v of output column n (g, u for kEpiSwiglu)
-  __device__ __forceinline__ void store(const GemmArgs& a, int n, float v, float u = 0.f) const {
+  __device__ __forceinline__ void store(int n, float v, float u = 0.f) const {
     if constexpr (EPI == kEpiSwiglu) {
       y[n] = f32_to_bf16_bits(v / (1.f + expf(-v)) * u);
     } else if constexpr (EPI == kEpiScale) {
       y[n] = term_bits(w * v);
-    } else if constexpr (EPI == kEpiCombine) {
-      float s = v;
-      for (int j = 0; j < a.k; ++j) s += term_value(dw[(size_t)j * a.ldy + n]);
-      y[n] = f32_to_bf16_bits(s);
+    } else if constexpr (EPI == kEpiTerm) {
+      y[n] = term_bits(v);
     } else {
       y[n] = f32_to_bf16_bits(v);
     }
@@ -410,8 +415,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
       for (int f = 0; f < NFO; ++f) {
         if (f >= nf_live) break;
         const int n = n_wave + f * 16 + (lane & 15);
-        if constexpr (EPI == kEpiSwiglu) er.store(a, n, acc[r][f][i], acc[r][f + NFO][i]);
-        else er.store(a, n, acc[r][f][i]);
+        if constexpr (EPI == kEpiSwiglu) er.store(n, acc[r][f][i], acc[r][f + NFO][i]);
+        else er.store(n, acc[r][f][i]);
       }
     }
   }
@@ -563,7 +568,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][f][i] = 0.f;
 
-  auto compute = [&](int buf, const St32& s, int ngroups) {
+  // MFA: the number of filled 32-row tiles, a compile-time constant so that the
+  // LDS reads and MFMAs of a K-step are straight-line code the compiler can
+  // schedule (one copy of the loop per value)
+  auto compute = [&](auto mfa_c, int buf, const St32& s, int ngroups) {
+    constexpr int MFA = decltype(mfa_c)::value;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       if (gi >= ngroups) break;
@@ -578,40 +587,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
           bfr[f] = rebuild_dq(s.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
         }
         const uint16_t* xb = &xs[buf][col * kXRow + gi * 64 + half * 32 + s4 * 8];
+        bf16x8 av[MFA];
 #pragma unroll
-        for (int r = 0; r < MF32; ++r) {
-          if (r >= mfa) break;
-          const bf16x8 a = *(const bf16x8*)(xb + r * 32 * kXRow);
+        for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kXRow);
+#pragma unroll
+        for (int r = 0; r < MFA; ++r)
 #pragma unroll
           for (int f = 0; f < NF32; ++f)
-            acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[f], acc[r][f], 0, 0, 0);
-        }
+            acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[r], bfr[f], acc[r][f], 0, 0, 0);
       }
     }
   };
 
-  if (nfull > 0) {
+  auto run = [&](auto mfa_c) {
+    if (nfull > 0) {
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) load(st[s], s);
-    store_x(st[0], 0);
-    __syncthreads();
-    for (int c0 = 0; c0 < nfull; c0 += S) {
+      for (int s = 0; s < S - 1; ++s) load(st[s], s);
+      store_x(st[0], 0);
+      __syncthreads();
+      for (int c0 = 0; c0 < nfull; c0 += S) {
 #pragma unroll
-      for (int u = 0; u < S; ++u) {
-        const int c = c0 + u;
-        load(st[(u + S - 1) % S], c + S - 1);
-        store_x(st[(u + 1) % S], (c + 1) & 1);
-        if (c < nfull) compute(c & 1, st[u], 2);
-        __syncthreads();
+        for (int u = 0; u < S; ++u) {
+          const int c = c0 + u;
+          load(st[(u + S - 1) % S], c + S - 1);
+          store_x(st[(u + 1) % S], (c + 1) & 1);
+          if (c < nfull) compute(mfa_c, c & 1, st[u], 2);
+          __syncthreads();
+        }
       }
     }
-  }
-  if (odd_tail) {
-    load_tail(st[0]);
-    store_x(st[0], 0);
-    __syncthreads();
-    compute(0, st[0], 1);
-  }
+    if (odd_tail) {
+      load_tail(st[0]);
+      store_x(st[0], 0);
+      __syncthreads();
+      compute(mfa_c, 0, st[0], 1);
+    }
+  };
+  static_assert(MF32 >= 1 && MF32 <= 4, "row tiles per block");
+  if (mfa == MF32) run(std::integral_constant<int, MF32>{});
+  else if (MF32 > 1 && mfa == 1) run(std::integral_constant<int, 1>{});
+  else if (MF32 > 2 && mfa == 2) run(std::integral_constant<int, (MF32 > 2 ? 2 : 1)>{});
+  else run(std::integral_constant<int, (MF32 > 3 ? 3 : 1)>{});
 
   // epilogue: 32x32 accumulator layout -- lane holds column lane&31 and rows
   // 8*(i/4) + 4*half + i%4 (i = 0..15) of each tile
@@ -628,8 +644,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
         if (f >= nf_live) break;
         const int n = n_wave + f * 32 + col;
         if (n >= NOUT) continue;
-        if constexpr (EPI == kEpiSwiglu) er.store(a, n, acc[r][f][i], acc[r][f + NFO][i]);
-        else er.store(a, n, acc[r][f][i]);
+        if constexpr (EPI == kEpiSwiglu) er.store(n, acc[r][f][i], acc[r][f + NFO][i]);
+        else er.store(n, acc[r][f][i]);
       }
     }
   }
@@ -672,10 +688,10 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiScale),
     MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiScale),
     MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiScale),
-    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiCombine),
-    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiCombine),
-    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiCombine),
-    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiCombine),
+    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiTerm),
+    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiTerm),
+    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiTerm),
+    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiTerm),
     // alternatives for tuning sweeps
     MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 4, kEpiPlain),
     MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 4, kEpiPlain),
@@ -684,6 +700,13 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiPlain),
     MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiPlain),
     MOEQ4_GEMM_W32(64, 2, 2, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 1, 3, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 1, 4, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 2, 3, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 1, 3, 4, kEpiPlain),
+    MOEQ4_GEMM_W32(64, 2, 3, 4, kEpiPlain),
+    MOEQ4_GEMM_W32(64, 2, 4, 4, kEpiPlain),
+    MOEQ4_GEMM_W32(64, 1, 3, 8, kEpiPlain),
 };
 #undef MOEQ4_GEMM_VARIANT
 #undef MOEQ4_GEMM_W32
