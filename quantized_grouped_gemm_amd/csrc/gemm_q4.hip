@@ -439,10 +439,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   static_assert(EPI != kEpiSwiglu || NF32 % 2 == 0, "SwiGLU pairs gate and up fragments");
   constexpr int MF32 = BM / 32;
   constexpr int NTHR = WAVES * 64;
-  constexpr int XP = (BM * (kKC / 8) + NTHR - 1) / NTHR;
   constexpr int NFO = EPI == kEpiSwiglu ? NF32 / 2 : NF32;  // output fragments per wave
   constexpr int TILE_N = WAVES * NFO * 32;                  // output columns per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kXRow];
+  // Activations reach LDS by DMA (buffer_load ... lds): each wave instruction
+  // fills 1 KB = 4 rows of 256 B.  In row r, 16-byte slot s holds the row's
+  // 16-byte column s ^ (r & 15), so that the 32 rows an MFMA operand read
+  // touches sit in distinct banks.
+  constexpr int IPW = BM * 16 / 64 / WAVES;  // DMA instructions per wave per chunk
+  static_assert(IPW * 64 * WAVES == BM * 16, "rows split evenly over the waves");
+  (void)NTHR;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kKC];
   const int K = a.K, N = a.N;
   const uint8_t* __restrict__ Wt = a.Wt;
   const uint16_t* __restrict__ St = a.St;
@@ -496,18 +502,33 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   const int nf_live = min(NFO, max(0, (NOUT - n_wave + 31) / 32));
 
   const int x_oob = a.xrows * K * 2;  // rows past the block: the load returns zeros, no traffic
-  int xoff[XP];
+  // this lane's DMA source per instruction: row rb + lane/16, 16-byte column
+  // (lane & 15) ^ (row & 15) of it
+  int xoff[IPW];
 #pragma unroll
-  for (int i = 0; i < XP; ++i) {
-    const int p = tid + i * NTHR;
-    const int r = p >> 4, c16 = p & 15;
-    xoff[i] = (r < rows && p < BM * 16) ? gemm_xrow(a, row0 + r) + c16 * 16 : x_oob;
+  for (int i = 0; i < IPW; ++i) {
+    const int r = 4 * (wave * IPW + i) + (lane >> 4);
+    const int c16 = (lane & 15) ^ (r & 15);
+    xoff[i] = r < rows ? gemm_xrow(a, row0 + r) + c16 * 16 : x_oob;
   }
+  typedef __attribute__((address_space(3))) void lds_void;
+  // activations of chunk c (K values [128c, 128c + 128)) into LDS buffer buf.
+  // The tail chunk of an odd G has only 8 columns: the other slots get the
+  // out-of-range offset (the range check covers the vector offset only, so the
+  // row must not be overrun through the chunk offset).
+  auto dma_x = [&](int c, int buf, bool tail) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = 4 * (wave * IPW + i) + (lane >> 4);
+      const int off = (tail && ((lane & 15) ^ (r & 15)) >= 8) ? x_oob : xoff[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (lds_void*)&xs[buf][4 * (wave * IPW + i) * kKC], 16, off,
+                                               c * kKC * 2, 0, 0);
+    }
+  };
 
   struct St32 {
     u32x4 w[NF32][2];   // quarter slices 2h and 2h+1
     uint32_t s[NF32], b[NF32];
-    uint4 x[XP];
   };
   St32 st[S];
   auto load = [&](St32& s, int c) {
@@ -520,11 +541,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
       const int gbase = ((cl * NT + tile16[f]) * 32 + 2 * r16) * 2;
       s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, gbase, 0, 0);
       s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, gbase, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[i], cl * kKC * 2, 0);
-      s.x[i] = make_uint4(r[0], r[1], r[2], r[3]);
     }
   };
   auto load_tail = [&](St32& s) {
@@ -540,23 +556,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
       const int gbase = (c * NT * 32 + tile16[f] * 16 + r16) * 2;
       s.s[f] = __builtin_amdgcn_raw_buffer_load_b16(ssrc, gbase, 0, 0);
       s.b[f] = __builtin_amdgcn_raw_buffer_load_b16(bsrc, gbase, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const int c16 = (tid + i * NTHR) & 15;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c16 < 8) {
-        const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(xsrc, xoff[i], c * kKC * 2, 0);
-        v = make_uint4(r[0], r[1], r[2], r[3]);
-      }
-      s.x[i] = v;
-    }
-  };
-  auto store_x = [&](const St32& s, int buf) {
-#pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const int p = tid + i * NTHR;
-      if (XP * NTHR == BM * 16 || p < BM * 16) *(uint4*)(&xs[buf][(p >> 4) * kXRow + (p & 15) * 8]) = s.x[i];
     }
   };
 
@@ -586,10 +585,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
           const float bv = gi ? __uint_as_float(s.b[f] & 0xFFFF0000u) : __uint_as_float(s.b[f] << 16);
           bfr[f] = rebuild_dq(s.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
         }
-        const uint16_t* xb = &xs[buf][col * kXRow + gi * 64 + half * 32 + s4 * 8];
+        // row col (+32 per row tile), 16-byte column gi*8 + half*4 + s4, swizzled
+        const uint16_t* xb = &xs[buf][col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8)];
         bf16x8 av[MFA];
 #pragma unroll
-        for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kXRow);
+        for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kKC);
 #pragma unroll
         for (int r = 0; r < MFA; ++r)
 #pragma unroll
@@ -599,18 +599,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
     }
   };
 
+  // Pipeline over the full chunks: at iteration c the DMA of chunk c+1's
+  // activations (into the LDS buffer chunk c-1 used) and the weight loads of
+  // chunk c+S-1 go out, then chunk c's MFMAs run; the barrier that ends the
+  // iteration waits for those loads, so their latency hides behind the MFMAs.
+  // Loads past the last chunk re-read it (clamped) and are not used.
   auto run = [&](auto mfa_c) {
     if (nfull > 0) {
 #pragma unroll
       for (int s = 0; s < S - 1; ++s) load(st[s], s);
-      store_x(st[0], 0);
+      dma_x(0, 0, false);
       __syncthreads();
       for (int c0 = 0; c0 < nfull; c0 += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
           const int c = c0 + u;
+          dma_x(min(c + 1, nfull - 1), (c + 1) & 1, false);
           load(st[(u + S - 1) % S], c + S - 1);
-          store_x(st[(u + 1) % S], (c + 1) & 1);
+          // keep the loads ahead of the MFMAs (the scheduler would otherwise
+          // sink them to the end of the iteration and expose their latency)
+          asm volatile("" ::: "memory");
           if (c < nfull) compute(mfa_c, c & 1, st[u], 2);
           __syncthreads();
         }
@@ -618,7 +626,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
     }
     if (odd_tail) {
       load_tail(st[0]);
-      store_x(st[0], 0);
+      dma_x(nfull, 0, true);
       __syncthreads();
       compute(mfa_c, 0, st[0], 1);
     }
