@@ -1,21 +1,30 @@
 """Benchmark of the MoE routing + Q4 grouped-GEMM hot path on one MI355X.
 
-One step = moe_route (top-k, histogram, scan, block map, scatter) followed by
-moe_grouped_gemm_q4 over the routed rows, on the prefill-chunk workload
-(T=512 tokens, E=256 experts, top-8, K=2048 -> N=512, group-64 affine 4-bit
-weights).  Inputs are seeded synthetic arrays already resident in HBM when
-the timed region starts.
+Default (the prefill-chunk workload: T=512 tokens, E=256 experts, top-8,
+K=2048 -> N=512, group-64 affine 4-bit weights): one step = moe_route (top-k,
+histogram, scan, block map, scatter) followed by moe_grouped_gemm_q4 over the
+routed rows.  Other workloads:
+  --workload 4   the same step at T=16384 with Zipf-skewed routing
+  --workload 3   one step = moe_route + moe_expert_ffn_q4 (gate+up, SwiGLU,
+                 down, weighted combine, shared expert) at T=4096, H=2048, I=512
+  --workload 5   one step = one batch-1 decode step (moe_decode_ffn_q4:
+                 routing, 8 of 256 experts + the shared expert) with fresh
+                 logits and activations every step
+Inputs are seeded synthetic arrays already resident in HBM when the timed
+region starts.
 
 Cold weights: consecutive steps use different resident copies of the layer's
-weights (like consecutive MoE layers), at least 1 GiB in all, so every GEMM
-reads its weights from HBM rather than from the 256 MB Infinity Cache.
+weights (like consecutive MoE layers), so every step reads its weights from
+HBM rather than from the 256 MB Infinity Cache: at least 1 GiB of copies for
+the prefill workloads, and for decode enough copies that more than 256 MB of
+other weights are read between two uses of a copy.
 
-Prints one JSON line with the throughput of the whole step, the roofline of
-the grouped-GEMM kernel (timed with HIP events on its launch stream; HBM
-traffic from the committed rocprofv3 counter summary when it matches the
-kernel source) and the CPU oracle timed on the host cores.
+Prints one JSON line: the throughput of the whole step, the roofline of the
+dominant kernel (timed with HIP events on its launch stream; HBM traffic from
+the committed rocprofv3 counter summary when it matches the kernel source)
+and the CPU oracle timed on the host cores.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 2|4|1]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 2|4|3|5|1]
                     [--block-rows BM] [--layers L] [--no-cpu-baseline] [--cpu-reps R]
 """
 from __future__ import annotations
@@ -34,6 +43,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE q4 grouped-GEMM TFLOP/s + weight GB/s at T=512/4096; % of roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+DATA = ("synthetic (seeded numpy PCG64; logits N(0,1){skew}, activations bf16 N(0,1), uniform 4-bit codes, "
+        "bf16 scale |N(0,0.02)|, bias -8*scale + N(0,0.002))")
 
 
 def q4_bytes(N: int, K: int) -> int:
@@ -57,71 +68,70 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(p, w, bm, reps):
-    import oracle
-    t_all = []
-    for _ in range(reps):
+def roofline(flops: float, alg_bytes: float, kernel_ms: float, kernel: str, workload: str) -> dict:
+    gbps = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    tflops = flops / (kernel_ms * 1e-3) / 1e12
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if flops / alg_bytes < ridge:
+        roof = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / BF16_PEAK_TFLOPS}
+    roof["traffic"] = load_traffic(kernel, workload)
+    roof["kernel"] = kernel
+    roof["algorithmic_bytes_per_launch"] = alg_bytes
+    roof["algorithmic_flops_per_launch"] = flops
+    return roof
+
+
+class Timer:
+    """Times exactly `steps` calls of step(i, ev) back to back between two
+    synchronisations; ev holds HIP events recorded on the launch stream."""
+
+    def __init__(self, torch, nev):
+        self.torch, self.nev = torch, nev
+
+    def run(self, step, warmup, steps):
+        torch = self.torch
+        for i in range(warmup):
+            step(i, None)
+        torch.cuda.synchronize()
+        ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(self.nev)) for _ in range(steps)]
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ids, _ = oracle.topk_softmax(p.logits, w.k)
-        rt = oracle.route(ids, w.E, bm)
-        oracle.grouped_gemm_q4(p.X, w.k, p.Wq, p.S, p.B, rt["perm"], rt["offsets"])
-        t_all.append(time.perf_counter() - t0)
-    t = float(np.median(t_all))
-    flops = 2.0 * w.T * w.k * w.N * w.K
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"the whole step (route + grouped GEMM) of the same workload, median of {reps} runs, "
-                      f"{t:.2f} s each"}
+        for i in range(steps):
+            step(warmup + i, ev[i])
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+        seg = [np.array([e[j].elapsed_time(e[j + 1]) for e in ev]) for j in range(self.nev - 1)]
+        return ms_per_step, seg
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--block-rows", type=int, default=0)
-    ap.add_argument("--layers", type=int, default=0, help="resident weight copies used in turn (0: >= 1 GiB)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=40)
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the path is single-GPU "
-                                   "(expert-parallel sharding is described in DESIGN.md)",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+def base_line(args, w, value, ms_per_step, config, roof):
+    return {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": DATA.format(skew=f" + Zipf expert bias, alpha {w.skew_alpha}" if w.skew_alpha else ""),
+        "config": config, "roofline": roof,
+    }
 
-    import torch
-    import quantized_grouped_gemm_amd as q
-    import workloads as W
 
-    w = W.WORKLOADS[args.workload]
-    assert not w.ffn, "bench.py times the single-projection workloads (1, 2, 4)"
+# ------------------------------------------------------------ single projection
+def bench_gemm(args, torch, q, W, w, d):
     p = W.make_problem(w)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    def d(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            a = a.view(np.int16)
-        return torch.from_numpy(a).to(dev)
-
     T, E, k, K, N = w.T, w.E, w.k, w.K, w.N
-    # Cold weights, as in a model: consecutive MoE layers each read their own
-    # weights.  `layers` resident copies (>= 1 GiB in all, four times the
-    # 256 MB Infinity Cache) are used in turn, so a step's weights were last
-    # touched a whole rotation earlier and come from HBM.
     w_layer = E * q4_bytes(N, K)
     layers = args.layers or max(2, -(-(1 << 30) // w_layer))
     packed0 = q.prepack(d(p.Wq), d(p.S), d(p.B))     # one-time re-tiling at load time
     packs = [packed0] + [tuple(t.clone() for t in packed0) for _ in range(layers - 1)]
     logits, X = d(p.logits), d(p.X)
-    rt = q.alloc_route(T, E, k, args.block_rows, device=dev)
-    Y = torch.empty((T * k, N), dtype=torch.int16, device=dev)
+    rt = q.alloc_route(T, E, k, args.block_rows, device=X.device)
+    Y = torch.empty((T * k, N), dtype=torch.int16, device=X.device)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, ev):
         if ev is not None:
             ev[0].record(stream)
         q.route(logits, k, bufs=rt, stream=stream)
@@ -131,76 +141,219 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed: exactly `steps` steps back to back between two synchronisations;
-    # HIP events on the launch stream split each step into route and GEMM
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, ev[i])
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    ev_step_ms = float(np.mean([a.elapsed_time(c) for a, b, c in ev]))
-    route_ms = float(np.mean([a.elapsed_time(b) for a, b, c in ev]))
-    gemm_all = np.array([b.elapsed_time(c) for a, b, c in ev])
+    ms_per_step, (route_all, gemm_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
     gemm_ms = float(gemm_all.mean())
-
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     A = T * k
     flops = 2.0 * A * N * K
     w_bytes = touched * q4_bytes(N, K)
     alg_bytes = w_bytes + T * K * 2 + A * N * 2
-    achieved_gbps = alg_bytes / (gemm_ms * 1e-3) / 1e9
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    hbm_bound = flops / alg_bytes < ridge
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved_gbps / HBM_PEAK_GBPS}
-    else:
-        roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": gemm_tflops / BF16_PEAK_TFLOPS}
-    roof["traffic"] = load_traffic("k_gemm_q4", w.name)
-    roof["kernel"] = "k_gemm_q4"
-    roof["algorithmic_bytes_per_launch"] = alg_bytes
-    roof["algorithmic_flops_per_launch"] = flops
-
-    out = {
-        "metric": METRIC,
-        "value": flops / (ms_per_step * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded numpy PCG64; logits N(0,1)" + (f" + Zipf expert bias, alpha {w.skew_alpha}"
-                if w.skew_alpha else "") + ", activations bf16 N(0,1), uniform 4-bit codes, bf16 scale "
-                "|N(0,0.02)|, bias -8*scale + N(0,0.002))",
-        "config": {"workload": w.name, "T": T, "E": E, "top_k": k, "K": K, "N": N,
-                   "block_rows": rt["block_rows"], "group": 64, "parallelism": "single GPU"},
+    out = base_line(args, w, flops / (ms_per_step * 1e-3) / 1e12, ms_per_step,
+                    {"workload": w.name, "T": T, "E": E, "top_k": k, "K": K, "N": N,
+                     "block_rows": rt["block_rows"], "group": 64, "parallelism": "single GPU"},
+                    roofline(flops, alg_bytes, gemm_ms, "k_gemm_q4", w.name))
+    out.update({
         "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
-        "gemm": {"us": gemm_ms * 1e3, "TFLOP/s": gemm_tflops, "weight_GB/s": w_bytes / (gemm_ms * 1e-3) / 1e9,
-                 "experts_touched": touched, "rows_max_over_mean": float(counts.max() / counts.mean()),
+        "gemm": {"us": gemm_ms * 1e3, "TFLOP/s": flops / (gemm_ms * 1e-3) / 1e12,
+                 "weight_GB/s": w_bytes / (gemm_ms * 1e-3) / 1e9, "experts_touched": touched,
+                 "rows_max_over_mean": float(counts.max() / counts.mean()),
                  "experts_below_2_rows": float((counts < 2).mean())},
-        "route_us": route_ms * 1e3,
-        "event_ms_per_step": ev_step_ms,
+        "route_us": float(route_all.mean()) * 1e3,
         "timing": f"steps back to back, wall clock between two synchronisations; weights rotate over {layers} "
                   f"resident copies ({layers * w_layer / 2**30:.2f} GiB) so each GEMM reads them from HBM; "
                   "route and GEMM split by HIP events on the launch stream",
         "gemm_us_p10_p90": [float(np.percentile(gemm_all, 10)) * 1e3, float(np.percentile(gemm_all, 90)) * 1e3],
-        "roofline": roof,
-    }
+    })
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(p, w, rt["block_rows"], args.cpu_reps)
+        import oracle
+        t = []
+        for _ in range(args.cpu_reps):
+            t0 = time.perf_counter()
+            ids, _ = oracle.topk_softmax(p.logits, k)
+            r = oracle.route(ids, E, rt["block_rows"])
+            oracle.grouped_gemm_q4(p.X, k, p.Wq, p.S, p.B, r["perm"], r["offsets"])
+            t.append(time.perf_counter() - t0)
+        ts = float(np.median(t))
+        out["cpu_baseline"] = {"value": flops / ts / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"the whole step (route + grouped GEMM) of the same workload, median of "
+                                         f"{args.cpu_reps} runs, {ts:.2f} s each"}
+    return out
+
+
+def ffn_flops(T, H, I, k, shared):
+    """gate+up (2I x H) and down (H x I) per routed row, plus the shared expert per token."""
+    per_row = 2.0 * (2 * I * H + H * I)
+    return per_row * T * k + (per_row * T if shared else 0.0)
+
+
+def pack_ffn(q, d, p):
+    return (q.prepack(d(p.gu_q), d(p.gu_s), d(p.gu_b)), q.prepack(d(p.dn_q), d(p.dn_s), d(p.dn_b)),
+            q.prepack(d(p.sh_gu_q), d(p.sh_gu_s), d(p.sh_gu_b)), q.prepack(d(p.sh_dn_q), d(p.sh_dn_s), d(p.sh_dn_b)))
+
+
+def clone_pack(pk):
+    return tuple(tuple(t.clone() for t in m) for m in pk)
+
+
+# ----------------------------------------------------------------- expert FFN
+def bench_ffn(args, torch, q, W, w, d):
+    p = W.make_problem(w)
+    T, E, k, H, I = w.T, w.E, w.k, w.K, w.N
+    expert_bytes = q4_bytes(2 * I, H) + q4_bytes(H, I)
+    w_layer = (E + 1) * expert_bytes
+    layers = args.layers or max(2, -(-(1 << 30) // w_layer))
+    pk0 = pack_ffn(q, d, p)
+    packs = [pk0] + [clone_pack(pk0) for _ in range(layers - 1)]
+    logits, X = d(p.logits), d(p.X)
+    rt = q.alloc_route(T, E, k, args.block_rows, device=X.device)
+    bufs = q.alloc_ffn(T, H, I, E, k, True, device=X.device)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev):
+        if ev is not None:
+            ev[0].record(stream)
+        q.route(logits, k, bufs=rt, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        q.expert_ffn(X, k, rt, *packs[i % layers], bufs=bufs, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms_per_step, (route_all, ffn_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
+    ffn_ms = float(ffn_all.mean())
+    counts = rt["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    flops = ffn_flops(T, H, I, k, True)
+    w_bytes = (touched + 1) * expert_bytes
+    alg_bytes = w_bytes + T * H * 2 * 2   # weights, X once, out once
+    out = base_line(args, w, flops / (ms_per_step * 1e-3) / 1e12, ms_per_step,
+                    {"workload": w.name, "T": T, "E": E, "top_k": k, "H": H, "I": I, "shared_expert": True,
+                     "block_rows": rt["block_rows"], "group": 64, "parallelism": "single GPU"},
+                    roofline(flops, alg_bytes, ffn_ms, "expert_ffn", w.name))
+    out.update({
+        "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
+        "ffn": {"us": ffn_ms * 1e3, "TFLOP/s": flops / (ffn_ms * 1e-3) / 1e12, "experts_touched": touched,
+                "kernels": "routed gate+up (SwiGLU), shared gate+up, routed down (x routing weight), "
+                           "shared down, combine"},
+        "route_us": float(route_all.mean()) * 1e3,
+        "timing": f"steps back to back, wall clock between two synchronisations; weights rotate over {layers} "
+                  f"resident copies ({layers * w_layer / 2**30:.2f} GiB); route and FFN split by HIP events "
+                  "on the launch stream",
+    })
+    if not args.no_cpu_baseline:
+        import oracle
+        ids, wts = oracle.topk_softmax(p.logits, k)
+        sh = (p.sh_gu_q, p.sh_gu_s, p.sh_gu_b, p.sh_dn_q, p.sh_dn_s, p.sh_dn_b)
+        ntok = 192
+        tokens = np.arange(ntok, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.expert_ffn_q4(p.X, ids, wts, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b, sh=sh, tokens=tokens)
+        ts = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": ffn_flops(ntok, H, I, k, True) / ts / 1e12, "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"the FFN of the first {ntok} tokens of the same batch (all 9 experts "
+                                         f"per token), {ts:.2f} s"}
+    return out
+
+
+# --------------------------------------------------------------------- decode
+def bench_decode(args, torch, q, W, w, d):
+    p = W.make_problem(w)
+    E, k, H, I = w.E, w.k, w.K, w.N
+    expert_bytes = q4_bytes(2 * I, H) + q4_bytes(H, I)
+    step_bytes = (k + 1) * expert_bytes
+    # a copy's weights are read again only after > 256 MB of other weights
+    layers = args.layers or max(2, -(-(384 << 20) // step_bytes))
+    pk0 = pack_ffn(q, d, p)
+    packs = [pk0] + [clone_pack(pk0) for _ in range(layers - 1)]
+    steps_total = args.warmup + args.steps
+    lg = d(np.stack([W.gen_logits(w.cid, 1, E, s)[0] for s in range(steps_total)]))
+    xs = d(np.stack([W.gen_acts(w.cid, 1, H, s)[0] for s in range(steps_total)]))
+    bufs = q.alloc_decode(E, k, H, I, True, device=xs.device)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev):
+        if ev is not None:
+            ev[0].record(stream)
+        gu, dn, sg, sd = packs[i % layers]
+        q.decode_ffn(lg[i], xs[i], k, gu, dn, sg, sd, bufs=bufs, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    ms_per_step, (dec_all,) = Timer(torch, 2).run(step, args.warmup, args.steps)
+    dec_ms = float(dec_all.mean())
+    flops = ffn_flops(1, H, I, k, True)
+    alg_bytes = step_bytes + H * 2 * 2 + E * 4
+    out = base_line(args, w, flops / (ms_per_step * 1e-3) / 1e12, ms_per_step,
+                    {"workload": w.name, "T": 1, "E": E, "top_k": k, "H": H, "I": I, "shared_expert": True,
+                     "steps_of_fresh_tokens": args.steps, "group": 64, "parallelism": "single GPU"},
+                    roofline(flops, alg_bytes, dec_ms, "decode_step", w.name))
+    out.update({
+        "weight_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "decode": {"us_per_step_kernels": dec_ms * 1e3, "weight_GB/s": step_bytes / (dec_ms * 1e-3) / 1e9,
+                   "weight_bytes_per_step": step_bytes,
+                   "kernels": "k_decode_gateup (routing + gate/up + SwiGLU), k_decode_down (down + combine)"},
+        "timing": f"steps back to back, wall clock between two synchronisations (includes the host launch of "
+                  f"two kernels per step); weights rotate over {layers} resident copies so more than 256 MB "
+                  "of other weights are read between two uses of a copy; kernel time by HIP events",
+        "p10_p90_us": [float(np.percentile(dec_all, 10)) * 1e3, float(np.percentile(dec_all, 90)) * 1e3],
+    })
+    if not args.no_cpu_baseline:
+        import oracle
+        sh = (p.sh_gu_q, p.sh_gu_s, p.sh_gu_b, p.sh_dn_q, p.sh_dn_s, p.sh_dn_b)
+        n = 20
+        t0 = time.perf_counter()
+        for s in range(n):
+            lgs = W.gen_logits(w.cid, 1, E, s)
+            ids, wts = oracle.topk_softmax(lgs, k)
+            oracle.expert_ffn_q4(W.gen_acts(w.cid, 1, H, s), ids, wts, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s,
+                                 p.dn_b, sh=sh)
+        ts = (time.perf_counter() - t0) / n
+        out["cpu_baseline"] = {"value": flops / ts / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} decode steps of the same workload (input generation included), "
+                                         f"{ts * 1e3:.1f} ms each"}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--block-rows", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0, help="resident weight copies used in turn (0: automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=40)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the path measured here is the "
+                                   "single-GPU hot path", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import quantized_grouped_gemm_amd as q
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    if w.ffn and w.T == 1:
+        out = bench_decode(args, torch, q, W, w, d)
+    elif w.ffn:
+        out = bench_ffn(args, torch, q, W, w, d)
+    else:
+        out = bench_gemm(args, torch, q, W, w, d)
     print(json.dumps(out), flush=True)
 
 
