@@ -253,7 +253,7 @@ size_t moe_decode_workspace_bytes(int E, int k, int H, int I, int shared);
  * Out: out     uint16 (bf16) [H].
  *      topk_ids int32 [k], topk_w float [k]   the routing (each may be NULL).
  * Sizes: 1 <= k <= min(E, MOEQ4_MAX_TOPK), E <= MOEQ4_MAX_EXPERTS, H and I
- *        multiples of 64 and at least 128, H <= 16384, ceil((k + shared) / 2) * I * 2 bytes
+ *        multiples of 64 and at least 128, H <= 8192, (k + shared) * I * 2 bytes
  *        <= 64 KiB, E*2I*H/2 below 2^31.  Returns MOEQ4_ERR_UNSUPPORTED when
  *        the sizes exceed the kernels' LDS budget. */
 int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int H, int I,

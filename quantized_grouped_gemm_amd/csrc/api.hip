@@ -150,7 +150,7 @@ static int check_decode_shape(int E, int k, int H, int I, int shared) {
   if (k > MOEQ4_MAX_TOPK) return MOEQ4_ERR_UNSUPPORTED;
   if (H < 128 || H % 64 != 0 || I < 128 || I % 64 != 0) return MOEQ4_ERR_SHAPE;
   if ((long long)E * 2 * I * (H / 2) >= (1LL << 31)) return MOEQ4_ERR_SHAPE;
-  if (H > 16384) return MOEQ4_ERR_UNSUPPORTED;
+  if (H > 8192) return MOEQ4_ERR_UNSUPPORTED;  // x staged as at most two 16-byte pieces per thread
   const DecodePlan p = decode_plan(E, k, H, I, shared != 0);
   if (p.lds_down > 65536 || p.lds_gateup > 65536) return MOEQ4_ERR_UNSUPPORTED;
   return MOEQ4_OK;

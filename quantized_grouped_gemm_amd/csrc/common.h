@@ -205,7 +205,7 @@ hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, 
 
 struct DecodePlan {
   int J;               // experts per step: k routed + the shared one if given
-  size_t ws_ids, ws_w, ws_h, ws_tickets, ws_part, ws_bytes;  // workspace byte offsets / total
+  size_t ws_ids, ws_w, ws_h, ws_bytes;  // workspace byte offsets / total
   size_t lds_gateup, lds_down;                               // dynamic LDS bytes per kernel
 };
 

@@ -18,14 +18,11 @@
 //                    routing launch, no host round trip), reads gate tile t and
 //                    up tile t + I/16 of expert e_j and writes
 //                    h_j[16t..16t+16) = bf16(silu(g) * u).  Workgroup 0 also
-//                    writes the k ids and softmax weights and clears the
-//                    tickets of the down kernel.
-//   k_decode_down    one workgroup per (16-row tile of H, half of the experts):
-//                    sum over its experts of w_j * (Wd[e_j] h_j), with w = 1 for
-//                    the shared expert.  Of the two workgroups of a tile, the
-//                    one that finishes second adds the two fp32 halves (always
-//                    half 0 + half 1) and writes bf16 out, so the result does not
-//                    depend on which finished first.
+//                    writes the k ids and softmax weights.
+//   k_decode_down    one 16-wave workgroup per 16-row tile of H: the sum over
+//                    all selected experts of w_j * (Wd[e_j] h_j), with w = 1 for
+//                    the shared expert, reduced across the waves in a fixed
+//                    order, so the result is the same run after run.
 //
 // GEMV inner loop: a wave reads one 1 KB block of the tiled layout (16 rows x
 // 128 K values; lane 16q+r holds 32 codes of row r) and rebuilds every weight
@@ -39,9 +36,12 @@
 
 namespace moeq4 {
 
-constexpr int kDecWaves = 8;
+constexpr int kDecWaves = 8;          // gate/up workgroup
 constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kDecBatch = 8;      // weight blocks a wave keeps in flight
+constexpr int kDecBatch = 4;          // weight blocks a gate/up wave keeps in flight
+constexpr int kDownWaves = 16;        // down workgroup
+constexpr int kDownThreads = kDownWaves * 64;
+constexpr int kDownBatch = 3;         // weight blocks a down wave keeps in flight
 
 typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
 
@@ -146,21 +146,38 @@ __device__ __forceinline__ float sum_quarters(float v) {
   return v;
 }
 
-// Staging of bf16 vectors (n values each, n % 8 == 0) in LDS.  The first
-// 16-byte piece of each thread is loaded into registers (stage_load) before
-// the weight loads are issued, so that the wait for it does not also wait for
-// the weights (loads complete in issue order); stage_store writes it to LDS,
-// then any further pieces are staged directly.
-__device__ __forceinline__ uint4 stage_load(const uint16_t* __restrict__ src, int npieces) {
-  const int i = min((int)threadIdx.x, npieces - 1);
-  return *(const uint4*)(src + 8 * (size_t)i);
+// Staging of bf16 vectors in LDS, npieces 16-byte pieces in all.  Each thread
+// loads its P pieces into registers (stage_load, indices clamped so the loads
+// are unconditional) before the weight loads are issued, so that the wait for
+// them does not also wait for the weights (loads complete in issue order);
+// stage_store then writes them to LDS.  The host keeps npieces <= P * threads.
+template <int P>
+struct Staged {
+  uint4 v[P];
+};
+
+template <int P>
+__device__ __forceinline__ Staged<P> stage_load(const uint16_t* __restrict__ src, int npieces) {
+  Staged<P> st;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int p = min((int)(threadIdx.x + i * blockDim.x), npieces - 1);
+    st.v[i] = *(const uint4*)(src + 8 * (size_t)p);
+  }
+  return st;
 }
 
-__device__ __forceinline__ void stage_store(uint4 first, const uint16_t* __restrict__ src, int npieces,
-                                            uint4* xl) {
-  if ((int)threadIdx.x < npieces) xl[threadIdx.x] = first;
-  for (int i = threadIdx.x + kDecThreads; i < npieces; i += kDecThreads) xl[i] = *(const uint4*)(src + 8 * (size_t)i);
+template <int P>
+__device__ __forceinline__ void stage_store(const Staged<P>& st, int npieces, uint4* xl) {
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int p = threadIdx.x + i * blockDim.x;
+    if (p < npieces) xl[p] = st.v[i];
+  }
 }
+
+constexpr int kGateupPieces = 2;  // H <= 2 * 8 * kDecThreads
+constexpr int kDownPieces = 4;    // J * I <= 4 * 8 * kDownThreads
 
 // ----------------------------------------------------------------------------
 template <int VPT>
@@ -169,7 +186,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_gateup(
     const uint8_t* __restrict__ gu_q, const uint16_t* __restrict__ gu_s, const uint16_t* __restrict__ gu_b,
     const uint8_t* __restrict__ sh_q, const uint16_t* __restrict__ sh_s, const uint16_t* __restrict__ sh_b,
     int32_t* __restrict__ ids_ws, float* __restrict__ w_ws, uint16_t* __restrict__ h_ws,
-    int32_t* __restrict__ tickets, int ntickets, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
   extern __shared__ uint4 dsm[];
   uint4* xl = dsm;  // x as bf16, H values
   __shared__ float red[kDecWaves][16];
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_gateup(
   const int IT = I / 16;
   const int j = blockIdx.x / IT, t = blockIdx.x % IT;
 
-  const uint4 xr = stage_load(x, H / 8);  // x is needed by every workgroup: its load goes first
+  const Staged<kGateupPieces> xr = stage_load<kGateupPieces>(x, H / 8);  // needed by every workgroup: first
   // ---- which expert: the token's j-th choice (every wave selects on its own)
   int e = 0;
   if (j < k) {
@@ -203,8 +220,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_gateup(
       }
     }
   }
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < ntickets; i += kDecThreads) tickets[i] = 0;
 
   const size_t mat_codes = (size_t)I * H;  // bytes of one [2I][H] code matrix
   const size_t mat_groups = (size_t)2 * I * (H / kGroup);
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_gateup(
   FullBlock f[kDecBatch];
 #pragma unroll
   for (int i = 0; i < kDecBatch; ++i) f[i] = load_full(m, tile, min(c_first + WPT * i, nfull - 1), lane);
-  stage_store(xr, x, H / 8, xl);
+  stage_store(xr, H / 8, xl);
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
@@ -251,58 +266,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_gateup(
 }
 
 // ----------------------------------------------------------------------------
-// Ends a down-projection workgroup: reduces the waves' partials of the tile's 16
-// outputs, publishes them, and if the other half of the tile is already done,
-// adds the two halves (half 0 + half 1) and writes bf16 out.
-__device__ __forceinline__ void finish_tile(float acc, int t, int half, float (*red)[16],
-                                            int32_t* __restrict__ tickets, float* __restrict__ part,
-                                            uint16_t* __restrict__ out) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (lane < 16) red[wv][lane] = acc;
-  __syncthreads();
-  if (wv == 0) {
-    const int r = lane & 15;
-    float p = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) p += red[w][r];
-    if (lane < 16)
-      __hip_atomic_store(part + ((size_t)t * 2 + half) * 16 + r, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(tickets + t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0);
-    if (old == 1 && lane < 16) {  // the other half is complete: combine in a fixed order
-      const float other = __hip_atomic_load(part + ((size_t)t * 2 + (1 - half)) * 16 + r, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-      const float total = half == 0 ? p + other : other + p;
-      out[16 * t + r] = f32_to_bf16_bits(total);
-    }
-  }
-}
-
-__global__ __launch_bounds__(kDecThreads) void k_decode_down(
+__global__ __launch_bounds__(kDownThreads) void k_decode_down(
     int k, int H, int I, int J, const uint8_t* __restrict__ dn_q, const uint16_t* __restrict__ dn_s,
     const uint16_t* __restrict__ dn_b, const uint8_t* __restrict__ sh_q, const uint16_t* __restrict__ sh_s,
     const uint16_t* __restrict__ sh_b, const int32_t* __restrict__ ids_ws, const float* __restrict__ w_ws,
-    const uint16_t* __restrict__ h_ws, int32_t* __restrict__ tickets, float* __restrict__ part,
-    uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ h_ws, uint16_t* __restrict__ out) {
   extern __shared__ uint4 dsm[];
-  __shared__ float red[kDecWaves][16];
+  __shared__ float red[kDownWaves][16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x >> 1, half = blockIdx.x & 1;
-  const int J0 = (J + 1) / 2;
-  const int j_lo = half ? J0 : 0, j_hi = half ? J : J0;
-  const int nj = j_hi - j_lo;
-  if (nj == 0) {  // a single expert in all: this half has nothing to add
-    finish_tile(0.f, t, half, red, tickets, part, out);
-    return;
-  }
-  const uint4 hr = stage_load(h_ws + (size_t)j_lo * I, nj * (I / 8));
-  uint4* hl = dsm;  // [nj][I] bf16: h of this half's experts
+  const int t = blockIdx.x;  // 16-row tile of the output
+
+  const Staged<kDownPieces> hr = stage_load<kDownPieces>(h_ws, J * (I / 8));
+  uint4* hl = dsm;  // [J][I] bf16: h of every expert of the step
 
   const size_t mat_codes = (size_t)H * I / 2;
   const size_t mat_groups = (size_t)H * (I / kGroup);
   const int G = I / kGroup, nfull = G / 2;
-  const int nb = nj * nfull;  // full blocks of this workgroup: (expert, chunk); wave w takes w, w+8, ...
+  const int nb = J * nfull;  // full blocks: (expert, chunk); wave w takes w, w+16, ...
   auto mat = [&](int j, size_t e) {
     TiledMat m1;
     m1.q = j < k ? dn_q + e * mat_codes : sh_q;
@@ -312,51 +292,57 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_down(
     return m1;
   };
   float acc = 0.f;
-  FullBlock f[kDecBatch];
-  float wb[kDecBatch];
+  FullBlock f[kDownBatch];
+  float wb[kDownBatch];
   // loads are unconditional (indices clamped, surplus results unused), so the
   // expert ids arrive with one wait and the wait for h below is exact
   auto load_batch = [&](int b0) {
-    int eb[kDecBatch];
+    int eb[kDownBatch];
 #pragma unroll
-    for (int i = 0; i < kDecBatch; ++i) {
-      const int b = min(b0 + kDecWaves * i, nb - 1);
-      const int j = j_lo + b / nfull, jc = min(j, k - 1);
+    for (int i = 0; i < kDownBatch; ++i) {
+      const int b = min(b0 + kDownWaves * i, nb - 1);
+      const int j = b / nfull, jc = min(j, k - 1);
       eb[i] = ids_ws[jc];
       const float wl = w_ws[jc];
       wb[i] = j < k ? wl : 1.f;
     }
 #pragma unroll
-    for (int i = 0; i < kDecBatch; ++i) {
-      const int b = min(b0 + kDecWaves * i, nb - 1);
-      f[i] = load_full(mat(j_lo + b / nfull, (size_t)eb[i]), t, b % nfull, lane);
+    for (int i = 0; i < kDownBatch; ++i) {
+      const int b = min(b0 + kDownWaves * i, nb - 1);
+      f[i] = load_full(mat(b / nfull, (size_t)eb[i]), t, b % nfull, lane);
     }
   };
   auto compute_batch = [&](int b0) {
 #pragma unroll
-    for (int i = 0; i < kDecBatch; ++i) {
-      const int b = b0 + kDecWaves * i;
+    for (int i = 0; i < kDownBatch; ++i) {
+      const int b = b0 + kDownWaves * i;
       if (b < nb) acc = __builtin_fmaf(wb[i], gemv_full(f[i], b % nfull, lane, hl + (size_t)(b / nfull) * I / 8), acc);
     }
   };
   load_batch(wv);  // in flight while h is staged
-  stage_store(hr, h_ws + (size_t)j_lo * I, nj * (I / 8), hl);
+  stage_store(hr, J * (I / 8), hl);
   __syncthreads();
   compute_batch(wv);
-  for (int b0 = wv + kDecWaves * kDecBatch; b0 < nb; b0 += kDecWaves * kDecBatch) {
+  for (int b0 = wv + kDownWaves * kDownBatch; b0 < nb; b0 += kDownWaves * kDownBatch) {
     load_batch(b0);
     compute_batch(b0);
   }
-  if (G & 1) {  // half-size last chunk of every expert of this half
-    for (int jj = wv; jj < nj; jj += kDecWaves) {
-      const int j = j_lo + jj;
+  if (G & 1) {  // half-size last chunk of every expert
+    for (int j = wv; j < J; j += kDownWaves) {
       const float wj = j < k ? w_ws[j] : 1.f;
-      acc = __builtin_fmaf(wj, gemv_tail(mat(j, j < k ? (size_t)ids_ws[j] : 0), t, nfull, lane, hl + (size_t)jj * I / 8),
+      acc = __builtin_fmaf(wj, gemv_tail(mat(j, j < k ? (size_t)ids_ws[j] : 0), t, nfull, lane, hl + (size_t)j * I / 8),
                            acc);
     }
   }
   acc = sum_quarters(acc);
-  finish_tile(acc, t, half, red, tickets, part, out);
+  if (lane < 16) red[wv][lane] = acc;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float p = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDownWaves; ++w) p += red[w][threadIdx.x];
+    out[16 * t + threadIdx.x] = f32_to_bf16_bits(p);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -368,12 +354,9 @@ DecodePlan decode_plan(int E, int k, int H, int I, bool shared) {
   p.ws_ids = 0;
   p.ws_w = align256(sizeof(int32_t) * (size_t)k);
   p.ws_h = p.ws_w + align256(sizeof(float) * (size_t)k);
-  p.ws_tickets = p.ws_h + align256(sizeof(uint16_t) * (size_t)p.J * I);
-  p.ws_part = p.ws_tickets + align256(sizeof(int32_t) * (size_t)(H / 16));
-  p.ws_bytes = p.ws_part + align256(sizeof(float) * (size_t)(H / 16) * 2 * 16);
+  p.ws_bytes = p.ws_h + align256(sizeof(uint16_t) * (size_t)p.J * I);
   p.lds_gateup = (size_t)H * 2;
-  const int J0 = (p.J + 1) / 2;
-  p.lds_down = (size_t)J0 * I * 2;
+  p.lds_down = (size_t)p.J * I * 2;
   (void)E;
   return p;
 }
@@ -388,8 +371,6 @@ hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_
   int32_t* ids_ws = (int32_t*)(ws + p.ws_ids);
   float* w_ws = (float*)(ws + p.ws_w);
   uint16_t* h_ws = (uint16_t*)(ws + p.ws_h);
-  int32_t* tickets = (int32_t*)(ws + p.ws_tickets);
-  float* part = (float*)(ws + p.ws_part);
   const void* fn;
   if (E <= 64) fn = (const void*)&k_decode_gateup<1>;
   else if (E <= 128) fn = (const void*)&k_decode_gateup<2>;
@@ -398,11 +379,11 @@ hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_
   else fn = (const void*)&k_decode_gateup<16>;
   hipError_t err = launch("k_decode_gateup", fn, dim3(p.J * (I / 16)), dim3(kDecThreads), p.lds_gateup, stream,
                           logits, x, E, k, H, I, gu_q, gu_s, gu_b, sh_gu_q, sh_gu_s, sh_gu_b, ids_ws, w_ws, h_ws,
-                          tickets, H / 16, ids_out, w_out);
+                          ids_out, w_out);
   if (err != hipSuccess) return err;
-  return launch("k_decode_down", (const void*)&k_decode_down, dim3(2 * (H / 16)), dim3(kDecThreads), p.lds_down,
+  return launch("k_decode_down", (const void*)&k_decode_down, dim3(H / 16), dim3(kDownThreads), p.lds_down,
                 stream, k, H, I, p.J, dn_q, dn_s, dn_b, sh_dn_q, sh_dn_s, sh_dn_b, (const int32_t*)ids_ws,
-                (const float*)w_ws, (const uint16_t*)h_ws, tickets, part, out);
+                (const float*)w_ws, (const uint16_t*)h_ws, out);
 }
 
 }  // namespace moeq4
