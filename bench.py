@@ -19,13 +19,16 @@ HBM rather than from the 256 MB Infinity Cache: at least 1 GiB of copies for
 the prefill workloads, and for decode enough copies that more than 256 MB of
 other weights are read between two uses of a copy.
 
+Prefill steps are replayed from HIP graphs (one per weight copy) unless
+--no-graph; an eager run of the same steps gives the per-kernel event times.
+
 Prints one JSON line: the throughput of the whole step, the roofline of the
 dominant kernel (timed with HIP events on its launch stream; HBM traffic from
 the committed rocprofv3 counter summary when it matches the kernel source)
 and the CPU oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 2|4|3|5|1]
-                    [--block-rows BM] [--layers L] [--no-cpu-baseline] [--cpu-reps R]
+                    [--block-rows BM] [--layers L] [--no-graph] [--no-cpu-baseline] [--cpu-reps R]
 """
 from __future__ import annotations
 
@@ -108,6 +111,32 @@ class Timer:
         return ms_per_step, seg
 
 
+def graph_ms_per_step(torch, args, capture_step, layers):
+    """Whole-step wall time with every step replayed from a HIP graph (one graph
+    per resident weight copy, captured from the same library calls), so the
+    step's small kernels start back to back without host launch gaps."""
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm the calls once outside capture
+        capture_step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for l in range(layers):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            capture_step(l)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % layers].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % layers].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / args.steps
+
+
 def base_line(args, w, value, ms_per_step, config, roof):
     return {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -141,8 +170,13 @@ def bench_gemm(args, torch, q, W, w, d):
         if ev is not None:
             ev[2].record(stream)
 
-    ms_per_step, (route_all, gemm_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
+    eager_ms, (route_all, gemm_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
     gemm_ms = float(gemm_all.mean())
+    ms_per_step = eager_ms
+    if not args.no_graph:
+        ms_per_step = graph_ms_per_step(torch, args, lambda l: (
+            q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
+            q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y, stream=torch.cuda.current_stream())), layers)
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     A = T * k
@@ -160,9 +194,11 @@ def bench_gemm(args, torch, q, W, w, d):
                  "rows_max_over_mean": float(counts.max() / counts.mean()),
                  "experts_below_2_rows": float((counts < 2).mean())},
         "route_us": float(route_all.mean()) * 1e3,
-        "timing": f"steps back to back, wall clock between two synchronisations; weights rotate over {layers} "
-                  f"resident copies ({layers * w_layer / 2**30:.2f} GiB) so each GEMM reads them from HBM; "
-                  "route and GEMM split by HIP events on the launch stream",
+        "eager_ms_per_step": eager_ms,
+        "timing": f"steps back to back, wall clock between two synchronisations" +
+                  ("" if args.no_graph else ", each step replayed from a HIP graph of its route + GEMM launches") +
+                  f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB) so each "
+                  "GEMM reads them from HBM; route and GEMM split by HIP events on the launch stream in an eager run",
         "gemm_us_p10_p90": [float(np.percentile(gemm_all, 10)) * 1e3, float(np.percentile(gemm_all, 90)) * 1e3],
     })
     if not args.no_cpu_baseline:
@@ -221,8 +257,13 @@ def bench_ffn(args, torch, q, W, w, d):
         if ev is not None:
             ev[2].record(stream)
 
-    ms_per_step, (route_all, ffn_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
+    eager_ms, (route_all, ffn_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
     ffn_ms = float(ffn_all.mean())
+    ms_per_step = eager_ms
+    if not args.no_graph:
+        ms_per_step = graph_ms_per_step(torch, args, lambda l: (
+            q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
+            q.expert_ffn(X, k, rt, *packs[l], bufs=bufs, stream=torch.cuda.current_stream())), layers)
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     flops = ffn_flops(T, H, I, k, True)
@@ -238,9 +279,11 @@ def bench_ffn(args, torch, q, W, w, d):
                 "kernels": "routed gate+up (SwiGLU), shared gate+up, routed down (x routing weight), "
                            "shared down, combine"},
         "route_us": float(route_all.mean()) * 1e3,
-        "timing": f"steps back to back, wall clock between two synchronisations; weights rotate over {layers} "
-                  f"resident copies ({layers * w_layer / 2**30:.2f} GiB); route and FFN split by HIP events "
-                  "on the launch stream",
+        "eager_ms_per_step": eager_ms,
+        "timing": f"steps back to back, wall clock between two synchronisations" +
+                  ("" if args.no_graph else ", each step replayed from a HIP graph of its route + FFN launches") +
+                  f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB); route "
+                  "and FFN split by HIP events on the launch stream in an eager run",
     })
     if not args.no_cpu_baseline:
         import oracle
@@ -327,6 +370,7 @@ def main():
     ap.add_argument("--block-rows", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0, help="resident weight copies used in turn (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--cpu-reps", type=int, default=40)
     args = ap.parse_args()
     if args.gpus != 1:

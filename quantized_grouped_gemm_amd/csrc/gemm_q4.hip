@@ -139,13 +139,14 @@ __device__ __forceinline__ int gemm_xrow(const GemmArgs& a, int p) {
 // Epilogue of one output row (sorted row p): per-row values are read once.
 template <int EPI>
 struct EpiRow {
-  uint16_t* y;    // output row
+  uint16_t* y;    // output row (null: not written)
   float w;        // kEpiScale: routing weight of the row's assignment
   __device__ __forceinline__ EpiRow(const GemmArgs& a, int p) {
     if constexpr (EPI == kEpiScale) {
       const int as = a.perm[p];
-      y = a.Y + (size_t)as * a.ldy;
-      w = a.topk_w[as];
+      const bool ok = as >= 0 && as < a.A;  // a malformed permutation writes nothing
+      y = ok ? a.Y + (size_t)as * a.ldy : nullptr;
+      w = ok ? a.topk_w[as] : 0.f;
     } else {
       y = a.Y + (size_t)p * a.ldy;
       w = 1.f;
@@ -153,6 +154,9 @@ struct EpiRow {
   }
   // value v of output column n (g, u for kEpiSwiglu)
   __device__ __forceinline__ void store(int n, float v, float u = 0.f) const {
+    if constexpr (EPI == kEpiScale) {
+      if (!y) return;
+    }
     if constexpr (EPI == kEpiSwiglu) {
       y[n] = f32_to_bf16_bits(v / (1.f + expf(-v)) * u);
     } else if constexpr (EPI == kEpiScale) {

@@ -29,7 +29,9 @@ constexpr int kRouteThreads = kRouteWaves * 64;
 constexpr int kChunkAssignMax = 2048;      // assignments per chunk (LDS bound)
 constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / kRouteWaves;
 constexpr int kFusedScatterMax = 8192;     // assignments the scan workgroup also scatters
+constexpr int kFusedBasesMax = 8192;       // chunk bases it keeps in LDS for that (32 KB)
 constexpr int kScanThreads = 1024;
+constexpr int kFusedPerThread = kFusedScatterMax / kScanThreads;  // assignments per scan thread
 constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 
 // ----------------------------------------------------------------------------
@@ -138,30 +140,36 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
 }
 
 // ----------------------------------------------------------------------------
+// Inclusive scan of an int over the 64 lanes of a wave: Hillis-Steele inside
+// each row of 16 lanes (row_shr 1, 2, 4, 8), then row_bcast 15 / 31 carry the
+// row totals upward.
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Block-wide exclusive scan over kScanThreads values (one per thread).
 __device__ int block_exclusive_scan(int v, int* scratch /* >= kScanThreads/64 + 1 ints */,
                                     int* total) {
+  constexpr int NW = kScanThreads / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
+  const int incl = wave_incl_scan_i32(v);
   if (lane == 63) scratch[wv] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < kScanThreads / 64; ++i) {
-      const int x = scratch[i];
-      scratch[i] = run;
-      run += x;
-    }
-    scratch[kScanThreads / 64] = run;
+  if (wv == 0) {
+    const int t = lane < NW ? scratch[lane] : 0;
+    const int ti = wave_incl_scan_i32(t);
+    if (lane < NW) scratch[lane] = ti - t;
+    if (lane == NW - 1) scratch[NW] = ti;
   }
   __syncthreads();
   const int r = scratch[wv] + incl - v;
-  *total = scratch[kScanThreads / 64];
+  *total = scratch[NW];
   __syncthreads();
   return r;
 }
@@ -171,11 +179,24 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
     int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks,
     int fuse_scatter, const int32_t* __restrict__ ids, int A, int k, int tpc,
     const int32_t* __restrict__ local_rank, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  extern __shared__ int cb_s[];  // fused scatter: the chunk bases [nchunks][E]
   __shared__ int part[kScanThreads];
   __shared__ int offs_s[MOEQ4_MAX_EXPERTS + 1];
   __shared__ int boffs_s[MOEQ4_MAX_EXPERTS + 1];
   __shared__ int scratch[kScanThreads / 64 + 1];
   const int tid = threadIdx.x;
+
+  // ---- fused scatter: its inputs do not depend on the scan, so their loads
+  // go out first (indices clamped: unconditional loads)
+  int pf_e[kFusedPerThread], pf_r[kFusedPerThread];
+  if (fuse_scatter && A > 0) {
+#pragma unroll
+    for (int i = 0; i < kFusedPerThread; ++i) {
+      const int a = min(tid + i * kScanThreads, A - 1);
+      pf_e[i] = ids[a];
+      pf_r[i] = local_rank[a];
+    }
+  }
 
   // ---- per expert, exclusive scan over chunks (S threads per expert).  Each
   // thread holds its chunk counts in registers, fetched with independent loads.
@@ -216,7 +237,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
 #pragma unroll
     for (int i = 0; i < kScanRegs; ++i) {
       const int c = c_lo + i;
-      if (c < c_hi) chunk_counts[(size_t)c * E + e] = run;
+      if (c < c_hi) {
+        if (fuse_scatter) cb_s[c * E + e] = run;  // bases stay in LDS for the scatter below
+        else chunk_counts[(size_t)c * E + e] = run;
+      }
       run += vals[i];
     }
   } else if (act) {
@@ -263,15 +287,19 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
     blocks[4 * (size_t)b + 3] = i;
   }
 
-  // ---- small inputs: the scatter too (chunk bases were written above, before
-  // the barriers of the scans)
+  // ---- small inputs: the scatter too (chunk bases were written to LDS above,
+  // before the barriers of the scans)
   if (fuse_scatter) {
-    for (int a = tid; a < A; a += kScanThreads) {
-      const int e = ids[a];
-      const int c = (a / k) / tpc;
-      const int p = offs_s[e] + chunk_counts[(size_t)c * E + e] + local_rank[a];
-      if (p >= 0 && p < A) perm[p] = a;
-      inv_perm[a] = p;
+#pragma unroll
+    for (int i = 0; i < kFusedPerThread; ++i) {
+      const int a = tid + i * kScanThreads;
+      if (a < A) {
+        const int e = pf_e[i];
+        const int c = (a / k) / tpc;
+        const int p = offs_s[e] + cb_s[c * E + e] + pf_r[i];
+        if (p >= 0 && p < A) perm[p] = a;
+        inv_perm[a] = p;
+      }
     }
   }
 }
@@ -337,8 +365,9 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
     if (err != hipSuccess) return err;
   }
   const int A = T * k;
-  const int fuse = A <= kFusedScatterMax;
-  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), 0, stream, chunk_counts,
+  const int fuse = A <= kFusedScatterMax && (long long)plan.nchunks * E <= kFusedBasesMax;
+  const size_t cb_bytes = fuse ? sizeof(int) * (size_t)plan.nchunks * E : 0;
+  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), cb_bytes, stream, chunk_counts,
                plan.nchunks, E, BM, counts, offsets, blocks, num_blocks, fuse, (const int32_t*)ids, A, k,
                plan.tpc, (const int32_t*)local_rank, perm, inv_perm);
   if (err != hipSuccess) return err;
