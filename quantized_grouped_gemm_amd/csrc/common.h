@@ -221,7 +221,8 @@ hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_
 struct FfnPlan {
   // workspace: routed h [T*k][I], shared h [T][I], routed terms [T*k][H], shared term [T][H]
   size_t ws_h, ws_hs, ws_dw, ws_dsh, ws_bytes;
-  int bm_shared;                        // dense block height of the shared expert
+  int bm_shared;                        // dense block height of the shared expert's gate+up
+  int bm_shared_dn;                     // ... and of its down projection
 };
 
 FfnPlan ffn_plan(int T, int H, int I, int k, bool shared);

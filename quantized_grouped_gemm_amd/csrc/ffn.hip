@@ -69,6 +69,7 @@ FfnPlan ffn_plan(int T, int H, int I, int k, bool shared) {
   int bm = 16;
   while (bm < 128 && bm < (5LL * T + 3) / 4) bm <<= 1;
   p.bm_shared = bm;
+  p.bm_shared_dn = bm < 64 ? bm : 64;  // the short-K down kernel keeps 64 rows' activations resident
   return p;
 }
 
@@ -162,7 +163,7 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
     s.Bt = sh_dn_b;
     s.Y = Dsh;
     s.ldy = H;
-    err = gemm_launch(s, kEpiTerm, p.bm_shared, sh_blocks, stream);
+    err = gemm_launch(s, kEpiTerm, p.bm_shared_dn, (T + p.bm_shared_dn - 1) / p.bm_shared_dn, stream);
     if (err != hipSuccess) return err;
   }
 

@@ -136,19 +136,38 @@ __device__ __forceinline__ int gemm_xrow(const GemmArgs& a, int p) {
   return (a.gather ? a.gather[p] / a.k : p) * a.K * 2;
 }
 
-// Epilogue of one output row (sorted row p): per-row values are read once.
+// Per-workgroup table of the kEpiScale rows: the assignment each sorted row
+// goes back to and its routing weight, read once before the main loop (the
+// epilogue then needs no dependent global loads between its stores).
+struct EpiTab {
+  int as[128];
+  float w[128];
+};
+
+template <int EPI>
+__device__ __forceinline__ void epi_fill(const GemmArgs& a, int row0, int rows, EpiTab* tab) {
+  if constexpr (EPI == kEpiScale) {
+    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+      const int as = a.perm[row0 + r];
+      const bool ok = as >= 0 && as < a.A;  // a malformed permutation writes nothing
+      tab->as[r] = ok ? as : -1;
+      tab->w[r] = ok ? a.topk_w[as] : 0.f;
+    }
+  }
+}
+
+// Epilogue of one output row (row `row` of the block starting at sorted row row0).
 template <int EPI>
 struct EpiRow {
   uint16_t* y;    // output row (null: not written)
   float w;        // kEpiScale: routing weight of the row's assignment
-  __device__ __forceinline__ EpiRow(const GemmArgs& a, int p) {
+  __device__ __forceinline__ EpiRow(uint16_t* Y, int ldy, int row0, int row, const EpiTab* tab) {
     if constexpr (EPI == kEpiScale) {
-      const int as = a.perm[p];
-      const bool ok = as >= 0 && as < a.A;  // a malformed permutation writes nothing
-      y = ok ? a.Y + (size_t)as * a.ldy : nullptr;
-      w = ok ? a.topk_w[as] : 0.f;
+      const int as = tab->as[row];
+      y = as >= 0 ? Y + (size_t)as * ldy : nullptr;
+      w = tab->w[row];
     } else {
-      y = a.Y + (size_t)p * a.ldy;
+      y = Y + (size_t)(row0 + row) * ldy;
       w = 1.f;
     }
   }
@@ -198,6 +217,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   const int ntile = task - blk * ntiles;
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
+  static_assert(BM <= 128, "the epilogue table holds 128 rows");
+  __shared__ EpiTab ep_tab;
+  epi_fill<EPI>(a, row0, rows, &ep_tab);
+  uint16_t* const Yout = a.Y;
+  const int ldy = a.ldy;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -250,7 +274,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   Stage<NF, XP> st[S];
   // full chunk c (clamped to the last full chunk): every lane loads, no branches,
   // so the compiler's wait counts stay exact across the ring
-  auto load = [&](Stage<NF, XP>& s, int c) {
+  auto load = [&](Stage<NF, XP>& s, int c) __attribute__((always_inline)) {
     const int cl = min(c, nfull - 1);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -267,7 +291,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
     }
   };
   // the single-group chunk that ends an odd G
-  auto load_tail = [&](Stage<NF, XP>& s) {
+  auto load_tail = [&](Stage<NF, XP>& s) __attribute__((always_inline)) {
     const int c = nfull;
     typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 #pragma unroll
@@ -290,7 +314,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
       s.x[i] = v;
     }
   };
-  auto store_x = [&](const Stage<NF, XP>& s, int buf) {
+  auto store_x = [&](const Stage<NF, XP>& s, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int p = tid + i * NTHR;
@@ -306,7 +330,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
     for (int f = 0; f < NF; ++f) acc[r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // MFA > 0: exactly MFA row sub-tiles (straight-line code); MFA == 0: `mfa` at run time
-  auto compute = [&](auto mfa_c, int buf, const Stage<NF, XP>& s, int ngroups) {
+  auto compute = [&](auto mfa_c, int buf, const Stage<NF, XP>& s, int ngroups) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
     constexpr int RMAX = MFA > 0 ? MFA : MF;
 #pragma unroll
@@ -374,7 +398,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   // issued S-2 iterations earlier, never the newer prefetches.  Iterations past
   // the last chunk (when S does not divide it) reload the last chunk and skip
   // the MFMAs.
-  auto run = [&](auto mfa_c) {
+  auto run = [&](auto mfa_c) __attribute__((always_inline)) {
     if (nfull > 0) {
 #pragma unroll
       for (int s = 0; s < S - 1; ++s) load(st[s], s);
@@ -414,7 +438,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int row = r * 16 + quarter * 4 + i;
       if (row >= rows) continue;
-      const EpiRow<EPI> er(a, row0 + row);
+      const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
 #pragma unroll
       for (int f = 0; f < NFO; ++f) {
         if (f >= nf_live) break;
@@ -470,6 +494,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   const int ntile = task - blk * ntiles;
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
+  static_assert(BM <= 128, "the epilogue table holds 128 rows");
+  __shared__ EpiTab ep_tab;
+  epi_fill<EPI>(a, row0, rows, &ep_tab);
+  uint16_t* const Yout = a.Y;
+  const int ldy = a.ldy;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -520,7 +549,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   // The tail chunk of an odd G has only 8 columns: the other slots get the
   // out-of-range offset (the range check covers the vector offset only, so the
   // row must not be overrun through the chunk offset).
-  auto dma_x = [&](int c, int buf, bool tail) {
+  auto dma_x = [&](int c, int buf, bool tail) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int r = 4 * (wave * IPW + i) + (lane >> 4);
@@ -535,7 +564,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
     uint32_t s[NF32], b[NF32];
   };
   St32 st[S];
-  auto load = [&](St32& s, int c) {
+  auto load = [&](St32& s, int c) __attribute__((always_inline)) {
     const int cl = min(c, nfull - 1);
 #pragma unroll
     for (int f = 0; f < NF32; ++f) {
@@ -547,7 +576,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
       s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, gbase, 0, 0);
     }
   };
-  auto load_tail = [&](St32& s) {
+  auto load_tail = [&](St32& s) __attribute__((always_inline)) {
     const int c = nfull;
     typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 #pragma unroll
@@ -574,7 +603,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   // MFA: the number of filled 32-row tiles, a compile-time constant so that the
   // LDS reads and MFMAs of a K-step are straight-line code the compiler can
   // schedule (one copy of the loop per value)
-  auto compute = [&](auto mfa_c, int buf, const St32& s, int ngroups) {
+  auto compute = [&](auto mfa_c, int buf, const St32& s, int ngroups) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
@@ -608,7 +637,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   // chunk c+S-1 go out, then chunk c's MFMAs run; the barrier that ends the
   // iteration waits for those loads, so their latency hides behind the MFMAs.
   // Loads past the last chunk re-read it (clamped) and are not used.
-  auto run = [&](auto mfa_c) {
+  auto run = [&](auto mfa_c) __attribute__((always_inline)) {
     if (nfull > 0) {
 #pragma unroll
       for (int s = 0; s < S - 1; ++s) load(st[s], s);
@@ -650,7 +679,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
     for (int i = 0; i < 16; ++i) {
       const int row = r * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
       if (row >= rows) continue;
-      const EpiRow<EPI> er(a, row0 + row);
+      const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
 #pragma unroll
       for (int f = 0; f < NFO; ++f) {
         if (f >= nf_live) break;
@@ -661,6 +690,184 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Short K (K <= 512, K % 128 == 0; the FFN's down projections): the block's
+// activations for the whole of K stay in LDS (BM x K bf16, swizzled as in
+// k_gemm_q4_w32, loaded once by DMA), and each wave then streams the weights of
+// its columns through an S-stage register ring across all the N tiles of the
+// workgroup's range, with no barrier in the loop.  A workgroup covers one
+// block and NR output columns, so every weight of that range is rebuilt once
+// per block and the activations are read once.
+constexpr int kKResMax = 512;
+
+template <int BM, int NF32, int NCH, int WAVES, int EPI>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a, int NR) {
+  // NCH = K / 128 chunks; the register ring has NCH stages, so that the stage
+  // of step (N tile nt, chunk c) is c: a compile-time index in the unrolled loop
+  constexpr int S = NCH;
+  static_assert(EPI != kEpiSwiglu, "gate/up pairs columns across the whole N: not this kernel");
+  constexpr int MF32 = BM / 32;
+  constexpr int TILE_N = WAVES * NF32 * 32;
+  constexpr int IPW = BM * 16 / 64 / WAVES;  // DMA instructions per wave per chunk
+  static_assert(IPW * 64 * WAVES == BM * 16, "rows split evenly over the waves");
+  extern __shared__ __attribute__((aligned(16))) uint16_t xk[];  // [K/128][BM][128]
+  const int K = a.K, N = a.N;
+  const int nsplit = (N + NR - 1) / NR;
+  const int total = gemm_nblocks(a, BM) * nsplit;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int task = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (task >= total) return;
+  const int blk = task / nsplit;
+  const int n_lo = (task - blk * nsplit) * NR;
+  const int n_hi = min(N, n_lo + NR);
+  int e, row0, rows;
+  if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
+  static_assert(BM <= 128, "the epilogue table holds 128 rows");
+  __shared__ EpiTab ep_tab;
+  epi_fill<EPI>(a, row0, rows, &ep_tab);
+  uint16_t* const Yout = a.Y;
+  const int ldy = a.ldy;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = K / kGroup;
+  constexpr int nch = NCH;
+  const int NT = N / 16;
+  const int mfa = (rows + 31) >> 5;
+  const int ntl = (n_hi - n_lo + TILE_N - 1) / TILE_N;  // N tiles of this workgroup
+  const int nsteps = ntl * nch;                          // (N tile, chunk) steps, chunk fastest
+
+  const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.Wt + (size_t)e * N * (K / 2)), (short)0, N * (K / 2), kBufFlags);  // rsrcs hold the fields
+  const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.St + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t bsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.Bt + (size_t)e * N * G), (short)0, N * G * 2, kBufFlags);
+  const __amdgpu_buffer_rsrc_t xsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, a.xrows * K * 2, kBufFlags);
+
+  // ---- the block's activations, all chunks, by DMA (rows past the block: zeros)
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int x_oob = a.xrows * K * 2;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = 4 * (wave * IPW + i) + (lane >> 4);
+    const int c16 = (lane & 15) ^ (r & 15);
+    const int off = r < rows ? gemm_xrow(a, row0 + r) + c16 * 16 : x_oob;
+    for (int c = 0; c < nch; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xsrc, (lds_void*)&xk[((size_t)c * BM + 4 * (wave * IPW + i)) * kKC], 16, off, c * kKC * 2, 0, 0);
+  }
+
+  struct StK {
+    u32x4 w[NF32][2];
+    uint32_t s[NF32], b[NF32];
+  };
+  StK st[S];
+  // weights of step j (clamped to the last step: every lane loads, so the
+  // compiler's wait counts stay exact)
+  auto load = [&](StK& sg, int j) __attribute__((always_inline)) {
+    const int jc = min(j, nsteps - 1);
+    const int nt = jc / nch, c = jc - nt * nch;
+    const int n_wave = n_lo + nt * TILE_N + wave * NF32 * 32;
+#pragma unroll
+    for (int f = 0; f < NF32; ++f) {
+      const int tile16 = min((n_wave + f * 32 + col) >> 4, NT - 1);
+      const int r16 = col & 15;
+      const int base = (c * NT + tile16) * 1024 + r16 * 16;
+      sg.w[f][0] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, base + (2 * half) * 256, 0, 0);
+      sg.w[f][1] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, base + (2 * half + 1) * 256, 0, 0);
+      const int gbase = ((c * NT + tile16) * 32 + 2 * r16) * 2;
+      sg.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, gbase, 0, 0);
+      sg.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, gbase, 0, 0);
+    }
+  };
+
+  f32x16 acc[MF32][NF32];
+  auto zero = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < MF32; ++r)
+#pragma unroll
+      for (int f = 0; f < NF32; ++f)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[r][f][i] = 0.f;
+  };
+  zero();
+
+  auto compute = [&](auto mfa_c, int c, const StK& sg) __attribute__((always_inline)) {
+    constexpr int MFA = decltype(mfa_c)::value;
+    const uint16_t* xc = &xk[(size_t)c * BM * kKC];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        bf16x8 bfr[NF32];
+#pragma unroll
+        for (int f = 0; f < NF32; ++f) {
+          const float sv = gi ? __uint_as_float(sg.s[f] & 0xFFFF0000u) : __uint_as_float(sg.s[f] << 16);
+          const float bv = gi ? __uint_as_float(sg.b[f] & 0xFFFF0000u) : __uint_as_float(sg.b[f] << 16);
+          bfr[f] = rebuild_dq(sg.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
+        }
+        const uint16_t* xb = xc + col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8);
+        bf16x8 av[MFA];
+#pragma unroll
+        for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kKC);
+#pragma unroll
+        for (int r = 0; r < MFA; ++r)
+#pragma unroll
+          for (int f = 0; f < NF32; ++f)
+            acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[r], bfr[f], acc[r][f], 0, 0, 0);
+      }
+    }
+  };
+
+  auto epilogue = [&](int nt) __attribute__((always_inline)) {
+    const int n_wave = n_lo + nt * TILE_N + wave * NF32 * 32;
+#pragma unroll
+    for (int r = 0; r < MF32; ++r) {
+      if (r >= mfa) break;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = r * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (row >= rows) continue;
+        const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
+#pragma unroll
+        for (int f = 0; f < NF32; ++f) {
+          const int n = n_wave + f * 32 + col;
+          if (n < n_hi) er.store(n, acc[r][f][i]);
+        }
+      }
+    }
+  };
+
+  auto run = [&](auto mfa_c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) load(st[s], s);
+    __syncthreads();  // the activations are in LDS (the barrier waits for the DMA)
+    for (int nt = 0; nt < ntl; ++nt) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        // the load of step j + S - 1 (the same chunk index as c - 1 of this ring)
+        load(st[(c + S - 1) % S], nt * NCH + c + S - 1);
+        asm volatile("" ::: "memory");  // keep the loads ahead of the MFMAs
+        compute(mfa_c, c, st[c]);
+      }
+      epilogue(nt);
+      zero();
+    }
+  };
+  static_assert(MF32 >= 1 && MF32 <= 4, "row tiles per block");
+  if (mfa == MF32) run(std::integral_constant<int, MF32>{});
+  else if (MF32 > 1 && mfa == 1) run(std::integral_constant<int, 1>{});
+  else if (MF32 > 2 && mfa == 2) run(std::integral_constant<int, (MF32 > 2 ? 2 : 1)>{});
+  else run(std::integral_constant<int, (MF32 > 3 ? 3 : 1)>{});
 }
 
 namespace {
@@ -737,8 +944,58 @@ const GemmVariant* pick_variant(int bm, int epi) {
 
 }  // namespace
 
+namespace {
+// the short-K kernel for the FFN's down projections (blocks of 64 or 128 rows)
+const void* pick_kres(int bm, int epi, int nch, int& waves, int& tile_n) {
+  waves = 8;
+  tile_n = 8 * 32;
+#define MOEQ4_KRES(NCH)                                                                            \
+  if (epi == kEpiScale)                                                                          \
+    return bm == 128 ? (const void*)&k_gemm_q4_kres<128, 1, NCH, 8, kEpiScale>                   \
+           : bm == 64 ? (const void*)&k_gemm_q4_kres<64, 1, NCH, 8, kEpiScale> : nullptr;        \
+  if (epi == kEpiTerm) /* 128-row blocks of this epilogue spill: 64 rows only */              \
+    return bm == 64 ? (const void*)&k_gemm_q4_kres<64, 1, NCH, 8, kEpiTerm> : nullptr;           \
+  return nullptr;
+  if (nch == 4) { MOEQ4_KRES(4) }
+  if (nch == 2) { MOEQ4_KRES(2) }
+#undef MOEQ4_KRES
+  return nullptr;
+}
+}  // namespace
+
 hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipStream_t stream) {
   if (max_blocks <= 0) return hipSuccess;
+  static const bool no_kres = getenv("MOEQ4_NO_KRES") != nullptr;  // for comparisons
+  if (!no_kres && a.K <= kKResMax && a.K % kKC == 0) {
+    int waves, tile_n;
+    const void* fn = pick_kres(BM, epi, a.K / kKC, waves, tile_n);
+    if (fn) {
+      // columns per workgroup: all of N, or fewer when there are too few blocks
+      // to fill the GPU (the dense shared expert)
+      int nsplit = max(1, min(a.N / tile_n, 512 / max(1, max_blocks)));
+      const int NR = (a.N / nsplit + tile_n - 1) / tile_n * tile_n;
+      nsplit = (a.N + NR - 1) / NR;
+      const long long tasks = (long long)max_blocks * nsplit;
+      const dim3 grid((unsigned)((tasks + kXcds - 1) / kXcds * kXcds));
+      const size_t lds = (size_t)BM * a.K * 2;  // up to 128 KB of the 160 KB a workgroup may use
+      static const void* raised[8] = {};
+      bool done = false;
+      for (const void* r : raised) done |= r == fn;
+      if (!done) {
+        const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(BM * kKResMax * 2));
+        if (err != hipSuccess) {
+          note_hip_error(err, "hipFuncSetAttribute(k_gemm_q4_kres)");
+          return err;
+        }
+        for (const void*& r : raised)
+          if (!r) {
+            r = fn;
+            break;
+          }
+      }
+      return launch("k_gemm_q4_kres", fn, grid, dim3(waves * 64), lds, stream, a, NR);
+    }
+  }
   const GemmVariant* v = pick_variant(BM, epi);
   if (!v) return hipErrorInvalidValue;
   const int nout = epi == kEpiSwiglu ? a.N / 2 : a.N;
