@@ -37,6 +37,9 @@
  *   scales uint16 [N, K/64]  bf16
  *   biases uint16 [N, K/64]  bf16
  *   weight(n, kk) = bf16( scale[n, kk/64] * code(n, kk) + bias[n, kk/64] )
+ *   (scale * code + bias formed in fp32 with one rounding, as fma does).
+ *   Scales must be finite with magnitude below 2^100 (the kernels scale them by
+ *   2^24 on the way); biases must be finite.
  * A stack of E such matrices is [E, N, K/2] / [E, N, K/64].
  */
 #ifndef MOEQ4_H

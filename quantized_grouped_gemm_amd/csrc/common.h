@@ -26,6 +26,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
+// two fp32 values as one packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
+}
+
+// ---- exact rebuild of 4-bit codes: bf16(s*q + b) with s*q + b formed by one
+// ---- fp32 fma (exact for bf16 s, b and q < 16 unless the sum needs more than
+// ---- 24 bits, in which case it is the correctly rounded fp32 value).
+//
+// A dword of the tiled weight layout holds 8 consecutive codes with its low
+// 16-bit half holding c0,c2,c4,c6 and its high half c1,c3,c5,c7 (nibble 0 = the
+// lowest bits).  Masking leaves one code in each half; read as fp16, such a half
+// is the subnormal q*2^-24 (code in bits 0..3) or q*2^-20 (bits 4..7), exactly
+// (fp16 subnormals are kept: the kernels run with fp16 denormals on), so with
+// sc = s*2^24 (or s*2^20) one v_fma_mix_f32 per code forms s*q + b with the
+// same single rounding as fma(s, q, b).  Requires s*2^24 finite (|s| < 2^104).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t mix_pair(uint32_t m, float sc, float b) {
+  const f16x2 h = __builtin_bit_cast(f16x2, m);
+  return pk_bf16(__builtin_fmaf(sc, (float)h[0], b), __builtin_fmaf(sc, (float)h[1], b));
+}
+// the 8 codes of dword wd as 4 packed bf16 pairs (c0,c1), (c2,c3), (c4,c5), (c6,c7);
+// 17 VALU ops
+__device__ __forceinline__ uint4 rebuild_words(uint32_t wd, float s, float b) {
+  const float s24 = s * 16777216.f, s20 = s * 1048576.f;
+  const uint32_t t = wd >> 8;
+  return make_uint4(mix_pair(wd & 0x000F000Fu, s24, b), mix_pair(wd & 0x00F000F0u, s20, b),
+                    mix_pair(t & 0x000F000Fu, s24, b), mix_pair(t & 0x00F000F0u, s20, b));
+}
+
 // The FFN keeps the weighted routed terms between its two projections as fp16
 // holding value * 2^-8 (11-bit significand, range to ~1.7e7): the combine then
 // adds terms rounded 8x finer than bf16 at the same bytes.

@@ -50,33 +50,21 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
-// bf16(s*q0 + b) and bf16(s*q1 + b) packed low / high
-__device__ __forceinline__ uint32_t rebuild_pair(uint32_t q0, uint32_t q1, float s, float b) {
-  const __bf16 w0 = (__bf16)__builtin_fmaf((float)q0, s, b);  // s*q + b is exact in fp32
-  const __bf16 w1 = (__bf16)__builtin_fmaf((float)q1, s, b);
-  return (uint32_t)__builtin_bit_cast(uint16_t, w0) | ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
-}
-
-// sum over 16 consecutive K values of x * bf16(s*q + b): codes in tiled dwords
-// d0 (K +0..7) and d1 (K +8..15), x pairs in xa (K +0..7) and xb (K +8..15).
-// A tiled dword holds c0..c7 as nibbles c0,c2,c4,c6,c1,c3,c5,c7, so its bytes
-// masked with 0x0F0F0F0F are (c0,c4,c1,c5) and shifted by 4 are (c2,c6,c3,c7).
+// sum over 16 K of x * bf16(s*q + b): codes in tiled dwords d0 (K +0..7) and
+// d1 (K +8..15), x pairs in xa (K +0..7) and xb (K +8..15); the weights are
+// rebuilt exactly (rebuild_words) and multiplied in pairs by v_dot2c_f32_bf16
 __device__ __forceinline__ float dot16(uint32_t d0, uint32_t d1, uint4 xa, uint4 xb, float s, float b) {
   float p = 0.f, q = 0.f;
-  {
-    const uint32_t lo = d0 & 0x0F0F0F0Fu, hi = (d0 >> 4) & 0x0F0F0F0Fu;
-    p = dot2(rebuild_pair(lo & 0xFF, (lo >> 16) & 0xFF, s, b), xa.x, p);  // c0, c1
-    q = dot2(rebuild_pair(hi & 0xFF, (hi >> 16) & 0xFF, s, b), xa.y, q);  // c2, c3
-    p = dot2(rebuild_pair((lo >> 8) & 0xFF, lo >> 24, s, b), xa.z, p);    // c4, c5
-    q = dot2(rebuild_pair((hi >> 8) & 0xFF, hi >> 24, s, b), xa.w, q);    // c6, c7
-  }
-  {
-    const uint32_t lo = d1 & 0x0F0F0F0Fu, hi = (d1 >> 4) & 0x0F0F0F0Fu;
-    p = dot2(rebuild_pair(lo & 0xFF, (lo >> 16) & 0xFF, s, b), xb.x, p);
-    q = dot2(rebuild_pair(hi & 0xFF, (hi >> 16) & 0xFF, s, b), xb.y, q);
-    p = dot2(rebuild_pair((lo >> 8) & 0xFF, lo >> 24, s, b), xb.z, p);
-    q = dot2(rebuild_pair((hi >> 8) & 0xFF, hi >> 24, s, b), xb.w, q);
-  }
+  const uint4 w0 = rebuild_words(d0, s, b);
+  p = dot2(w0.x, xa.x, p);  // c0, c1
+  q = dot2(w0.y, xa.y, q);  // c2, c3
+  p = dot2(w0.z, xa.z, p);  // c4, c5
+  q = dot2(w0.w, xa.w, q);  // c6, c7
+  const uint4 w1 = rebuild_words(d1, s, b);
+  p = dot2(w1.x, xb.x, p);
+  q = dot2(w1.y, xb.y, q);
+  p = dot2(w1.z, xb.z, p);
+  q = dot2(w1.w, xb.w, q);
   return p + q;
 }
 

@@ -69,30 +69,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
 // (bits 4p..4p+3) holding c0,c2,c4,c6,c1,c3,c5,c7 for p = 0..7, so that
 // (dword >> 4i) & 0x000F000F is the pair (c_2i, c_2i+1) in the two 16-bit halves.
 
-// two fp32 values as one packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  typedef float f32x2v __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
-}
-
-// exact rebuild of 8 codes: bf16(s*q + b), natural K order.  The two masked
-// words are made opaque to the compiler so that each code converts with one
-// v_cvt_f32_ubyteN of its byte (the compiler would otherwise re-extract every
-// nibble with its own shift and mask).
+// exact rebuild of 8 codes as bf16 MFMA operand, natural K order (see rebuild_words)
 __device__ __forceinline__ bf16x8 rebuild_dq(uint32_t wd, float s, float b) {
-  uint32_t lo = wd & 0x0F0F0F0Fu;         // bytes: c0, c4, c1, c5
-  uint32_t hi = (wd >> 4) & 0x0F0F0F0Fu;  // bytes: c2, c6, c3, c7
-  asm("" : "+v"(lo), "+v"(hi));
-  const float c0 = __builtin_fmaf((float)(lo & 0xFF), s, b);
-  const float c4 = __builtin_fmaf((float)((lo >> 8) & 0xFF), s, b);
-  const float c1 = __builtin_fmaf((float)((lo >> 16) & 0xFF), s, b);
-  const float c5 = __builtin_fmaf((float)(lo >> 24), s, b);
-  const float c2 = __builtin_fmaf((float)(hi & 0xFF), s, b);
-  const float c6 = __builtin_fmaf((float)((hi >> 8) & 0xFF), s, b);
-  const float c3 = __builtin_fmaf((float)((hi >> 16) & 0xFF), s, b);
-  const float c7 = __builtin_fmaf((float)(hi >> 24), s, b);
-  return as_bf16x8(pk_bf16(c0, c1), pk_bf16(c2, c3), pk_bf16(c4, c5), pk_bf16(c6, c7));
+  const uint4 w = rebuild_words(wd, s, b);
+  return as_bf16x8(w.x, w.y, w.z, w.w);
 }
 
 // 8 codes as the exact bf16 values 128+q, natural K order; `one28` holds
@@ -156,6 +136,11 @@ __device__ __forceinline__ void epi_fill(const GemmArgs& a, int row0, int rows, 
   }
 }
 
+// elements 4j..4j+3 of a 32x32 MFMA accumulator (j compile-time after unrolling)
+__device__ __forceinline__ f32x4 quad(const f32x16& a, int j) {
+  return f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+}
+
 // Epilogue of one output row (row `row` of the block starting at sorted row row0).
 template <int EPI>
 struct EpiRow {
@@ -185,6 +170,22 @@ struct EpiRow {
     } else {
       y[n] = f32_to_bf16_bits(v);
     }
+  }
+  // values v[0..3] (and u[0..3] for kEpiSwiglu) of output columns n..n+3 (n % 4 == 0),
+  // written with one 8-byte store
+  __device__ __forceinline__ void store4(int n, f32x4 v, f32x4 u) const {
+    if constexpr (EPI == kEpiScale) {
+      if (!y) return;
+    }
+    uint32_t b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (EPI == kEpiSwiglu) b[q] = f32_to_bf16_bits(v[q] / (1.f + expf(-v[q])) * u[q]);
+      else if constexpr (EPI == kEpiScale) b[q] = term_bits(w * v[q]);
+      else if constexpr (EPI == kEpiTerm) b[q] = term_bits(v[q]);
+      else b[q] = f32_to_bf16_bits(v[q]);
+    }
+    *(uint2*)(y + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
   }
 };
 
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   constexpr int IPW = BM * 16 / 64 / WAVES;  // DMA instructions per wave per chunk
   static_assert(IPW * 64 * WAVES == BM * 16, "rows split evenly over the waves");
   (void)NTHR;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kKC];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[3][BM * kKC];
   const int K = a.K, N = a.N;
   const uint8_t* __restrict__ Wt = a.Wt;
   const uint16_t* __restrict__ St = a.St;
@@ -600,68 +601,109 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][f][i] = 0.f;
 
-  // MFA: the number of filled 32-row tiles, a compile-time constant so that the
-  // LDS reads and MFMAs of a K-step are straight-line code the compiler can
-  // schedule (one copy of the loop per value)
-  auto compute = [&](auto mfa_c, int buf, const St32& s, int ngroups) __attribute__((always_inline)) {
+  // K-step ks (0..7) of a chunk: K indices 64*(ks/4) + 32*half + 8*(ks%4) + [0,8) of the
+  // chunk, from lane half `half`, for the activations (LDS, row col + 32 per row
+  // tile, swizzled 16-byte column) and the rebuilt weights alike
+  auto load_a = [&](auto mfa_c, bf16x8* av, int buf, int ks) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
+    const int gi = ks >> 2, s4 = ks & 3;
+    const uint16_t* xb = &xs[buf][col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8)];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      if (gi >= ngroups) break;
+    for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kKC);
+  };
+  auto rebuild_b = [&](bf16x8* bw, const St32& s, int ks) __attribute__((always_inline)) {
+    const int gi = ks >> 2, s4 = ks & 3;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        // K indices gi*64 + 32*half + 8*s4 + [0,8): slice (2*half + s4/2), dword 2*gi + s4%2
-        bf16x8 bfr[NF32];
-#pragma unroll
-        for (int f = 0; f < NF32; ++f) {
-          const float sv = gi ? __uint_as_float(s.s[f] & 0xFFFF0000u) : __uint_as_float(s.s[f] << 16);
-          const float bv = gi ? __uint_as_float(s.b[f] & 0xFFFF0000u) : __uint_as_float(s.b[f] << 16);
-          bfr[f] = rebuild_dq(s.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
-        }
-        // row col (+32 per row tile), 16-byte column gi*8 + half*4 + s4, swizzled
-        const uint16_t* xb = &xs[buf][col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8)];
-        bf16x8 av[MFA];
-#pragma unroll
-        for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kKC);
-#pragma unroll
-        for (int r = 0; r < MFA; ++r)
-#pragma unroll
-          for (int f = 0; f < NF32; ++f)
-            acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[r], bfr[f], acc[r][f], 0, 0, 0);
-      }
+    for (int f = 0; f < NF32; ++f) {
+      const float sv = gi ? __uint_as_float(s.s[f] & 0xFFFF0000u) : __uint_as_float(s.s[f] << 16);
+      const float bv = gi ? __uint_as_float(s.b[f] & 0xFFFF0000u) : __uint_as_float(s.b[f] << 16);
+      bw[f] = rebuild_dq(s.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
     }
   };
+  auto mfma_step = [&](auto mfa_c, const bf16x8* av, const bf16x8* bw) __attribute__((always_inline)) {
+    constexpr int MFA = decltype(mfa_c)::value;
+#pragma unroll
+    for (int r = 0; r < MFA; ++r)
+#pragma unroll
+      for (int f = 0; f < NF32; ++f)
+        acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[f], av[r], acc[r][f], 0, 0, 0);
+  };
 
-  // Pipeline over the full chunks: at iteration c the DMA of chunk c+1's
-  // activations (into the LDS buffer chunk c-1 used) and the weight loads of
-  // chunk c+S-1 go out, then chunk c's MFMAs run; the barrier that ends the
-  // iteration waits for those loads, so their latency hides behind the MFMAs.
-  // Loads past the last chunk re-read it (clamped) and are not used.
+  // Pipeline over the full chunks, with three LDS buffers.  Iteration c first
+  // sends the weight loads of chunk c+S-1 and then the DMA of chunk c+2's
+  // activations (into the buffer chunk c-1 used), then runs chunk c's MFMAs,
+  // then waits until only the loads that iteration c+1 does not need are still
+  // in flight (vector memory operations complete in issue order, so this is a
+  // count: the DMA just sent, plus the weights just sent when S > 2) and ends
+  // in a barrier, after which every wave's part of chunk c+1 is in LDS.  The
+  // weights thus have S-1 chunks of compute to arrive and the activations two.
+  // Inside a chunk the K-steps are software pipelined one step deep: while the
+  // MFMAs of a step run, the next step's activation fragments are read from
+  // LDS and its weights rebuilt into the other register set; each step ends in
+  // a scheduling barrier that keeps this order.  Loads and DMAs past the last
+  // chunk re-read it (clamped) and are not used.  MFA, the number of filled
+  // 32-row tiles, is a compile-time constant (one copy of the loop per value).
+  constexpr int kLoadsPerChunk = 4 * NF32;  // vector memory instructions of load()
+  constexpr int kInFlight = IPW + (S > 2 ? kLoadsPerChunk : 0);
+  static_assert(kInFlight < 64, "vmcnt range");
   auto run = [&](auto mfa_c) __attribute__((always_inline)) {
+    constexpr int MFA = decltype(mfa_c)::value;
+    bf16x8 av[2][MFA];
+    bf16x8 bw[2][NF32];
     if (nfull > 0) {
 #pragma unroll
       for (int s = 0; s < S - 1; ++s) load(st[s], s);
       dma_x(0, 0, false);
+      dma_x(min(1, nfull - 1), 1, false);
       __syncthreads();
       for (int c0 = 0; c0 < nfull; c0 += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
           const int c = c0 + u;
-          dma_x(min(c + 1, nfull - 1), (c + 1) & 1, false);
+          const int buf = c % 3;
           load(st[(u + S - 1) % S], c + S - 1);
-          // keep the loads ahead of the MFMAs (the scheduler would otherwise
-          // sink them to the end of the iteration and expose their latency)
+          dma_x(min(c + 2, nfull - 1), (c + 2) % 3, false);
+          // keep the loads ahead of the compute (the scheduler would otherwise
+          // sink them and expose their latency)
           asm volatile("" ::: "memory");
-          if (c < nfull) compute(mfa_c, c & 1, st[u], 2);
-          __syncthreads();
+          if (c < nfull) {
+            load_a(mfa_c, av[0], buf, 0);
+            rebuild_b(bw[0], st[u], 0);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+              const int p = ks & 1;
+              if (ks < 7) {
+                load_a(mfa_c, av[p ^ 1], buf, ks + 1);
+                rebuild_b(bw[p ^ 1], st[u], ks + 1);
+              }
+              mfma_step(mfa_c, av[p], bw[p]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // vmcnt <= kInFlight (expcnt and lgkmcnt unconstrained): this wave's DMA
+          // of chunk c+1 has landed in LDS, and its LDS reads of this chunk have
+          // all returned (their MFMAs used them); the barrier then makes every
+          // wave's part of chunk c+1 visible and frees buffer c%3 for the DMA of
+          // chunk c+3.  A plain s_barrier: a __syncthreads() here would also wait
+          // for the DMA just sent (vmcnt(0)), which must stay in flight.
+          __builtin_amdgcn_s_waitcnt((kInFlight & 15) | ((kInFlight >> 4) << 14) | (7 << 4) | (15 << 8));
+          __builtin_amdgcn_s_barrier();
         }
       }
+      // drain the DMAs of the clamped chunks past the end: no write into this
+      // workgroup's LDS may still be in flight when it moves on (or ends)
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
     }
     if (odd_tail) {
       load_tail(st[0]);
       dma_x(nfull, 0, true);
       __syncthreads();
-      compute(mfa_c, 0, st[0], 1);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        load_a(mfa_c, av[0], 0, ks);
+        rebuild_b(bw[0], st[0], ks);
+        mfma_step(mfa_c, av[0], bw[0]);
+      }
     }
   };
   static_assert(MF32 >= 1 && MF32 <= 4, "row tiles per block");
@@ -670,23 +712,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   else if (MF32 > 2 && mfa == 2) run(std::integral_constant<int, (MF32 > 2 ? 2 : 1)>{});
   else run(std::integral_constant<int, (MF32 > 3 ? 3 : 1)>{});
 
-  // epilogue: 32x32 accumulator layout -- lane holds column lane&31 and rows
-  // 8*(i/4) + 4*half + i%4 (i = 0..15) of each tile
+  // epilogue: the MFMAs take the weights as the A operand, so each 32x32
+  // accumulator tile is transposed: lane l holds block row r*32 + l%32 and output
+  // columns 8*(i/4) + 4*(l/32) + i%4 (i = 0..15) of the wave's 32-column tile, i.e.
+  // four runs of 4 adjacent columns, each written with one 8-byte store
 #pragma unroll
   for (int r = 0; r < MF32; ++r) {
     if (r >= mfa) break;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = r * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (row >= rows) continue;
+    const int row = r * 32 + col;
+    if (row < rows) {
       const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
 #pragma unroll
       for (int f = 0; f < NFO; ++f) {
         if (f >= nf_live) break;
-        const int n = n_wave + f * 32 + col;
-        if (n >= NOUT) continue;
-        if constexpr (EPI == kEpiSwiglu) er.store(n, acc[r][f][i], acc[r][f + NFO][i]);
-        else er.store(n, acc[r][f][i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n_wave + f * 32 + 8 * j + 4 * half;
+          if (n >= NOUT) continue;
+          const f32x4 v = quad(acc[r][f], j);
+          if constexpr (EPI == kEpiSwiglu) er.store4(n, v, quad(acc[r][f + NFO], j));
+          else er.store4(n, v, v);
+        }
       }
     }
   }
@@ -702,11 +748,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
 // per block and the activations are read once.
 constexpr int kKResMax = 512;
 
-template <int BM, int NF32, int NCH, int WAVES, int EPI>
+template <int BM, int NF32, int NCH, int S, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a, int NR) {
-  // NCH = K / 128 chunks; the register ring has NCH stages, so that the stage
-  // of step (N tile nt, chunk c) is c: a compile-time index in the unrolled loop
-  constexpr int S = NCH;
+  // NCH = K / 128 chunks; the register ring has S stages, S dividing NCH, so
+  // that the stage of step (N tile nt, chunk c) is c % S: a compile-time index
+  // in the unrolled loop
+  static_assert(NCH % S == 0 && S >= 2, "ring stages divide the chunks");
   static_assert(EPI != kEpiSwiglu, "gate/up pairs columns across the whole N: not this kernel");
   constexpr int MF32 = BM / 32;
   constexpr int TILE_N = WAVES * NF32 * 32;
@@ -801,63 +848,88 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a, i
   };
   zero();
 
-  auto compute = [&](auto mfa_c, int c, const StK& sg) __attribute__((always_inline)) {
+  // K-step ks (0..7) of chunk c takes K indices 128c + 64*(ks/4) + 32*half + 8*(ks%4) + [0,8)
+  // from lane half `half`, for the activations (LDS) and the rebuilt weights alike
+  auto load_a = [&](auto mfa_c, bf16x8* av, int c, int ks) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
-    const uint16_t* xc = &xk[(size_t)c * BM * kKC];
+    const int gi = ks >> 2, s4 = ks & 3;
+    const uint16_t* xb = &xk[(size_t)c * BM * kKC] + col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8);
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
+    for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kKC);
+  };
+  auto rebuild_b = [&](bf16x8* bw, const StK& sg, int ks) __attribute__((always_inline)) {
+    const int gi = ks >> 2, s4 = ks & 3;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        bf16x8 bfr[NF32];
-#pragma unroll
-        for (int f = 0; f < NF32; ++f) {
-          const float sv = gi ? __uint_as_float(sg.s[f] & 0xFFFF0000u) : __uint_as_float(sg.s[f] << 16);
-          const float bv = gi ? __uint_as_float(sg.b[f] & 0xFFFF0000u) : __uint_as_float(sg.b[f] << 16);
-          bfr[f] = rebuild_dq(sg.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
-        }
-        const uint16_t* xb = xc + col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8);
-        bf16x8 av[MFA];
-#pragma unroll
-        for (int r = 0; r < MFA; ++r) av[r] = *(const bf16x8*)(xb + r * 32 * kKC);
-#pragma unroll
-        for (int r = 0; r < MFA; ++r)
-#pragma unroll
-          for (int f = 0; f < NF32; ++f)
-            acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[r], bfr[f], acc[r][f], 0, 0, 0);
-      }
+    for (int f = 0; f < NF32; ++f) {
+      const float sv = gi ? __uint_as_float(sg.s[f] & 0xFFFF0000u) : __uint_as_float(sg.s[f] << 16);
+      const float bv = gi ? __uint_as_float(sg.b[f] & 0xFFFF0000u) : __uint_as_float(sg.b[f] << 16);
+      bw[f] = rebuild_dq(sg.w[f][s4 >> 1][2 * gi + (s4 & 1)], sv, bv);
     }
   };
+  auto mfma_step = [&](auto mfa_c, const bf16x8* av, const bf16x8* bw) __attribute__((always_inline)) {
+    constexpr int MFA = decltype(mfa_c)::value;
+#pragma unroll
+    for (int r = 0; r < MFA; ++r)
+#pragma unroll
+      for (int f = 0; f < NF32; ++f)
+        acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[f], av[r], acc[r][f], 0, 0, 0);
+  };
 
+  // transposed accumulator tiles (weights are the A operand): lane l holds block
+  // row r*32 + l%32 and columns 8*(i/4) + 4*(l/32) + i%4 of each 32-column tile
   auto epilogue = [&](int nt) __attribute__((always_inline)) {
     const int n_wave = n_lo + nt * TILE_N + wave * NF32 * 32;
 #pragma unroll
     for (int r = 0; r < MF32; ++r) {
       if (r >= mfa) break;
+      const int row = r * 32 + col;
+      if (row >= rows) continue;
+      const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = r * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (row >= rows) continue;
-        const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
+      for (int f = 0; f < NF32; ++f)
 #pragma unroll
-        for (int f = 0; f < NF32; ++f) {
-          const int n = n_wave + f * 32 + col;
-          if (n < n_hi) er.store(n, acc[r][f][i]);
+        for (int j = 0; j < 4; ++j) {
+          const int n = n_wave + f * 32 + 8 * j + 4 * half;
+          if (n < n_hi) er.store4(n, quad(acc[r][f], j), quad(acc[r][f], j));
         }
-      }
     }
   };
 
+  // Software pipeline, one K-step deep: while the MFMAs of step g run, the
+  // activation fragments of step g+1 are read from LDS and its weights rebuilt
+  // into the other register set.  The last step of a chunk reads the next
+  // chunk's activations (or chunk 0's, for the next N tile); it also rebuilds
+  // that chunk's first weights when the ring is deep enough (S > 2) for them
+  // to have been loaded a chunk earlier -- with S = 2 they were sent at the
+  // start of this chunk, and the first rebuild waits for the chunk boundary.
+  // Each step ends in a scheduling barrier so that the compiler keeps this
+  // order rather than reading LDS just before each MFMA.
+  constexpr bool kCrossRebuild = S > 2;
   auto run = [&](auto mfa_c) __attribute__((always_inline)) {
+    constexpr int MFA = decltype(mfa_c)::value;
+    bf16x8 av[2][MFA > 0 ? MFA : 1];
+    bf16x8 bw[2][NF32];
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) load(st[s], s);
     __syncthreads();  // the activations are in LDS (the barrier waits for the DMA)
+    load_a(mfa_c, av[0], 0, 0);
+    if (kCrossRebuild) rebuild_b(bw[0], st[0], 0);
     for (int nt = 0; nt < ntl; ++nt) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        // the load of step j + S - 1 (the same chunk index as c - 1 of this ring)
+        // the load of step j + S - 1 into the stage step j - 1 used
         load(st[(c + S - 1) % S], nt * NCH + c + S - 1);
         asm volatile("" ::: "memory");  // keep the loads ahead of the MFMAs
-        compute(mfa_c, c, st[c]);
+        if (!kCrossRebuild) rebuild_b(bw[0], st[c % S], 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int p = ks & 1;  // 8 steps per chunk: the parity restarts with each chunk
+          const int cn = ks < 7 ? c : (c + 1) % NCH;
+          load_a(mfa_c, av[p ^ 1], cn, (ks + 1) & 7);
+          if (ks < 7 || kCrossRebuild) rebuild_b(bw[p ^ 1], st[cn % S], (ks + 1) & 7);
+          mfma_step(mfa_c, av[p], bw[p]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       epilogue(nt);
       zero();
@@ -926,6 +998,8 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM_W32(64, 2, 3, 4, kEpiPlain),
     MOEQ4_GEMM_W32(64, 2, 4, 4, kEpiPlain),
     MOEQ4_GEMM_W32(64, 1, 3, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiSwiglu),
+    MOEQ4_GEMM_W32(128, 2, 3, 8, kEpiSwiglu),
 };
 #undef MOEQ4_GEMM_VARIANT
 #undef MOEQ4_GEMM_W32
@@ -945,20 +1019,39 @@ const GemmVariant* pick_variant(int bm, int epi) {
 }  // namespace
 
 namespace {
-// the short-K kernel for the FFN's down projections (blocks of 64 or 128 rows)
-const void* pick_kres(int bm, int epi, int nch, int& waves, int& tile_n) {
-  waves = 8;
-  tile_n = 8 * 32;
-#define MOEQ4_KRES(NCH)                                                                            \
-  if (epi == kEpiScale)                                                                          \
-    return bm == 128 ? (const void*)&k_gemm_q4_kres<128, 1, NCH, 8, kEpiScale>                   \
-           : bm == 64 ? (const void*)&k_gemm_q4_kres<64, 1, NCH, 8, kEpiScale> : nullptr;        \
-  if (epi == kEpiTerm) /* 128-row blocks of this epilogue spill: 64 rows only */              \
-    return bm == 64 ? (const void*)&k_gemm_q4_kres<64, 1, NCH, 8, kEpiTerm> : nullptr;           \
-  return nullptr;
-  if (nch == 4) { MOEQ4_KRES(4) }
-  if (nch == 2) { MOEQ4_KRES(2) }
+// the short-K kernel for the FFN's down projections (blocks of 64 or 128 rows);
+// the first entry of each (block height, epilogue, chunks) is its default and
+// MOEQ4_KRES_VARIANT=<name> picks another for tuning sweeps
+struct KresVariant {
+  const char* name;
+  int bm, epi, nch, waves, tile_n;
+  const void* fn;
+};
+#define MOEQ4_KRES(BM, NF32, NCH, S, WAVES, EPI)                                                   \
+  {"kres_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, EPI, NCH, WAVES, WAVES * NF32 * 32,           \
+   (const void*)&k_gemm_q4_kres<BM, NF32, NCH, S, WAVES, EPI>}
+const KresVariant kKres[] = {
+    MOEQ4_KRES(128, 1, 4, 4, 8, kEpiScale),
+    MOEQ4_KRES(64, 1, 4, 4, 8, kEpiScale),
+    MOEQ4_KRES(64, 1, 4, 4, 8, kEpiTerm),  // 128-row blocks of this epilogue: see the tall-block kernel
+    MOEQ4_KRES(128, 1, 2, 2, 8, kEpiScale),
+    MOEQ4_KRES(64, 1, 2, 2, 8, kEpiScale),
+    MOEQ4_KRES(64, 1, 2, 2, 8, kEpiTerm),
+    // alternatives for tuning sweeps
+    MOEQ4_KRES(128, 2, 4, 2, 8, kEpiScale),
+    MOEQ4_KRES(128, 2, 4, 2, 4, kEpiScale),
+    MOEQ4_KRES(64, 2, 4, 2, 8, kEpiTerm),
+    MOEQ4_KRES(64, 2, 4, 2, 4, kEpiTerm),
+    MOEQ4_KRES(128, 1, 4, 2, 8, kEpiScale),
+};
 #undef MOEQ4_KRES
+const KresVariant* pick_kres(int bm, int epi, int nch) {
+  static const char* forced = getenv("MOEQ4_KRES_VARIANT");
+  if (forced)
+    for (const KresVariant& v : kKres)
+      if (v.bm == bm && v.epi == epi && v.nch == nch && strcmp(v.name, forced) == 0) return &v;
+  for (const KresVariant& v : kKres)
+    if (v.bm == bm && v.epi == epi && v.nch == nch) return &v;
   return nullptr;
 }
 }  // namespace
@@ -967,9 +1060,10 @@ hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipSt
   if (max_blocks <= 0) return hipSuccess;
   static const bool no_kres = getenv("MOEQ4_NO_KRES") != nullptr;  // for comparisons
   if (!no_kres && a.K <= kKResMax && a.K % kKC == 0) {
-    int waves, tile_n;
-    const void* fn = pick_kres(BM, epi, a.K / kKC, waves, tile_n);
-    if (fn) {
+    const KresVariant* kv = pick_kres(BM, epi, a.K / kKC);
+    if (kv) {
+      const void* fn = kv->fn;
+      const int waves = kv->waves, tile_n = kv->tile_n;
       // columns per workgroup: all of N, or fewer when there are too few blocks
       // to fill the GPU (the dense shared expert)
       int nsplit = max(1, min(a.N / tile_n, 512 / max(1, max_blocks)));
@@ -978,7 +1072,7 @@ hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipSt
       const long long tasks = (long long)max_blocks * nsplit;
       const dim3 grid((unsigned)((tasks + kXcds - 1) / kXcds * kXcds));
       const size_t lds = (size_t)BM * a.K * 2;  // up to 128 KB of the 160 KB a workgroup may use
-      static const void* raised[8] = {};
+      static const void* raised[16] = {};
       bool done = false;
       for (const void* r : raised) done |= r == fn;
       if (!done) {
