@@ -224,9 +224,61 @@ struct GemmArgs {
   const int32_t* num_blocks;  // device count of block-map entries
   uint16_t* Y;                // output, row stride ldy
   int ldy;
-  const int32_t* perm;        // kEpiScale
+  const int32_t* perm;        // kEpiScale; null: row p goes to row p with weight 1
   const float* topk_w;        // kEpiScale
+  // Optional dense second problem run by the same launch (the shared expert
+  // next to the routed ones): rows 0..d_rows-1 of dX through one expert's
+  // weights dWt/dSt/dBt into dY (same K, N, ldy and epilogue; kEpiScale rows
+  // keep their index and weight 1).  d_rows == 0: none.
+  const uint16_t* dX;
+  int d_rows;
+  const uint8_t* dWt;
+  const uint16_t* dSt;
+  const uint16_t* dBt;
+  uint16_t* dY;
 };
+
+// Workgroup -> task of a launch with dense tasks (dense_tasks, first on every
+// XCD) ahead of the routed ones (routed_tasks, counted on the device).
+// Workgroup i runs on XCD i % 8; on each XCD the first ceil(dense_tasks / 8)
+// slots take the dense tasks, so they start in the first wave of workgroups
+// and spread over all XCDs.  Returns false when the workgroup has no task.
+__device__ __forceinline__ bool gemm_task(int dense_tasks, int routed_tasks, bool& dense, int& task) {
+  constexpr int kX = 8;
+  const int xcd = blockIdx.x % kX, slot = blockIdx.x / kX;
+  const int dper = (dense_tasks + kX - 1) / kX;
+  if (slot < dper) {
+    dense = true;
+    task = xcd * dper + slot;
+    return task < dense_tasks;
+  }
+  dense = false;
+  const int per_xcd = (routed_tasks + kX - 1) / kX;
+  if (slot - dper >= per_xcd) return false;
+  task = xcd * per_xcd + (slot - dper);
+  return task < routed_tasks;
+}
+
+// the arguments of the dense problem, as a problem of its own
+__device__ __forceinline__ GemmArgs gemm_dense(const GemmArgs& a) {
+  GemmArgs d = a;
+  d.X = a.dX;
+  d.xrows = a.d_rows;
+  d.E = 1;
+  d.A = a.d_rows;
+  d.k = 1;
+  d.Wt = a.dWt;
+  d.St = a.dSt;
+  d.Bt = a.dBt;
+  d.gather = nullptr;
+  d.blocks = nullptr;
+  d.num_blocks = nullptr;
+  d.Y = a.dY;
+  d.perm = nullptr;
+  d.topk_w = nullptr;
+  d.d_rows = 0;
+  return d;
+}
 
 hipError_t gemm_launch(const GemmArgs& a, int epi, int block_rows, int max_blocks, hipStream_t stream);
 

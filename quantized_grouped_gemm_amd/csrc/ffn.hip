@@ -10,6 +10,10 @@
 //   section "Dequantize weights during matrix multiplication": all four
 //   products rebuild the 4-bit weights on chip.
 //
+// Steps 1 and 2 (and 3 and 4) share one launch when the routed blocks are tall:
+// the shared expert is then the launch's dense second problem, whose tasks the
+// first workgroups on every XCD take.
+//
 //   1. routed gate+up   h[p]  = bf16(silu(G x) * (U x))   rows p in expert-sorted order,
 //                                                      x = X[perm[p] / k]
 //   2. shared gate+up   hs[t] = bf16(silu(Gs x_t) * (Us x_t))   dense, all T tokens
@@ -89,7 +93,12 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   uint16_t* Dsh = shared ? (uint16_t*)(ws + p.ws_dsh) : nullptr;
   const int sh_blocks = (T + p.bm_shared - 1) / p.bm_shared;
 
-  // 1. routed gate+up with SwiGLU
+  // The shared expert's two projections join the routed launches as their
+  // dense second problem when the routed blocks are tall (64 or 128 rows: the
+  // kernels that take one); otherwise they are launches of their own.
+  const bool fuse = shared && BM >= 64;
+
+  // 1. routed gate+up with SwiGLU (+ shared gate+up)
   GemmArgs g{};
   g.X = X;
   g.xrows = T;
@@ -106,11 +115,19 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   g.num_blocks = num_blocks;
   g.Y = h;
   g.ldy = I;
+  if (fuse) {
+    g.dX = X;
+    g.d_rows = T;
+    g.dWt = sh_gu_q;
+    g.dSt = sh_gu_s;
+    g.dBt = sh_gu_b;
+    g.dY = hs;
+  }
   hipError_t err = gemm_launch(g, kEpiSwiglu, BM, max_blocks, stream);
   if (err != hipSuccess) return err;
 
   // 2. shared gate+up, dense over the tokens
-  if (shared) {
+  if (shared && !fuse) {
     GemmArgs s = g;
     s.E = 1;
     s.A = T;
@@ -145,11 +162,19 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   d.ldy = H;
   d.perm = perm;
   d.topk_w = topk_w;
+  if (fuse) {  // the shared rows keep their index and weight 1: Dsh[t] = term_bits(Ds hs[t])
+    d.dX = hs;
+    d.d_rows = T;
+    d.dWt = sh_dn_q;
+    d.dSt = sh_dn_s;
+    d.dBt = sh_dn_b;
+    d.dY = Dsh;
+  }
   err = gemm_launch(d, kEpiScale, BM, max_blocks, stream);
   if (err != hipSuccess) return err;
 
   // 4. shared down, dense over the tokens
-  if (shared) {
+  if (shared && !fuse) {
     GemmArgs s{};
     s.X = hs;
     s.xrows = T;

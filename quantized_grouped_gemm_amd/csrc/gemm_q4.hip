@@ -128,6 +128,11 @@ template <int EPI>
 __device__ __forceinline__ void epi_fill(const GemmArgs& a, int row0, int rows, EpiTab* tab) {
   if constexpr (EPI == kEpiScale) {
     for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+      if (!a.perm) {  // dense problem: rows keep their index, weight 1
+        tab->as[r] = row0 + r;
+        tab->w[r] = 1.f;
+        continue;
+      }
       const int as = a.perm[row0 + r];
       const bool ok = as >= 0 && as < a.A;  // a malformed permutation writes nothing
       tab->as[r] = ok ? as : -1;
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
 // g then takes K indices g*64 + 32h + 8*s4 + [0,8) from lane half h, for both
 // operands, so every K-step stays inside one scale group.
 template <int BM, int NF32, int S, int WAVES, int EPI>
-__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
   static_assert(EPI != kEpiSwiglu || NF32 % 2 == 0, "SwiGLU pairs gate and up fragments");
   constexpr int MF32 = BM / 32;
   constexpr int NTHR = WAVES * 64;
@@ -478,19 +483,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
   static_assert(IPW * 64 * WAVES == BM * 16, "rows split evenly over the waves");
   (void)NTHR;
   __shared__ __attribute__((aligned(16))) uint16_t xs[3][BM * kKC];
+  const int NOUT = EPI == kEpiSwiglu ? a0.N / 2 : a0.N;
+  const int ntiles = (NOUT + TILE_N - 1) / TILE_N;
+  bool dense;
+  int task;
+  if (!gemm_task((a0.d_rows + BM - 1) / BM * ntiles, gemm_nblocks(a0, BM) * ntiles, dense, task)) return;
+  const GemmArgs a = dense ? gemm_dense(a0) : a0;
   const int K = a.K, N = a.N;
   const uint8_t* __restrict__ Wt = a.Wt;
   const uint16_t* __restrict__ St = a.St;
   const uint16_t* __restrict__ Bt = a.Bt;
-  const int NOUT = EPI == kEpiSwiglu ? N / 2 : N;
-
-  const int ntiles = (NOUT + TILE_N - 1) / TILE_N;
-  const int total = gemm_nblocks(a, BM) * ntiles;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int task = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (task >= total) return;
   const int blk = task / ntiles;
   const int ntile = task - blk * ntiles;
   int e, row0, rows;
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a) {
 constexpr int kKResMax = 512;
 
 template <int BM, int NF32, int NCH, int S, int WAVES, int EPI>
-__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a, int NR) {
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a0, int NR) {
   // NCH = K / 128 chunks; the register ring has S stages, S dividing NCH, so
   // that the stage of step (N tile nt, chunk c) is c % S: a compile-time index
   // in the unrolled loop
@@ -760,14 +762,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a, i
   constexpr int IPW = BM * 16 / 64 / WAVES;  // DMA instructions per wave per chunk
   static_assert(IPW * 64 * WAVES == BM * 16, "rows split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) uint16_t xk[];  // [K/128][BM][128]
+  const int nsplit = (a0.N + NR - 1) / NR;
+  bool dense;
+  int task;
+  if (!gemm_task((a0.d_rows + BM - 1) / BM * nsplit, gemm_nblocks(a0, BM) * nsplit, dense, task)) return;
+  const GemmArgs a = dense ? gemm_dense(a0) : a0;
   const int K = a.K, N = a.N;
-  const int nsplit = (N + NR - 1) / NR;
-  const int total = gemm_nblocks(a, BM) * nsplit;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int task = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (task >= total) return;
   const int blk = task / nsplit;
   const int n_lo = (task - blk * nsplit) * NR;
   const int n_hi = min(N, n_lo + NR);
@@ -951,14 +951,16 @@ struct GemmVariant {
   int tile_n;  // output columns per workgroup
   int waves;   // waves per workgroup
   const void* fn;
+  bool dense;  // runs a dense second problem (GemmArgs::d_rows)
 };
 
 #define MOEQ4_GEMM_VARIANT(BM, NF, CQ, S, WAUX, WAVES, EPI)                                      \
   {"bm" #BM "_nf" #NF "_" #CQ "_s" #S "_a" #WAUX "_w" #WAVES, BM, EPI,                         \
-   WAVES * NF * 16 / (EPI == kEpiSwiglu ? 2 : 1), WAVES, (const void*)&k_gemm_q4<BM, NF, CQ, S, WAUX, WAVES, EPI>}
+   WAVES * NF * 16 / (EPI == kEpiSwiglu ? 2 : 1), WAVES, (const void*)&k_gemm_q4<BM, NF, CQ, S, WAUX, WAVES, EPI>, \
+   false}
 #define MOEQ4_GEMM_W32(BM, NF32, S, WAVES, EPI)                                                  \
   {"w32_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, EPI, WAVES * NF32 * 32 / (EPI == kEpiSwiglu ? 2 : 1), \
-   WAVES, (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES, EPI>}
+   WAVES, (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES, EPI>, true}
 
 // The first entry of each (block height, epilogue) is its default, from sweeps
 // on MI355X.  WAUX is the cache policy of the weight loads.  The single
@@ -1056,8 +1058,15 @@ const KresVariant* pick_kres(int bm, int epi, int nch) {
 }
 }  // namespace
 
+// grid of a launch with dense_tasks dense tasks and at most routed_tasks routed ones
+static dim3 task_grid(long long dense_tasks, long long routed_tasks) {
+  return dim3((unsigned)(((dense_tasks + kXcds - 1) / kXcds + (routed_tasks + kXcds - 1) / kXcds) * kXcds));
+}
+
 hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipStream_t stream) {
-  if (max_blocks <= 0) return hipSuccess;
+  max_blocks = max(max_blocks, 0);
+  if (max_blocks == 0 && a.d_rows <= 0) return hipSuccess;
+  const long long dense_blocks = a.d_rows > 0 ? (a.d_rows + BM - 1) / BM : 0;
   static const bool no_kres = getenv("MOEQ4_NO_KRES") != nullptr;  // for comparisons
   if (!no_kres && a.K <= kKResMax && a.K % kKC == 0) {
     const KresVariant* kv = pick_kres(BM, epi, a.K / kKC);
@@ -1069,8 +1078,7 @@ hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipSt
       int nsplit = max(1, min(a.N / tile_n, 512 / max(1, max_blocks)));
       const int NR = (a.N / nsplit + tile_n - 1) / tile_n * tile_n;
       nsplit = (a.N + NR - 1) / NR;
-      const long long tasks = (long long)max_blocks * nsplit;
-      const dim3 grid((unsigned)((tasks + kXcds - 1) / kXcds * kXcds));
+      const dim3 grid = task_grid(dense_blocks * nsplit, (long long)max_blocks * nsplit);
       const size_t lds = (size_t)BM * a.K * 2;  // up to 128 KB of the 160 KB a workgroup may use
       static const void* raised[16] = {};
       bool done = false;
@@ -1091,11 +1099,11 @@ hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipSt
     }
   }
   const GemmVariant* v = pick_variant(BM, epi);
-  if (!v) return hipErrorInvalidValue;
+  if (!v || (dense_blocks > 0 && !v->dense)) return hipErrorInvalidValue;
   const int nout = epi == kEpiSwiglu ? a.N / 2 : a.N;
-  const long long tasks = (long long)max_blocks * ((nout + v->tile_n - 1) / v->tile_n);
-  const dim3 grid((unsigned)((tasks + kXcds - 1) / kXcds * kXcds));
-  return launch("k_gemm_q4", v->fn, grid, dim3(v->waves * 64), 0, stream, a);
+  const long long ntiles = (nout + v->tile_n - 1) / v->tile_n;
+  return launch("k_gemm_q4", v->fn, task_grid(dense_blocks * ntiles, max_blocks * ntiles), dim3(v->waves * 64), 0,
+                stream, a);
 }
 
 hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wt,
