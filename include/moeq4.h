@@ -109,7 +109,7 @@ size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows);
  * workspace: device scratch of at least moe_route_workspace_bytes(...) bytes
  *            (may be NULL when that is 0).
  * Sizes: T >= 0, 1 <= k <= min(E, MOEQ4_MAX_TOPK), E <= MOEQ4_MAX_EXPERTS,
- *        block_rows in {0 (default), 16, 32, 64, 128}.
+ *        block_rows in {0 (default), 16, 32, 64, 128, 256}.
  * T = 0 writes zero counts and offsets and num_blocks = 0.
  * Output buffers must not overlap each other or the workspace. */
 int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t* topk_ids,
@@ -168,7 +168,7 @@ int moe_prepack_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t*
  *                            assignment perm[p]); rows not covered by a block
  *                            are not written.
  * Sizes: T >= 0, K % 64 == 0, K >= 64, N % 16 == 0, N >= 16, 1 <= k <= E,
- *        E <= MOEQ4_MAX_EXPERTS, block_rows in {0, 16, 32, 64, 128} and equal
+ *        E <= MOEQ4_MAX_EXPERTS, block_rows in {0, 16, 32, 64, 128, 256} and equal
  *        to the value given to moe_route, max_blocks >= moe_max_blocks(T, E,
  *        k, block_rows), T*K*2 and E*N*K/2 below 2^31.  Y must not overlap the
  *        inputs. */

@@ -120,9 +120,22 @@ __device__ __forceinline__ int gemm_xrow(const GemmArgs& a, int p) {
 // goes back to and its routing weight, read once before the main loop (the
 // epilogue then needs no dependent global loads between its stores).
 struct EpiTab {
-  int as[128];
-  float w[128];
+  int as[256];
+  float w[256];
 };
+
+// f(std::integral_constant<int, m>) with m = clamp(mfa, 1, M): the number of
+// filled 32-row tiles of a block as a compile-time constant (one copy of the
+// caller's loop per value)
+template <int M, typename F>
+__device__ __forceinline__ void with_mfa(int mfa, F&& f) {
+  if constexpr (M <= 1) {
+    f(std::integral_constant<int, 1>{});
+  } else {
+    if (mfa >= M) f(std::integral_constant<int, M>{});
+    else with_mfa<M - 1>(mfa, f);
+  }
+}
 
 template <int EPI>
 __device__ __forceinline__ void epi_fill(const GemmArgs& a, int row0, int rows, EpiTab* tab) {
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   const int ntile = task - blk * ntiles;
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
-  static_assert(BM <= 128, "the epilogue table holds 128 rows");
+  static_assert(BM <= 256, "the epilogue table holds 256 rows");
   __shared__ EpiTab ep_tab;
   epi_fill<EPI>(a, row0, rows, &ep_tab);
   uint16_t* const Yout = a.Y;
@@ -457,11 +470,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tall blocks (64/128 rows): bf16 MFMA 32x32x16, exact bf16 rebuild (DQ).
+// Tall blocks (64/128/256 rows): bf16 MFMA 32x32x16, exact bf16 rebuild (DQ).
 //
 // One wave covers every row of the block (BM/32 row tiles) and NF32 tiles of
 // 32 columns, so each rebuilt weight feeds BM/32 MFMAs, and the 32x32x16 MFMA
-// keeps the matrix cores busy with only a few independent accumulators.  The
+// keeps the matrix cores busy with only a few independent accumulators.  With
+// SwiGLU and NF32 == 1 the wave's one tile pairs 16 gate columns (tile rows
+// 0..15) with their 16 up columns (rows 16..31); in the transposed accumulator
+// a lane then holds gate element i and its up partner at i + 8.  The
 // weights come from the same tiled layout: for 32-column tile u, lane
 // l = 32h + n (h in 0..1, n in 0..31) loads the two 16-byte quarter slices
 // q = 2h and 2h+1 of column n%16 of 16-row tile 2u + n/16, i.e. 32 codes of
@@ -469,12 +485,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
 // g then takes K indices g*64 + 32h + 8*s4 + [0,8) from lane half h, for both
 // operands, so every K-step stays inside one scale group.
 template <int BM, int NF32, int S, int WAVES, int EPI>
-__global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
-  static_assert(EPI != kEpiSwiglu || NF32 % 2 == 0, "SwiGLU pairs gate and up fragments");
+__global__ __launch_bounds__(WAVES * 64, WAVES == 4 ? 2 : 1) void k_gemm_q4_w32(const GemmArgs a0) {
+  constexpr bool PAIRED = EPI == kEpiSwiglu && NF32 == 1;  // gate and up in one tile
+  static_assert(EPI != kEpiSwiglu || NF32 % 2 == 0 || PAIRED, "SwiGLU pairs gate and up fragments");
   constexpr int MF32 = BM / 32;
   constexpr int NTHR = WAVES * 64;
-  constexpr int NFO = EPI == kEpiSwiglu ? NF32 / 2 : NF32;  // output fragments per wave
-  constexpr int TILE_N = WAVES * NFO * 32;                  // output columns per workgroup
+  constexpr int NFO = EPI == kEpiSwiglu && !PAIRED ? NF32 / 2 : NF32;  // output fragments per wave
+  constexpr int OUTF = PAIRED ? 16 : 32;                                // output columns per fragment
+  constexpr int TILE_N = WAVES * NFO * OUTF;                            // output columns per workgroup
+  // activation buffers in LDS: three (the DMA runs two chunks ahead) for 8-wave
+  // workgroups of up to 128 rows; two where that would not fit or where two
+  // 4-wave workgroups should share a CU (2 x 64 KB for 128 rows)
+  constexpr int NBUF = BM <= 128 && WAVES >= 8 ? 3 : 2;
   // Activations reach LDS by DMA (buffer_load ... lds): each wave instruction
   // fills 1 KB = 4 rows of 256 B.  In row r, 16-byte slot s holds the row's
   // 16-byte column s ^ (r & 15), so that the 32 rows an MFMA operand read
@@ -482,7 +504,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
   constexpr int IPW = BM * 16 / 64 / WAVES;  // DMA instructions per wave per chunk
   static_assert(IPW * 64 * WAVES == BM * 16, "rows split evenly over the waves");
   (void)NTHR;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[3][BM * kKC];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NBUF][BM * kKC];
   const int NOUT = EPI == kEpiSwiglu ? a0.N / 2 : a0.N;
   const int ntiles = (NOUT + TILE_N - 1) / TILE_N;
   bool dense;
@@ -497,7 +519,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
   const int ntile = task - blk * ntiles;
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
-  static_assert(BM <= 128, "the epilogue table holds 128 rows");
+  static_assert(BM <= 256, "the epilogue table holds 256 rows");
   __shared__ EpiTab ep_tab;
   epi_fill<EPI>(a, row0, rows, &ep_tab);
   uint16_t* const Yout = a.Y;
@@ -508,7 +530,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
   const int half = lane >> 5;   // K half inside a K-step
   const int col = lane & 31;    // column inside a 32-column tile
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_wave = ntile * TILE_N + wave * NFO * 32;  // first output column of the wave
+  const int n_wave = ntile * TILE_N + wave * NFO * OUTF;  // first output column of the wave
   const int G = K / kGroup;
   const int nfull = G >> 1;
   const bool odd_tail = (G & 1) != 0;
@@ -531,11 +553,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
   int tile16[NF32];
 #pragma unroll
   for (int f = 0; f < NF32; ++f) {
-    const int n = f < NFO ? n_wave + f * 32 + col : NOUT + n_wave + (f - NFO) * 32 + col;
+    int n;
+    if constexpr (PAIRED) n = col < 16 ? n_wave + col : NOUT + n_wave + (col - 16);
+    else n = f < NFO ? n_wave + f * 32 + col : NOUT + n_wave + (f - NFO) * 32 + col;
     tile16[f] = min(n >> 4, NT - 1);
   }
   const int r16 = col & 15;
-  const int nf_live = min(NFO, max(0, (NOUT - n_wave + 31) / 32));
+  const int nf_live = min(NFO, max(0, (NOUT - n_wave + OUTF - 1) / OUTF));
 
   const int x_oob = a.xrows * K * 2;  // rows past the block: the load returns zeros, no traffic
   // this lane's DMA source per instruction: row rb + lane/16, 16-byte column
@@ -631,22 +655,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
         acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[f], av[r], acc[r][f], 0, 0, 0);
   };
 
-  // Pipeline over the full chunks, with three LDS buffers.  Iteration c first
+  // Pipeline over the full chunks.  With three LDS buffers, iteration c first
   // sends the weight loads of chunk c+S-1 and then the DMA of chunk c+2's
-  // activations (into the buffer chunk c-1 used), then runs chunk c's MFMAs,
-  // then waits until only the loads that iteration c+1 does not need are still
-  // in flight (vector memory operations complete in issue order, so this is a
-  // count: the DMA just sent, plus the weights just sent when S > 2) and ends
-  // in a barrier, after which every wave's part of chunk c+1 is in LDS.  The
-  // weights thus have S-1 chunks of compute to arrive and the activations two.
-  // Inside a chunk the K-steps are software pipelined one step deep: while the
-  // MFMAs of a step run, the next step's activation fragments are read from
-  // LDS and its weights rebuilt into the other register set; each step ends in
-  // a scheduling barrier that keeps this order.  Loads and DMAs past the last
-  // chunk re-read it (clamped) and are not used.  MFA, the number of filled
-  // 32-row tiles, is a compile-time constant (one copy of the loop per value).
+  // activations (into the buffer chunk c-1 used); with two, the DMA of chunk
+  // c+1 and then the weight loads.  Then chunk c's MFMAs run, then the wave
+  // waits until only the loads that iteration c+1 does not need are still in
+  // flight (vector memory operations complete in issue order, so this is a
+  // count) and the iteration ends in a barrier, after which every wave's part
+  // of chunk c+1 is in LDS.  Inside a chunk the K-steps are software pipelined
+  // one step deep: while the MFMAs of a step run, the next step's activation
+  // fragments are read from LDS and its weights rebuilt into the other register
+  // set; each step ends in a scheduling barrier that keeps this order.  Loads
+  // and DMAs past the last chunk re-read it (clamped) and are not used.
   constexpr int kLoadsPerChunk = 4 * NF32;  // vector memory instructions of load()
-  constexpr int kInFlight = IPW + (S > 2 ? kLoadsPerChunk : 0);
+  constexpr int kAhead = NBUF - 1;           // chunks the DMA runs ahead
+  constexpr int kInFlight = (NBUF == 3 ? IPW : 0) + (S > 2 ? kLoadsPerChunk : 0);
   static_assert(kInFlight < 64, "vmcnt range");
   auto run = [&](auto mfa_c) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
@@ -655,16 +678,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
     if (nfull > 0) {
 #pragma unroll
       for (int s = 0; s < S - 1; ++s) load(st[s], s);
-      dma_x(0, 0, false);
-      dma_x(min(1, nfull - 1), 1, false);
+#pragma unroll
+      for (int b = 0; b < kAhead; ++b) dma_x(min(b, nfull - 1), b, false);
       __syncthreads();
       for (int c0 = 0; c0 < nfull; c0 += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
           const int c = c0 + u;
-          const int buf = c % 3;
-          load(st[(u + S - 1) % S], c + S - 1);
-          dma_x(min(c + 2, nfull - 1), (c + 2) % 3, false);
+          const int buf = c % NBUF;
+          if constexpr (NBUF == 3) {
+            load(st[(u + S - 1) % S], c + S - 1);
+            dma_x(min(c + kAhead, nfull - 1), (c + kAhead) % NBUF, false);
+          } else {
+            dma_x(min(c + kAhead, nfull - 1), (c + kAhead) % NBUF, false);
+            load(st[(u + S - 1) % S], c + S - 1);
+          }
           // keep the loads ahead of the compute (the scheduler would otherwise
           // sink them and expose their latency)
           asm volatile("" ::: "memory");
@@ -685,9 +713,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
           // vmcnt <= kInFlight (expcnt and lgkmcnt unconstrained): this wave's DMA
           // of chunk c+1 has landed in LDS, and its LDS reads of this chunk have
           // all returned (their MFMAs used them); the barrier then makes every
-          // wave's part of chunk c+1 visible and frees buffer c%3 for the DMA of
-          // chunk c+3.  A plain s_barrier: a __syncthreads() here would also wait
-          // for the DMA just sent (vmcnt(0)), which must stay in flight.
+          // wave's part of chunk c+1 visible and frees buffer c % NBUF for the
+          // next DMA.  A plain s_barrier: a __syncthreads() here would also wait
+          // for every DMA in flight (vmcnt(0)).
           __builtin_amdgcn_s_waitcnt((kInFlight & 15) | ((kInFlight >> 4) << 14) | (7 << 4) | (15 << 8));
           __builtin_amdgcn_s_barrier();
         }
@@ -708,32 +736,40 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_w32(const GemmArgs a0) {
       }
     }
   };
-  static_assert(MF32 >= 1 && MF32 <= 4, "row tiles per block");
-  if (mfa == MF32) run(std::integral_constant<int, MF32>{});
-  else if (MF32 > 1 && mfa == 1) run(std::integral_constant<int, 1>{});
-  else if (MF32 > 2 && mfa == 2) run(std::integral_constant<int, (MF32 > 2 ? 2 : 1)>{});
-  else run(std::integral_constant<int, (MF32 > 3 ? 3 : 1)>{});
+  static_assert(MF32 >= 1 && MF32 <= 8, "row tiles per block");
+  with_mfa<MF32>(mfa, run);
 
   // epilogue: the MFMAs take the weights as the A operand, so each 32x32
-  // accumulator tile is transposed: lane l holds block row r*32 + l%32 and output
-  // columns 8*(i/4) + 4*(l/32) + i%4 (i = 0..15) of the wave's 32-column tile, i.e.
-  // four runs of 4 adjacent columns, each written with one 8-byte store
+  // accumulator tile is transposed: lane l holds block row r*32 + l%32 and tile
+  // rows 8*(i/4) + 4*(l/32) + i%4 (i = 0..15), i.e. four runs of 4 adjacent
+  // columns, each written with one 8-byte store.  Paired SwiGLU: runs 0 and 1
+  // are gate columns whose up partners are runs 2 and 3.
 #pragma unroll
   for (int r = 0; r < MF32; ++r) {
     if (r >= mfa) break;
     const int row = r * 32 + col;
     if (row < rows) {
       const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
+      if constexpr (PAIRED) {
+        if (nf_live > 0) {
 #pragma unroll
-      for (int f = 0; f < NFO; ++f) {
-        if (f >= nf_live) break;
+          for (int j = 0; j < 2; ++j) {
+            const int n = n_wave + 8 * j + 4 * half;
+            if (n < NOUT) er.store4(n, quad(acc[r][0], j), quad(acc[r][0], j + 2));
+          }
+        }
+      } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n_wave + f * 32 + 8 * j + 4 * half;
-          if (n >= NOUT) continue;
-          const f32x4 v = quad(acc[r][f], j);
-          if constexpr (EPI == kEpiSwiglu) er.store4(n, v, quad(acc[r][f + NFO], j));
-          else er.store4(n, v, v);
+        for (int f = 0; f < NFO; ++f) {
+          if (f >= nf_live) break;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = n_wave + f * 32 + 8 * j + 4 * half;
+            if (n >= NOUT) continue;
+            const f32x4 v = quad(acc[r][f], j);
+            if constexpr (EPI == kEpiSwiglu) er.store4(n, v, quad(acc[r][f + NFO], j));
+            else er.store4(n, v, v);
+          }
         }
       }
     }
@@ -773,7 +809,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a0, 
   const int n_hi = min(N, n_lo + NR);
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
-  static_assert(BM <= 128, "the epilogue table holds 128 rows");
+  static_assert(BM <= 256, "the epilogue table holds 256 rows");
   __shared__ EpiTab ep_tab;
   epi_fill<EPI>(a, row0, rows, &ep_tab);
   uint16_t* const Yout = a.Y;
@@ -936,10 +972,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a0, 
     }
   };
   static_assert(MF32 >= 1 && MF32 <= 4, "row tiles per block");
-  if (mfa == MF32) run(std::integral_constant<int, MF32>{});
-  else if (MF32 > 1 && mfa == 1) run(std::integral_constant<int, 1>{});
-  else if (MF32 > 2 && mfa == 2) run(std::integral_constant<int, (MF32 > 2 ? 2 : 1)>{});
-  else run(std::integral_constant<int, (MF32 > 3 ? 3 : 1)>{});
+  with_mfa<MF32>(mfa, run);
 }
 
 namespace {
@@ -971,26 +1004,31 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 8, kEpiPlain),
     MOEQ4_GEMM_VARIANT(32, 2, true, 3, 0, 8, kEpiPlain),
     MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiPlain),
     // FFN: gate+up with SwiGLU, down scaled by the routing weight, shared down + combine
     MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiSwiglu),
     MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiSwiglu),
     MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiSwiglu),
-    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiSwiglu),
+    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiSwiglu),
     MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiScale),
     MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiScale),
     MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiScale),
-    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiScale),
+    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiScale),
     MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiTerm),
     MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiTerm),
     MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiTerm),
     MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiTerm),
+    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiSwiglu),
+    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiScale),
+    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiTerm),
     // alternatives for tuning sweeps
+    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiSwiglu),
     MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 4, kEpiPlain),
     MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 4, kEpiPlain),
     MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 8, kEpiPlain),
     MOEQ4_GEMM_VARIANT(32, 2, true, 4, 0, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiPlain),
     MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiPlain),
     MOEQ4_GEMM_W32(64, 2, 2, 8, kEpiPlain),
     MOEQ4_GEMM_W32(128, 1, 3, 8, kEpiPlain),
@@ -1000,8 +1038,11 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM_W32(64, 2, 3, 4, kEpiPlain),
     MOEQ4_GEMM_W32(64, 2, 4, 4, kEpiPlain),
     MOEQ4_GEMM_W32(64, 1, 3, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiSwiglu),
+    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiSwiglu),
     MOEQ4_GEMM_W32(128, 2, 3, 8, kEpiSwiglu),
+    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiScale),
+    MOEQ4_GEMM_W32(128, 1, 2, 4, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 1, 2, 4, kEpiSwiglu),
 };
 #undef MOEQ4_GEMM_VARIANT
 #undef MOEQ4_GEMM_W32
@@ -1033,13 +1074,14 @@ struct KresVariant {
   {"kres_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, EPI, NCH, WAVES, WAVES * NF32 * 32,           \
    (const void*)&k_gemm_q4_kres<BM, NF32, NCH, S, WAVES, EPI>}
 const KresVariant kKres[] = {
-    MOEQ4_KRES(128, 1, 4, 4, 8, kEpiScale),
     MOEQ4_KRES(64, 1, 4, 4, 8, kEpiScale),
-    MOEQ4_KRES(64, 1, 4, 4, 8, kEpiTerm),  // 128-row blocks of this epilogue: see the tall-block kernel
-    MOEQ4_KRES(128, 1, 2, 2, 8, kEpiScale),
+    MOEQ4_KRES(64, 1, 4, 4, 8, kEpiTerm),
     MOEQ4_KRES(64, 1, 2, 2, 8, kEpiScale),
     MOEQ4_KRES(64, 1, 2, 2, 8, kEpiTerm),
-    // alternatives for tuning sweeps
+    // alternatives for tuning sweeps (128-row blocks: two 4-wave tall-block
+    // workgroups per CU measured faster on MI355X)
+    MOEQ4_KRES(128, 1, 4, 4, 8, kEpiScale),
+    MOEQ4_KRES(128, 1, 2, 2, 8, kEpiScale),
     MOEQ4_KRES(128, 2, 4, 2, 8, kEpiScale),
     MOEQ4_KRES(128, 2, 4, 2, 4, kEpiScale),
     MOEQ4_KRES(64, 2, 4, 2, 8, kEpiTerm),
@@ -1052,6 +1094,7 @@ const KresVariant* pick_kres(int bm, int epi, int nch) {
   if (forced)
     for (const KresVariant& v : kKres)
       if (v.bm == bm && v.epi == epi && v.nch == nch && strcmp(v.name, forced) == 0) return &v;
+  if (bm != 64) return nullptr;  // defaults: 64-row blocks only
   for (const KresVariant& v : kKres)
     if (v.bm == bm && v.epi == epi && v.nch == nch) return &v;
   return nullptr;

@@ -55,18 +55,18 @@ class Layer:
         return out
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 def test_ffn_small(bm):
     Layer(W.custom(70, 64, 16, 2, 256, 128, ffn=True)).check(bm)
 
 
-@pytest.mark.parametrize("bm", [32, 128])
+@pytest.mark.parametrize("bm", [32, 128, 256])
 def test_ffn_odd_groups(bm):
     # H = 320 and I = 192: odd group counts in both matrices; T*k not a multiple of BM
     Layer(W.custom(71, 200, 8, 3, 320, 192, ffn=True)).check(bm)
 
 
-@pytest.mark.parametrize("bm", [16, 128])
+@pytest.mark.parametrize("bm", [16, 128, 256])
 def test_ffn_no_shared(bm):
     Layer(W.custom(72, 100, 16, 4, 256, 128, ffn=True), shared=False).check(bm)
 
@@ -89,11 +89,12 @@ def test_ffn_deterministic():
     np.testing.assert_array_equal(a, b)
 
 
-def test_ffn_workload_full_size_sampled():
+@pytest.mark.parametrize("bm", [128, 256])
+def test_ffn_workload_full_size_sampled(bm):
     # the expert-FFN workload: T=4096, 8 of 256 experts + shared, H=2048, I=512;
     # the oracle checks a sample of tokens
     w = W.WORKLOADS[3]
     L = Layer(w)
     tokens = np.random.default_rng(3).choice(w.T, size=48, replace=False).astype(np.int32)
-    out = L.check(128, tokens=np.sort(tokens))
+    out = L.check(bm, tokens=np.sort(tokens))
     assert np.isfinite(out.view(np.int16).astype(np.float32)).all()

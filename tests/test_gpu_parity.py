@@ -64,7 +64,7 @@ ROUTE_CASES = [
 
 
 @pytest.mark.parametrize("kind,T,E,k", ROUTE_CASES)
-@pytest.mark.parametrize("bm", [16, 128])
+@pytest.mark.parametrize("bm", [16, 128, 256])
 def test_route_bit_exact(kind, T, E, k, bm):
     _check_route(_logits(kind, T, E), k, bm)
 
@@ -119,12 +119,12 @@ def _gemm_full(w, bm, seed_logits=None):
     return Y, g, p
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 def test_gemm_tiny_workload(bm):
     _gemm_full(W.WORKLOADS[1], bm)
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 def test_gemm_ragged(bm):
     # N = 272 leaves a partial N tile; K = 320 is five K chunks; blocks end mid sub-tile
     _gemm_full(W.custom(31, 200, 8, 3, 320, 272), bm)
@@ -135,6 +135,7 @@ def test_gemm_ragged(bm):
     (1, 16, 2, 64, 16, 16),      # one token, minimum K and N
     (6, 4, 4, 128, 32, 128),     # k = E, T*k < BM
     (90, 3, 2, 256, 64, 32),     # few experts, many rows each
+    (300, 3, 2, 192, 80, 256),   # 256-row blocks: one full, partial ones; odd groups
 ])
 def test_gemm_edge_shapes(T, E, k, K, N, bm):
     _gemm_full(W.custom(32, T, E, k, K, N), bm)
@@ -167,8 +168,9 @@ def test_gemm_prefill_chunk_full_size():
     _sampled(W.WORKLOADS[2], 32, 96, 1)
 
 
-def test_gemm_skewed_full_size():
-    Y, g = _sampled(W.WORKLOADS[4], 128, 96, 2)
+@pytest.mark.parametrize("bm", [128, 256])
+def test_gemm_skewed_full_size(bm):
+    Y, g = _sampled(W.WORKLOADS[4], bm, 96, 2)
     assert np.isfinite(Y.view(np.int16).astype(np.float32)).all()
 
 
