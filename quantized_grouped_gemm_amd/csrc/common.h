@@ -238,25 +238,25 @@ struct GemmArgs {
   uint16_t* dY;
 };
 
-// Workgroup -> task of a launch with dense tasks (dense_tasks, first on every
-// XCD) ahead of the routed ones (routed_tasks, counted on the device).
-// Workgroup i runs on XCD i % 8; on each XCD the first ceil(dense_tasks / 8)
-// slots take the dense tasks, so they start in the first wave of workgroups
-// and spread over all XCDs.  Returns false when the workgroup has no task.
-__device__ __forceinline__ bool gemm_task(int dense_tasks, int routed_tasks, bool& dense, int& task) {
+// Workgroup -> (block, N tile) of a launch with dense_blocks dense blocks ahead
+// of the routed ones (routed_blocks, counted on the device), ntiles N tiles each.
+// Workgroup i runs on XCD i % 8.  Blocks are dealt to the XCDs round-robin
+// (block b to XCD b % 8) with all N tiles of a block on one XCD, so those
+// tiles, which gather the same activation rows, share an L2, and every XCD gets
+// a like share of full and partial blocks however skewed the experts are.  On
+// each XCD the dense blocks come first, so they start in the first wave of
+// workgroups.  Returns false when the workgroup has no task.
+__device__ __forceinline__ bool gemm_task(int dense_blocks, int routed_blocks, int ntiles, bool& dense, int& blk,
+                                          int& ntile) {
   constexpr int kX = 8;
-  const int xcd = blockIdx.x % kX, slot = blockIdx.x / kX;
-  const int dper = (dense_tasks + kX - 1) / kX;
-  if (slot < dper) {
-    dense = true;
-    task = xcd * dper + slot;
-    return task < dense_tasks;
-  }
-  dense = false;
-  const int per_xcd = (routed_tasks + kX - 1) / kX;
-  if (slot - dper >= per_xcd) return false;
-  task = xcd * per_xcd + (slot - dper);
-  return task < routed_tasks;
+  const int xcd = blockIdx.x % kX;
+  int slot = blockIdx.x / kX;
+  const int dslots = (dense_blocks + kX - 1) / kX * ntiles;
+  dense = slot < dslots;
+  if (!dense) slot -= dslots;
+  blk = slot / ntiles * kX + xcd;
+  ntile = slot % ntiles;
+  return blk < (dense ? dense_blocks : routed_blocks);
 }
 
 // the arguments of the dense problem, as a problem of its own

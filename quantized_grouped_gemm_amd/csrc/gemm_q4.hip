@@ -221,19 +221,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   constexpr int XP = (BM * (kKC / 8) + NTHR - 1) / NTHR;  // 16-B activation pieces per thread per stage
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kXRow];
 
-  // XCD-aware task order: the workgroups of one XCD take consecutive tasks
-  // (block, N tile), so the N tiles of a block -- which gather the same
-  // activation rows -- and the blocks of one expert -- which stream the same
-  // weights -- share that XCD's L2.  Tasks past the device-side block count exit.
+  // XCD-aware task order (gemm_task): the N tiles of a block, which gather the
+  // same activation rows, run on one XCD; blocks go round-robin over the XCDs.
+  // Tasks past the device-side block count exit.
   const int ntiles = (NOUT + WAVES * NFO * 16 - 1) / (WAVES * NFO * 16);
-  const int total = gemm_nblocks(a, BM) * ntiles;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int task = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (task >= total) return;
-  const int blk = task / ntiles;
-  const int ntile = task - blk * ntiles;
+  bool dense;
+  int blk, ntile;
+  if (!gemm_task(0, gemm_nblocks(a, BM), ntiles, dense, blk, ntile)) return;
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
   static_assert(BM <= 256, "the epilogue table holds 256 rows");
@@ -508,15 +502,13 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 4 ? 2 : 1) void k_gemm_q4_w32(
   const int NOUT = EPI == kEpiSwiglu ? a0.N / 2 : a0.N;
   const int ntiles = (NOUT + TILE_N - 1) / TILE_N;
   bool dense;
-  int task;
-  if (!gemm_task((a0.d_rows + BM - 1) / BM * ntiles, gemm_nblocks(a0, BM) * ntiles, dense, task)) return;
+  int blk, ntile;
+  if (!gemm_task((a0.d_rows + BM - 1) / BM, gemm_nblocks(a0, BM), ntiles, dense, blk, ntile)) return;
   const GemmArgs a = dense ? gemm_dense(a0) : a0;
   const int K = a.K, N = a.N;
   const uint8_t* __restrict__ Wt = a.Wt;
   const uint16_t* __restrict__ St = a.St;
   const uint16_t* __restrict__ Bt = a.Bt;
-  const int blk = task / ntiles;
-  const int ntile = task - blk * ntiles;
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
   static_assert(BM <= 256, "the epilogue table holds 256 rows");
@@ -800,12 +792,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a0, 
   extern __shared__ __attribute__((aligned(16))) uint16_t xk[];  // [K/128][BM][128]
   const int nsplit = (a0.N + NR - 1) / NR;
   bool dense;
-  int task;
-  if (!gemm_task((a0.d_rows + BM - 1) / BM * nsplit, gemm_nblocks(a0, BM) * nsplit, dense, task)) return;
+  int blk, split;
+  if (!gemm_task((a0.d_rows + BM - 1) / BM, gemm_nblocks(a0, BM), nsplit, dense, blk, split)) return;
   const GemmArgs a = dense ? gemm_dense(a0) : a0;
   const int K = a.K, N = a.N;
-  const int blk = task / nsplit;
-  const int n_lo = (task - blk * nsplit) * NR;
+  const int n_lo = split * NR;
   const int n_hi = min(N, n_lo + NR);
   int e, row0, rows;
   if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
@@ -1101,9 +1092,10 @@ const KresVariant* pick_kres(int bm, int epi, int nch) {
 }
 }  // namespace
 
-// grid of a launch with dense_tasks dense tasks and at most routed_tasks routed ones
-static dim3 task_grid(long long dense_tasks, long long routed_tasks) {
-  return dim3((unsigned)(((dense_tasks + kXcds - 1) / kXcds + (routed_tasks + kXcds - 1) / kXcds) * kXcds));
+// grid of a launch with dense_blocks dense blocks and at most max_blocks routed
+// ones, ntiles N tiles each (the layout gemm_task decodes)
+static dim3 task_grid(long long dense_blocks, long long max_blocks, long long ntiles) {
+  return dim3((unsigned)(((dense_blocks + kXcds - 1) / kXcds + (max_blocks + kXcds - 1) / kXcds) * ntiles * kXcds));
 }
 
 hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipStream_t stream) {
@@ -1121,7 +1113,7 @@ hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipSt
       int nsplit = max(1, min(a.N / tile_n, 512 / max(1, max_blocks)));
       const int NR = (a.N / nsplit + tile_n - 1) / tile_n * tile_n;
       nsplit = (a.N + NR - 1) / NR;
-      const dim3 grid = task_grid(dense_blocks * nsplit, (long long)max_blocks * nsplit);
+      const dim3 grid = task_grid(dense_blocks, max_blocks, nsplit);
       const size_t lds = (size_t)BM * a.K * 2;  // up to 128 KB of the 160 KB a workgroup may use
       static const void* raised[16] = {};
       bool done = false;
@@ -1145,8 +1137,7 @@ hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipSt
   if (!v || (dense_blocks > 0 && !v->dense)) return hipErrorInvalidValue;
   const int nout = epi == kEpiSwiglu ? a.N / 2 : a.N;
   const long long ntiles = (nout + v->tile_n - 1) / v->tile_n;
-  return launch("k_gemm_q4", v->fn, task_grid(dense_blocks * ntiles, max_blocks * ntiles), dim3(v->waves * 64), 0,
-                stream, a);
+  return launch("k_gemm_q4", v->fn, task_grid(dense_blocks, max_blocks, ntiles), dim3(v->waves * 64), 0, stream, a);
 }
 
 hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, const uint8_t* Wt,
