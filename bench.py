@@ -19,8 +19,10 @@ HBM rather than from the 256 MB Infinity Cache: at least 1 GiB of copies for
 the prefill workloads, and for decode enough copies that more than 256 MB of
 other weights are read between two uses of a copy.
 
-Prefill steps are replayed from HIP graphs (one per weight copy) unless
---no-graph; an eager run of the same steps gives the per-kernel event times.
+Steps are replayed from HIP graphs unless --no-graph: each graph holds a chain
+of consecutive steps, each on its own weight copy (and, for decode, its own
+fresh token), as consecutive layers run in one captured forward pass; an eager
+run of the same steps gives the per-kernel event times.
 
 Prints one JSON line: the throughput of the whole step, the roofline of the
 dominant kernel (timed with HIP events on its launch stream; HBM traffic from
@@ -112,27 +114,63 @@ class Timer:
 
 
 def graph_ms_per_step(torch, args, capture_step, layers):
-    """Whole-step wall time with every step replayed from a HIP graph (one graph
-    per resident weight copy, captured from the same library calls), so the
-    step's small kernels start back to back without host launch gaps."""
-    graphs = []
+    """Whole-step wall time with the steps replayed from HIP graphs captured
+    from the same library calls: one graph runs a chain of `layers` consecutive
+    steps (each on its own resident weight copy, as consecutive MoE layers of a
+    model run back to back in one captured forward pass), and single-step
+    graphs run the remainder, so exactly args.steps steps execute and their
+    small kernels start back to back without host launch gaps."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):       # warm the calls once outside capture
         capture_step(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    chain = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chain):
+        for l in range(layers):
+            capture_step(l)
+    singles = []
     for l in range(layers):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             capture_step(l)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % layers].replay()
+        singles.append(g)
+    for i in range(max(1, args.warmup // layers)):
+        chain.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % layers].replay()
+    for i in range(args.steps // layers):
+        chain.replay()
+    for l in range(args.steps % layers):
+        singles[l].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / args.steps
+
+
+def decode_graph_ms_per_step(torch, args, capture_step, layers):
+    """Decode steps replayed from HIP graphs: steps warmup .. warmup+steps-1 in
+    chains of `layers` consecutive steps, each captured with its own inputs and
+    weight copy (a decode pass through consecutive layers in one graph).
+    capture_step(i) launches step i on torch's current stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        capture_step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    chains = []
+    for c0 in range(args.warmup, args.warmup + args.steps, layers):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(c0, min(c0 + layers, args.warmup + args.steps)):
+                capture_step(i)
+        chains.append(g)
+    chains[0].replay()                   # warm the graph path once
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in chains:
+        g.replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / args.steps
 
@@ -196,7 +234,8 @@ def bench_gemm(args, torch, q, W, w, d):
         "route_us": float(route_all.mean()) * 1e3,
         "eager_ms_per_step": eager_ms,
         "timing": f"steps back to back, wall clock between two synchronisations" +
-                  ("" if args.no_graph else ", each step replayed from a HIP graph of its route + GEMM launches") +
+                  ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
+                   "(route + GEMM launches, one weight copy each)") +
                   f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB) so each "
                   "GEMM reads them from HBM; route and GEMM split by HIP events on the launch stream in an eager run",
         "gemm_us_p10_p90": [float(np.percentile(gemm_all, 10)) * 1e3, float(np.percentile(gemm_all, 90)) * 1e3],
@@ -282,7 +321,8 @@ def bench_ffn(args, torch, q, W, w, d):
         "route_us": float(route_all.mean()) * 1e3,
         "eager_ms_per_step": eager_ms,
         "timing": f"steps back to back, wall clock between two synchronisations" +
-                  ("" if args.no_graph else ", each step replayed from a HIP graph of its route + FFN launches") +
+                  ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
+                   "(route + FFN launches, one weight copy each)") +
                   f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB); route "
                   "and FFN split by HIP events on the launch stream in an eager run",
     })
@@ -326,8 +366,11 @@ def bench_decode(args, torch, q, W, w, d):
         if ev is not None:
             ev[1].record(stream)
 
-    ms_per_step, (dec_all,) = Timer(torch, 2).run(step, args.warmup, args.steps)
+    eager_ms, (dec_all,) = Timer(torch, 2).run(step, args.warmup, args.steps)
     dec_ms = float(dec_all.mean())
+    ms_per_step = eager_ms if args.no_graph else decode_graph_ms_per_step(
+        torch, args, lambda i: q.decode_ffn(lg[i], xs[i], k, *packs[i % layers], bufs=bufs,
+                                            stream=torch.cuda.current_stream()), layers)
     flops = ffn_flops(1, H, I, k, True)
     alg_bytes = step_bytes + H * 2 * 2 + E * 4
     out = base_line(args, w, flops / (ms_per_step * 1e-3) / 1e12, ms_per_step,
@@ -339,9 +382,12 @@ def bench_decode(args, torch, q, W, w, d):
         "decode": {"us_per_step_kernels": dec_ms * 1e3, "weight_GB/s": step_bytes / (dec_ms * 1e-3) / 1e9,
                    "weight_bytes_per_step": step_bytes,
                    "kernels": "k_decode_gateup (routing + gate/up + SwiGLU), k_decode_down (down + combine)"},
-        "timing": f"steps back to back, wall clock between two synchronisations (includes the host launch of "
-                  f"two kernels per step); weights rotate over {layers} resident copies so more than 256 MB "
-                  "of other weights are read between two uses of a copy; kernel time by HIP events",
+        "timing": f"steps back to back, wall clock between two synchronisations" +
+                  ("" if args.no_graph else f", replayed from HIP graphs each holding {layers} consecutive steps "
+                   "(every step its own fresh logits and activations and its own weight copy)") +
+                  f"; weights rotate over {layers} resident copies so more than 256 MB "
+                  "of other weights are read between two uses of a copy; kernel time by HIP events in an eager run",
+        "eager_ms_per_step": eager_ms,
         "p10_p90_us": [float(np.percentile(dec_all, 10)) * 1e3, float(np.percentile(dec_all, 90)) * 1e3],
     })
     if not args.no_cpu_baseline:
@@ -365,7 +411,7 @@ def bench_decode(args, torch, q, W, w, d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 1000 for decode)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--block-rows", type=int, default=0)
@@ -386,6 +432,8 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.steps is None:
+        args.steps = 1000 if (w.ffn and w.T == 1) else 50   # decode: the workload's 1000 fresh tokens
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
