@@ -478,8 +478,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
 // K indices 32h + [0,32) in each of the chunk's two groups.  K-step s4 of group
 // g then takes K indices g*64 + 32h + 8*s4 + [0,8) from lane half h, for both
 // operands, so every K-step stays inside one scale group.
-template <int BM, int NF32, int S, int WAVES, int EPI>
-__global__ __launch_bounds__(WAVES * 64, WAVES == 4 ? 2 : 1) void k_gemm_q4_w32(const GemmArgs a0) {
+// OCC: workgroups per CU the kernel is sized for (registers and LDS)
+template <int BM, int NF32, int S, int WAVES, int EPI, int OCC>
+__global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs a0) {
   constexpr bool PAIRED = EPI == kEpiSwiglu && NF32 == 1;  // gate and up in one tile
   static_assert(EPI != kEpiSwiglu || NF32 % 2 == 0 || PAIRED, "SwiGLU pairs gate and up fragments");
   constexpr int MF32 = BM / 32;
@@ -487,10 +488,10 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 4 ? 2 : 1) void k_gemm_q4_w32(
   constexpr int NFO = EPI == kEpiSwiglu && !PAIRED ? NF32 / 2 : NF32;  // output fragments per wave
   constexpr int OUTF = PAIRED ? 16 : 32;                                // output columns per fragment
   constexpr int TILE_N = WAVES * NFO * OUTF;                            // output columns per workgroup
-  // activation buffers in LDS: three (the DMA runs two chunks ahead) for 8-wave
-  // workgroups of up to 128 rows; two where that would not fit or where two
-  // 4-wave workgroups should share a CU (2 x 64 KB for 128 rows)
-  constexpr int NBUF = BM <= 128 && WAVES >= 8 ? 3 : 2;
+  // activation buffers in LDS: three (the DMA runs two chunks ahead) for one
+  // workgroup per CU of up to 128 rows; two where that would not fit or where
+  // two workgroups share a CU (2 x 66 KB for 128 rows)
+  constexpr int NBUF = BM <= 128 && OCC == 1 ? 3 : 2;
   // Activations reach LDS by DMA (buffer_load ... lds): each wave instruction
   // fills 1 KB = 4 rows of 256 B.  In row r, 16-byte slot s holds the row's
   // 16-byte column s ^ (r & 15), so that the 32 rows an MFMA operand read
@@ -984,7 +985,7 @@ struct GemmVariant {
    false}
 #define MOEQ4_GEMM_W32(BM, NF32, S, WAVES, EPI)                                                  \
   {"w32_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, EPI, WAVES * NF32 * 32 / (EPI == kEpiSwiglu ? 2 : 1), \
-   WAVES, (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES, EPI>, true}
+   WAVES, (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES, EPI, (WAVES == 4 ? 2 : 1)>, true}
 
 // The first entry of each (block height, epilogue) is its default, from sweeps
 // on MI355X.  WAUX is the cache policy of the weight loads.  The single
