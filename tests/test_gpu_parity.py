@@ -86,6 +86,23 @@ def test_route_workloads(cid):
         assert c.max() > 10 * c.mean() and (c < 2).mean() > 0.1
 
 
+def test_route_repeated_calls_reuse_workspace():
+    # one set of buffers serves call after call (different inputs, same buffers)
+    T, E, k, bm = 700, 64, 4, 32
+    b = q.alloc_route(T, E, k, bm)
+    for s in range(4):
+        lg = _logits("normal", T, E, seed=s)
+        d = torch.from_numpy(lg).cuda()
+        q.route(d, k, bufs=b)
+        torch.cuda.synchronize()
+        ids, _ = oracle.topk_softmax(lg, k)
+        ref = oracle.route(ids, E, bm)
+        np.testing.assert_array_equal(b["perm"].cpu().numpy(), ref["perm"])
+        nb = int(b["num_blocks"][0])
+        assert nb == ref["num_blocks"]
+        np.testing.assert_array_equal(b["blocks"].cpu().numpy().reshape(-1, 4)[:nb], ref["blocks"])
+
+
 def test_route_decode_steps():
     w = W.WORKLOADS[5]
     for s in range(20):
