@@ -73,6 +73,44 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
+_CEILINGS = None
+
+
+def measured_ceilings(torch, q) -> dict:
+    """What this GPU sustains, measured here beside the published peaks: a 1 GiB
+    device-to-device copy (HBM read + write) and the library's MFMA-only loop
+    (independent 32x32x16 bf16 MFMAs on every SIMD)."""
+    global _CEILINGS
+    if _CEILINGS is not None:
+        return _CEILINGS
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    wgs, iters = 256 * 8, 2000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    q.moe_calibrate_mfma(wgs, 10, out)
+    torch.cuda.synchronize()
+    e0.record()
+    q.moe_calibrate_mfma(wgs, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tflops = wgs * 4 * iters * 8 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    _CEILINGS = {"hbm_copy_GBps": copy_gbps, "mfma_bf16_TFLOPs": mfma_tflops,
+                 "how": "1 GiB device copy (read + write bytes / time, torch copy kernel); "
+                        "moe_calibrate_mfma: 2048 workgroups x 4 waves of independent 32x32x16 bf16 MFMAs"}
+    return _CEILINGS
+
+
 def roofline(flops: float, alg_bytes: float, kernel_ms: float, kernel: str, workload: str) -> dict:
     gbps = alg_bytes / (kernel_ms * 1e-3) / 1e9
     tflops = flops / (kernel_ms * 1e-3) / 1e12
@@ -84,6 +122,10 @@ def roofline(flops: float, alg_bytes: float, kernel_ms: float, kernel: str, work
         roof = {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / BF16_PEAK_TFLOPS}
     roof["traffic"] = load_traffic(kernel, workload)
+    if _CEILINGS is not None:
+        ceil = _CEILINGS["hbm_copy_GBps"] if roof["bound"] == "hbm" else _CEILINGS["mfma_bf16_TFLOPs"]
+        roof["measured_ceiling"] = ceil
+        roof["frac_of_measured_ceiling"] = roof["achieved"] / ceil
     roof["kernel"] = kernel
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["algorithmic_flops_per_launch"] = flops
@@ -443,12 +485,14 @@ def main():
             a = a.view(np.int16)
         return torch.from_numpy(a).to(dev)
 
+    ceilings = measured_ceilings(torch, q)
     if w.ffn and w.T == 1:
         out = bench_decode(args, torch, q, W, w, d)
     elif w.ffn:
         out = bench_ffn(args, torch, q, W, w, d)
     else:
         out = bench_gemm(args, torch, q, W, w, d)
+    out["measured_ceilings"] = ceilings
     print(json.dumps(out), flush=True)
 
 

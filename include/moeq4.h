@@ -269,6 +269,16 @@ int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int 
                       int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
                       size_t ws_bytes, void* stream);
 
+/* Measured MFMA ceiling (measurement only, not a step of the method): each of
+ * `workgroups` workgroups of 4 waves issues iters x 8 independent
+ * v_mfma_f32_32x32x16_bf16 per wave (32768 flops each), the instruction of the
+ * tall-block grouped GEMM, so flops / kernel time is the matrix-core
+ * throughput that kernel can reach on this GPU at its clock.
+ *   out  float [workgroups * 256], device, 16-byte aligned (results, unused).
+ * Errors: MOEQ4_ERR_NULL, MOEQ4_ERR_SHAPE (workgroups < 1 or > 2^20,
+ * iters < 0), MOEQ4_ERR_ALIGN, MOEQ4_ERR_HIP. */
+int moe_calibrate_mfma(int workgroups, int iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

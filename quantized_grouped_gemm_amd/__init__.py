@@ -48,6 +48,7 @@ SIGNATURES = {
                                                                        _vp]),
     "moe_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_decode_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_calibrate_mfma": (_i, [_i, _i, _vp, _vp]),
 }
 
 
@@ -172,6 +173,10 @@ def moe_decode_ffn_q4(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_
         _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
         _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), _p(topk_ids), _p(topk_w), _p(out),
         _p(workspace), int(ws_bytes), _stream(stream)))
+
+
+def moe_calibrate_mfma(workgroups, iters, out, stream=None):
+    _ok("moe_calibrate_mfma", lib().moe_calibrate_mfma(int(workgroups), int(iters), _p(out), _stream(stream)))
 
 
 # ---------------------------------------------------------------- plumbing --

@@ -252,4 +252,12 @@ int moe_expert_ffn_q4(const uint16_t* X, int T, int H, int I, int E, int k, cons
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 
+int moe_calibrate_mfma(int workgroups, int iters, float* out, void* stream) {
+  if (!out) return MOEQ4_ERR_NULL;
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 0) return MOEQ4_ERR_SHAPE;
+  if (!aligned16(out)) return MOEQ4_ERR_ALIGN;
+  return moeq4::calib_mfma_launch(workgroups, iters, out, (hipStream_t)stream) == hipSuccess ? MOEQ4_OK
+                                                                                            : MOEQ4_ERR_HIP;
+}
+
 }  // extern "C"

@@ -287,6 +287,10 @@ hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, 
                           const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
                           int block_rows, uint16_t* Y, hipStream_t stream);
 
+// measured MFMA ceiling (calib.hip): workgroups x 4 waves, each issuing
+// iters x 8 independent 32x32x16 bf16 MFMAs; out holds workgroups * 256 floats
+hipError_t calib_mfma_launch(int workgroups, int iters, float* out, hipStream_t stream);
+
 struct DecodePlan {
   int J;               // experts per step: k routed + the shared one if given
   size_t ws_ids, ws_w, ws_h, ws_bytes;  // workspace byte offsets / total

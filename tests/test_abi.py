@@ -174,3 +174,11 @@ def test_ffn_validation():
     assert _ffn(out=FAKE + 2) == q.MOEQ4_ERR_ALIGN
     assert _ffn(ws_bytes=64) == q.MOEQ4_ERR_WORKSPACE
     assert _ffn(T=0, X=None, out=None) == q.MOEQ4_OK                         # nothing to do: no launch
+
+
+def test_calibrate_mfma_validation():
+    L = q.lib()
+    assert L.moe_calibrate_mfma(8, 10, None, None) == q.MOEQ4_ERR_NULL
+    assert L.moe_calibrate_mfma(0, 10, FAKE, None) == q.MOEQ4_ERR_SHAPE
+    assert L.moe_calibrate_mfma(8, -1, FAKE, None) == q.MOEQ4_ERR_SHAPE
+    assert L.moe_calibrate_mfma(8, 10, FAKE + 4, None) == q.MOEQ4_ERR_ALIGN
