@@ -144,6 +144,19 @@ int moe_prepack_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t*
                    int N, int K, uint8_t* codes_t, uint16_t* scales_t, uint16_t* biases_t,
                    void* stream);
 
+/* Dequantization into memory: every weight of E tiled matrices rebuilt as
+ * bf16(scale*code + bias) (same rounding as the grouped GEMM's rebuild) into a
+ * row-major bf16 array.  This is the unfused path that section "Dequantize
+ * weights during matrix multiplication" compares the in-GEMM rebuild against
+ * (a separate pass that writes the expanded weights to memory); it exists for
+ * that comparison and for inspection, not on the fused path.
+ * In:  codes_t, scales_t, biases_t  [E, N, K] in the tiled layout of moe_prepack_q4.
+ * Out: out  uint16 (bf16) [E, N, K], 16-byte aligned; E*N*K*2 bytes.
+ * Sizes: as moe_prepack_q4.  Errors: MOEQ4_ERR_SHAPE, MOEQ4_ERR_NULL,
+ * MOEQ4_ERR_ALIGN, MOEQ4_ERR_HIP. */
+int moe_dequant_q4(const uint8_t* codes_t, const uint16_t* scales_t, const uint16_t* biases_t, int E,
+                   int N, int K, uint16_t* out, void* stream);
+
 /* Grouped GEMM over group-wise affine 4-bit expert weights (section
  * "Dequantize weights during matrix multiplication").
  *

@@ -49,6 +49,7 @@ SIGNATURES = {
     "moe_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_decode_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_calibrate_mfma": (_i, [_i, _i, _vp, _vp]),
+    "moe_dequant_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
 }
 
 
@@ -173,6 +174,20 @@ def moe_decode_ffn_q4(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_
         _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
         _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), _p(topk_ids), _p(topk_w), _p(out),
         _p(workspace), int(ws_bytes), _stream(stream)))
+
+
+def moe_dequant_q4(codes_t, scales_t, biases_t, E, N, K, out, stream=None):
+    _ok("moe_dequant_q4", lib().moe_dequant_q4(_p(codes_t), _p(scales_t), _p(biases_t), E, N, K, _p(out),
+                                               _stream(stream)))
+
+
+def dequant(packed, E: int, N: int, K: int, out=None, stream=None):
+    """Every weight rebuilt as bf16 into a [E, N, K] int16 (bf16 bits) device tensor."""
+    ct, st, bt = packed
+    if out is None:
+        out = torch.empty((E, N, K), dtype=torch.int16, device=ct.device)
+    moe_dequant_q4(ct, st, bt, E, N, K, out, stream)
+    return out
 
 
 def moe_calibrate_mfma(workgroups, iters, out, stream=None):

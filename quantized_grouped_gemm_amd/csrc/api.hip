@@ -118,6 +118,19 @@ int moe_prepack_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t*
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 
+int moe_dequant_q4(const uint8_t* codes_t, const uint16_t* scales_t, const uint16_t* biases_t, int E, int N,
+                   int K, uint16_t* out, void* stream) {
+  if (E < 1 || N < 16 || N % 16 != 0 || K < 64 || K % 64 != 0) return MOEQ4_ERR_SHAPE;
+  if ((long long)E * N * (K / 2) >= (1LL << 31)) return MOEQ4_ERR_SHAPE;
+  if (!codes_t || !scales_t || !biases_t || !out) return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {codes_t, scales_t, biases_t, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOEQ4_ERR_ALIGN;
+  return moeq4::dequant_launch(codes_t, scales_t, biases_t, E, N, K, out, (hipStream_t)stream) == hipSuccess
+             ? MOEQ4_OK
+             : MOEQ4_ERR_HIP;
+}
+
 int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
                         const uint8_t* codes_t, const uint16_t* scales_t,
                         const uint16_t* biases_t, const int32_t* perm, const int32_t* blocks,

@@ -287,6 +287,10 @@ hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, 
                           const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
                           int block_rows, uint16_t* Y, hipStream_t stream);
 
+// prepack.hip: every weight rebuilt exactly into row-major bf16 [E][N][K]
+hipError_t dequant_launch(const uint8_t* codes_t, const uint16_t* scales_t, const uint16_t* biases_t, int E, int N,
+                          int K, uint16_t* out, hipStream_t stream);
+
 // measured MFMA ceiling (calib.hip): workgroups x 4 waves, each issuing
 // iters x 8 independent 32x32x16 bf16 MFMAs; out holds workgroups * 256 floats
 hipError_t calib_mfma_launch(int workgroups, int iters, float* out, hipStream_t stream);

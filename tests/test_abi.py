@@ -182,3 +182,13 @@ def test_calibrate_mfma_validation():
     assert L.moe_calibrate_mfma(0, 10, FAKE, None) == q.MOEQ4_ERR_SHAPE
     assert L.moe_calibrate_mfma(8, -1, FAKE, None) == q.MOEQ4_ERR_SHAPE
     assert L.moe_calibrate_mfma(8, 10, FAKE + 4, None) == q.MOEQ4_ERR_ALIGN
+
+
+def test_dequant_validation():
+    L = q.lib()
+    assert L.moe_dequant_q4(FAKE, FAKE, FAKE, 0, 32, 128, FAKE, None) == q.MOEQ4_ERR_SHAPE
+    assert L.moe_dequant_q4(FAKE, FAKE, FAKE, 2, 24, 128, FAKE, None) == q.MOEQ4_ERR_SHAPE
+    assert L.moe_dequant_q4(FAKE, FAKE, FAKE, 2, 32, 96, FAKE, None) == q.MOEQ4_ERR_SHAPE
+    assert L.moe_dequant_q4(None, FAKE, FAKE, 2, 32, 128, FAKE, None) == q.MOEQ4_ERR_NULL
+    assert L.moe_dequant_q4(FAKE, FAKE, FAKE, 2, 32, 128, None, None) == q.MOEQ4_ERR_NULL
+    assert L.moe_dequant_q4(FAKE, FAKE, FAKE, 2, 32, 128, FAKE + 2, None) == q.MOEQ4_ERR_ALIGN

@@ -123,6 +123,35 @@ def test_prepack_layout_bit_exact(E, N, K):
     np.testing.assert_array_equal(host(bt, np.uint16), rb)
 
 
+# ---------------------------------------------------------------- dequant --
+
+def _bf16_bits(w64):
+    """bf16 bit patterns of float64 values that are bf16 numbers."""
+    return (w64.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 32, 256), (2, 48, 192), (1, 16, 64), (4, 64, 320)])
+def test_dequant_bit_exact(E, N, K):
+    # every weight rebuilt into memory equals the oracle's bf16(scale*code + bias)
+    w = W.custom(41, 1, E, 1, K, N)
+    p = W.make_problem(w)
+    out = q.dequant(q.prepack(dev(p.Wq), dev(p.S), dev(p.B)), E, N, K)
+    torch.cuda.synchronize()
+    got = host(out, np.uint16)
+    for e in range(E):
+        np.testing.assert_array_equal(got[e], _bf16_bits(oracle.dequant_q4(p.Wq[e], p.S[e], p.B[e])))
+
+
+def test_dequant_prefill_weights_sampled():
+    # the 256-expert [512 x 2048] weights of the prefill workload, three experts checked in full
+    w = W.WORKLOADS[2]
+    p = W.make_problem(w)
+    out = q.dequant(q.prepack(dev(p.Wq), dev(p.S), dev(p.B)), w.E, w.N, w.K)
+    torch.cuda.synchronize()
+    for e in (0, 127, 255):
+        np.testing.assert_array_equal(host(out[e], np.uint16), _bf16_bits(oracle.dequant_q4(p.Wq[e], p.S[e], p.B[e])))
+
+
 # ----------------------------------------------------------- grouped GEMM --
 
 def _gemm_full(w, bm, seed_logits=None):
