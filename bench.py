@@ -384,6 +384,120 @@ def bench_ffn(args, torch, q, W, w, d):
     return out
 
 
+# ------------------------------------------------------------------ ablations
+def bench_ablation(args, torch, q, W, T, d):
+    """The pages' two prefill mechanisms, each against its unfused alternative,
+    on the single-projection shape (E=256, k=8, K=2048, N=512) at T tokens:
+      fused     moe_route + moe_grouped_gemm_q4 (the product path);
+      unfused   moe_route + moe_dequant_q4 (every weight rebuilt as bf16 into
+                HBM) + a bf16 grouped GEMM on the expanded weights: the vendor
+                batched GEMM (torch.bmm -> hipBLASLt) over per-expert padded
+                rows, gathered through perm; its HBM floor is printed beside it;
+      hostsync  moe_route, then the expert counts copied to the host, the block
+                map built there and copied back before moe_grouped_gemm_q4
+                (the CPU round trip the GPU-resident routing removes).
+    Every variant runs the same seeded inputs and a fresh weight copy per step."""
+    w = W.custom(2, T, 256, 8, 2048, 512)
+    p = W.make_problem(w)
+    E, k, K, N = w.E, w.k, w.K, w.N
+    w_layer = E * q4_bytes(N, K)
+    layers = args.layers or max(2, -(-(1 << 30) // w_layer))
+    packed0 = q.prepack(d(p.Wq), d(p.S), d(p.B))
+    packs = [packed0] + [tuple(t.clone() for t in packed0) for _ in range(layers - 1)]
+    logits, X = d(p.logits), d(p.X)
+    rt = q.alloc_route(T, E, k, args.block_rows, device=X.device)
+    Y = torch.empty((T * k, N), dtype=torch.int16, device=X.device)
+    stream = torch.cuda.current_stream()
+    # the routing is the same every step (same logits): the padded layout of the
+    # unfused GEMM is taken from it once, outside the timed region
+    q.route(logits, k, bufs=rt, stream=stream)
+    torch.cuda.synchronize()
+    counts = rt["counts"].cpu().numpy()
+    offsets = rt["offsets"].cpu().numpy()
+    perm = rt["perm"].cpu().numpy()
+    mmax = int(counts.max())
+    mpad = max(16, -(-mmax // 16) * 16)
+    src_row = np.full((E, mpad), T, np.int64)   # row T of Xz is zeros
+    for e in range(E):
+        c = int(counts[e])
+        src_row[e, :c] = perm[offsets[e]: offsets[e] + c] // k
+    src_row = torch.from_numpy(src_row).to(X.device)
+    Xz = torch.cat([X.view(torch.bfloat16), torch.zeros((1, K), dtype=torch.bfloat16, device=X.device)])
+    Wbf = torch.empty((E, N, K), dtype=torch.int16, device=X.device)
+    blocks_host = torch.empty(rt["blocks"].numel(), dtype=torch.int32).pin_memory()
+    nb_host = torch.empty(4, dtype=torch.int32).pin_memory()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(step_fn, n):
+        for i in range(args.warmup):
+            step_fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step_fn(args.warmup + i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    def fused(i):
+        q.route(logits, k, bufs=rt, stream=stream)
+        q.grouped_gemm_q4(X, k, packs[i % layers], rt, Y=Y, stream=stream)
+
+    def unfused(i):
+        q.route(logits, k, bufs=rt, stream=stream)
+        q.dequant(packs[i % layers], E, N, K, out=Wbf, stream=stream)
+        xt = Xz[src_row].transpose(1, 2).contiguous()            # [E, K, mpad], right operand contiguous
+        torch.bmm(Wbf.view(torch.bfloat16), xt)                  # [E, N, mpad]
+
+    def hostsync(i):
+        q.route(logits, k, bufs=rt, stream=stream)
+        cnt = rt["counts"].cpu().numpy().astype(np.int64)       # the CPU wait
+        bm = rt["block_rows"]
+        nbe = (cnt + bm - 1) // bm
+        offs = np.concatenate([[0], np.cumsum(cnt)])
+        e_of = np.repeat(np.arange(E), nbe)
+        j = np.arange(int(nbe.sum())) - np.repeat(np.cumsum(nbe) - nbe, nbe)
+        blk = np.stack([e_of, offs[e_of] + j * bm, np.minimum(bm, cnt[e_of] - j * bm), j], 1)
+        blk = blk.astype(np.int32).reshape(-1)
+        blocks_host[: blk.size] = torch.from_numpy(blk)
+        nb_host[0] = int(nbe.sum())
+        rt["blocks"][: blk.size].copy_(blocks_host[: blk.size], non_blocking=True)
+        rt["num_blocks"][:1].copy_(nb_host[:1], non_blocking=True)
+        q.grouped_gemm_q4(X, k, packs[i % layers], rt, Y=Y, stream=stream)
+
+    steps = args.steps
+    res = {"fused_us": timed(fused, steps) * 1e3, "unfused_us": timed(unfused, steps) * 1e3,
+           "hostsync_us": timed(hostsync, steps) * 1e3}
+    # kernel-level split of the unfused path (events around the dequant and the GEMM)
+    e3 = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    dq, gm = [], []
+    for i in range(10):
+        q.route(logits, k, bufs=rt, stream=stream)
+        e3[0].record()
+        q.dequant(packs[i % layers], E, N, K, out=Wbf, stream=stream)
+        e3[1].record()
+        torch.bmm(Wbf.view(torch.bfloat16), Xz[src_row].transpose(1, 2).contiguous())
+        e3[2].record()
+        torch.cuda.synchronize()
+        dq.append(e3[0].elapsed_time(e3[1]))
+        gm.append(e3[0].elapsed_time(e3[2]) - e3[0].elapsed_time(e3[1]))
+    bf16_bytes = E * N * K * 2
+    res.update({
+        "unfused_dequant_kernel_us": float(np.median(dq)) * 1e3,
+        "unfused_gemm_us": float(np.median(gm)) * 1e3,
+        "unfused_hbm_floor_us": (w_layer + 2 * bf16_bytes) / 5.1e12 * 1e6,
+        "speedup_fused_vs_unfused": res["unfused_us"] / res["fused_us"],
+        "speedup_gpu_routing_vs_hostsync": res["hostsync_us"] / res["fused_us"],
+    })
+    return {"ablation": "in-GEMM dequant and GPU-resident routing vs their unfused alternatives", "T": T,
+            "config": {"workload": w.name, "E": E, "top_k": k, "K": K, "N": N, "block_rows": rt["block_rows"],
+                       "rows_per_expert_max": mmax},
+            "steps": steps, "warmup": args.warmup, "weight_copies": layers, "results_us": res,
+            "notes": "unfused GEMM = torch.bmm (hipBLASLt) over per-expert rows padded to a multiple of 16, "
+                     "activations gathered through perm; unfused_hbm_floor_us = (q4 read + bf16 write + bf16 read) "
+                     "at 5.1 TB/s (the measured copy rate); hostsync = D2H of the counts (synchronizing), block map "
+                     "on the host, H2D of the map, then the same grouped GEMM"}
+
+
 # --------------------------------------------------------------------- decode
 def bench_decode(args, torch, q, W, w, d):
     p = W.make_problem(w)
@@ -460,6 +574,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="resident weight copies used in turn (0: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
+    ap.add_argument("--ablation", type=int, default=0,
+                    help="T: run the fused / unfused-dequant / host-synced-routing comparison at T tokens instead")
     ap.add_argument("--cpu-reps", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="stop repeating the CPU oracle once this much time is spent (at least one run)")
@@ -485,6 +601,9 @@ def main():
             a = a.view(np.int16)
         return torch.from_numpy(a).to(dev)
 
+    if args.ablation:
+        print(json.dumps(bench_ablation(args, torch, q, W, args.ablation, d)), flush=True)
+        return
     ceilings = measured_ceilings(torch, q)
     if w.ffn and w.T == 1:
         out = bench_decode(args, torch, q, W, w, d)

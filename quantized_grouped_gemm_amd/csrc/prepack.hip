@@ -6,6 +6,8 @@
 
 namespace moeq4 {
 
+constexpr int kKCodes = 128;  // K values per chunk of the tiled layout
+
 // Row-major bytes hold codes (2i, 2i+1) in (low, high) nibble of byte i.  The
 // tiled dword of 8 codes c0..c7 holds c0,c2,c4,c6,c1,c3,c5,c7 in nibbles 0..7.
 __device__ __forceinline__ uint32_t tile_nibbles(uint32_t x) {
@@ -87,50 +89,68 @@ hipError_t prepack_launch(const uint8_t* codes, const uint16_t* scales, const ui
 // ----------------------------------------------------------------------------
 // Dequantization into memory (moe_dequant_q4): every weight rebuilt exactly as
 // bf16(scale*code + bias) from the tiled layout into a row-major bf16 [E][N][K]
-// array.  One thread per (expert, chunk, 16-row tile, lane): the lane's 16 (or,
-// in the half-size last chunk, 8) code bytes become 32 (16) bf16 weights of one
-// row, written as 16-byte stores.
-__global__ __launch_bounds__(256) void k_dequant_q4(const uint8_t* __restrict__ codes_t,
-                                                    const uint16_t* __restrict__ scales_t,
-                                                    const uint16_t* __restrict__ biases_t, int E, int N, int K,
-                                                    uint16_t* __restrict__ out) {
+// array.  One 256-thread workgroup per (expert, 16-row tile, span of up to
+// kDqChunks chunks = 512 K values): its code blocks are read whole (1 KB per
+// chunk, coalesced), rebuilt into LDS as 16 rows of the span, and written out
+// row by row, so every store instruction writes contiguous row memory.
+constexpr int kDqChunks = 4;
+constexpr int kDqThreads = 256;
+
+__global__ __launch_bounds__(kDqThreads) void k_dequant_q4(const uint8_t* __restrict__ codes_t,
+                                                           const uint16_t* __restrict__ scales_t,
+                                                           const uint16_t* __restrict__ biases_t, int E, int N,
+                                                           int K, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile_s[16][kDqChunks * kKCodes];
   const int G = K / kGroup, C = (G + 1) / 2, NT = N / 16;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)E * C * NT * 64) return;
-  const int l = (int)(idx & 63);
-  const int t = (int)((idx >> 6) % NT);
-  const int c = (int)((idx >> 6) / NT % C);
-  const long long e = (idx >> 6) / NT / C;
-  const int r = l & 15, q = l >> 4;
-  const int n = 16 * t + r;
-  const uint8_t* cq = codes_t + e * (long long)N * (K / 2) + (long long)c * NT * 1024;
+  const int spans = (C + kDqChunks - 1) / kDqChunks;
+  const long long wg = blockIdx.x;
+  const int sp = (int)(wg % spans);
+  const int t = (int)(wg / spans % NT);
+  const long long e = wg / spans / NT;
+  const int c0 = sp * kDqChunks, c1 = min(C, c0 + kDqChunks);
+  const uint8_t* cq = codes_t + e * (long long)N * (K / 2);
   const uint16_t* sq = scales_t + e * (long long)N * G;
   const uint16_t* bq = biases_t + e * (long long)N * G;
-  uint16_t* row = out + (e * N + n) * (long long)K + 128 * c + 16 * q;
-  auto put16 = [&](uint16_t* dst, uint2 w, uint16_t sb, uint16_t bb) {
-    const float sv = bf16_bits_to_f32(sb), bv = bf16_bits_to_f32(bb);
-    *(uint4*)dst = rebuild_words(w.x, sv, bv);        // K +0..7
-    *(uint4*)(dst + 8) = rebuild_words(w.y, sv, bv);  // K +8..15
-  };
-  if (2 * c + 1 < G) {
-    const uint4 w = *(const uint4*)(cq + (long long)t * 1024 + 16 * l);
-    const long long g = ((long long)c * NT + t) * 32 + 2 * r;
-    put16(row, make_uint2(w.x, w.y), sq[g], bq[g]);
-    put16(row + 64, make_uint2(w.z, w.w), sq[g + 1], bq[g + 1]);
-  } else {
-    const uint2 w = *(const uint2*)(cq + (long long)t * 512 + 8 * l);
-    const long long g = (long long)c * NT * 32 + 16 * t + r;
-    put16(row, w, sq[g], bq[g]);
+  // rebuild: thread (chunk slot cs = tid / 64, lane l = tid % 64) takes lane l of chunk c0 + cs
+  {
+    const int cs = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+    const int c = c0 + cs;
+    if (c < c1) {
+      uint16_t* dst = &tile_s[r][cs * kKCodes + 16 * q];
+      auto put16 = [&](uint16_t* d, uint2 w, uint16_t sb, uint16_t bb) {
+        const float sv = bf16_bits_to_f32(sb), bv = bf16_bits_to_f32(bb);
+        *(uint4*)d = rebuild_words(w.x, sv, bv);        // K +0..7
+        *(uint4*)(d + 8) = rebuild_words(w.y, sv, bv);  // K +8..15
+      };
+      if (2 * c + 1 < G) {
+        const uint4 w = *(const uint4*)(cq + ((long long)c * NT + t) * 1024 + 16 * l);
+        const long long g = ((long long)c * NT + t) * 32 + 2 * r;
+        put16(dst, make_uint2(w.x, w.y), sq[g], bq[g]);
+        put16(dst + 64, make_uint2(w.z, w.w), sq[g + 1], bq[g + 1]);
+      } else {
+        const uint2 w = *(const uint2*)(cq + (long long)c * NT * 1024 + (long long)t * 512 + 8 * l);
+        const long long g = (long long)c * NT * 32 + 16 * t + r;
+        put16(dst, w, sq[g], bq[g]);
+      }
+    }
+  }
+  __syncthreads();
+  // write: the span's K range of the 16 rows, 16 bytes per thread per step
+  const int k_lo = 128 * c0, k_hi = min(K, 128 * c1);
+  const int pieces = (k_hi - k_lo) / 8;  // 16-byte pieces per row
+  for (int i = threadIdx.x; i < 16 * pieces; i += kDqThreads) {
+    const int r = i / pieces, pc = i % pieces;
+    *(uint4*)(out + (e * N + 16 * t + r) * (long long)K + k_lo + 8 * pc) = *(const uint4*)&tile_s[r][8 * pc];
   }
 }
 
 hipError_t dequant_launch(const uint8_t* codes_t, const uint16_t* scales_t, const uint16_t* biases_t, int E, int N,
                           int K, uint16_t* out, hipStream_t stream) {
   const int G = K / kGroup, C = (G + 1) / 2;
-  const long long threads = (long long)E * C * (N / 16) * 64;
-  if (threads == 0) return hipSuccess;
-  return launch("k_dequant_q4", (const void*)&k_dequant_q4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                stream, codes_t, scales_t, biases_t, E, N, K, out);
+  const long long wgs = (long long)E * (N / 16) * ((C + kDqChunks - 1) / kDqChunks);
+  if (wgs == 0) return hipSuccess;
+  return launch("k_dequant_q4", (const void*)&k_dequant_q4, dim3((unsigned)wgs), dim3(kDqThreads), 0, stream,
+                codes_t, scales_t, biases_t, E, N, K, out);
 }
 
 }  // namespace moeq4
