@@ -384,6 +384,68 @@ def bench_ffn(args, torch, q, W, w, d):
     return out
 
 
+# ------------------------------------------------------------- few-row groups
+def bench_crossover(args, torch, q, W, d):
+    """Groups of T = 1..8 rows at the decode shapes (top-8 of 256 + shared
+    expert, H=2048, I=512), fresh rows every step, as a speculative
+    verification step hands the layer: the few-token path
+    (moe_small_batch_ffn_q4), the prefill path (moe_route + moe_expert_ffn_q4)
+    and, at T=1, the decode step.  Microseconds per step from HIP graph replays;
+    weights rotate over resident copies as in the decode benchmark."""
+    w = W.WORKLOADS[5]
+    p = W.make_problem(w)
+    E, k, H, I = w.E, w.k, w.K, w.N
+    expert_bytes = q4_bytes(2 * I, H) + q4_bytes(H, I)
+    layers = args.layers or max(2, -(-(384 << 20) // ((k + 1) * expert_bytes)))
+    pk0 = pack_ffn(q, d, p)
+    packs = [pk0] + [clone_pack(pk0) for _ in range(layers - 1)]
+    nst = args.warmup + args.steps
+    rows = []
+    sizes = [int(v) for v in args.crossover_rows.split(",")] if args.crossover_rows else \
+        list(range(1, q.MOEQ4_SMALL_MAX_T + 1))
+    for T in sizes:
+        lg = d(np.stack([W.gen_logits(w.cid, T, E, 1000 * T + s) for s in range(nst)]))
+        xs = d(np.stack([W.gen_acts(w.cid, T, H, 1000 * T + s) for s in range(nst)]))
+        sb = q.alloc_small(T, E, k, H, I, True, device=xs.device)
+        rt = q.alloc_route(T, E, k, 0, device=xs.device)
+        fb = q.alloc_ffn(T, H, I, E, k, True, device=xs.device)
+
+        def small_step(i):
+            q.small_batch_ffn(lg[i], xs[i], k, *packs[i % layers], bufs=sb, stream=torch.cuda.current_stream())
+
+        def prefill_step(i):
+            s = torch.cuda.current_stream()
+            q.route(lg[i], k, bufs=rt, stream=s)
+            q.expert_ffn(xs[i], k, rt, *packs[i % layers], bufs=fb, stream=s)
+
+        # distinct experts per step, from the few-token path's own routing output
+        distinct = []
+        for i in range(min(nst, 32)):
+            small_step(i)
+            distinct.append(len(np.unique(sb["topk_ids"].cpu().numpy())))
+        u = float(np.mean(distinct))
+        row = {"T": T, "distinct_experts_mean": u}
+        row["small_us"] = decode_graph_ms_per_step(torch, args, small_step, layers) * 1e3
+        row["prefill_path_us"] = decode_graph_ms_per_step(torch, args, prefill_step, layers) * 1e3
+        if T == 1:
+            db = q.alloc_decode(E, k, H, I, True, device=xs.device)
+            row["decode_us"] = decode_graph_ms_per_step(
+                torch, args, lambda i: q.decode_ffn(lg[i][0], xs[i][0], k, *packs[i % layers], bufs=db,
+                                                    stream=torch.cuda.current_stream()), layers) * 1e3
+        row["small_weight_GBps"] = (u + 1) * expert_bytes / (row["small_us"] * 1e-6) / 1e9
+        row["small_us_per_row"] = row["small_us"] / T
+        rows.append(row)
+        print(f"# T={T}: few-token {row['small_us']:.1f} us, prefill path {row['prefill_path_us']:.1f} us",
+              file=sys.stderr, flush=True)
+    return {"metric": "few-row MoE layer (groups of T rows at the decode shapes): us per step", "unit": "us",
+            "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
+            "config": {"workload": "few-row groups T=1..8 E=256 k=8 H=2048 I=512 + shared",
+                       "steps_per_T": args.steps, "weight_copies": layers},
+            "rows": rows,
+            "timing": "steps back to back from HIP graphs of consecutive steps, each with fresh rows and its own "
+                      "weight copy; wall clock between two synchronisations"}
+
+
 # ------------------------------------------------------------------ ablations
 def bench_ablation(args, torch, q, W, T, d):
     """The pages' two prefill mechanisms, each against its unfused alternative,
@@ -576,6 +638,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--ablation", type=int, default=0,
                     help="T: run the fused / unfused-dequant / host-synced-routing comparison at T tokens instead")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time groups of 1..8 rows on the few-token, prefill and decode paths instead")
+    ap.add_argument("--crossover-rows", default="", help="comma-separated T values for --crossover (default 1..8)")
     ap.add_argument("--cpu-reps", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="stop repeating the CPU oracle once this much time is spent (at least one run)")
@@ -603,6 +668,9 @@ def main():
 
     if args.ablation:
         print(json.dumps(bench_ablation(args, torch, q, W, args.ablation, d)), flush=True)
+        return
+    if args.crossover:
+        print(json.dumps(bench_crossover(args, torch, q, W, d)), flush=True)
         return
     ceilings = measured_ceilings(torch, q)
     if w.ffn and w.T == 1:

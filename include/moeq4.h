@@ -62,6 +62,7 @@ extern "C" {
 
 #define MOEQ4_MAX_EXPERTS 1024
 #define MOEQ4_MAX_TOPK 64
+#define MOEQ4_SMALL_MAX_T 8   /* tokens moe_small_batch_ffn_q4 takes at most */
 
 /* Human-readable text for a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
@@ -281,6 +282,54 @@ int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int 
                       const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
                       int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/* Bytes of device scratch moe_small_batch_ffn_q4 needs (0 on invalid or
+ * unsupported sizes).  shared: 1 when a shared expert is given, else 0. */
+size_t moe_small_batch_workspace_bytes(int T, int E, int k, int H, int I, int shared);
+
+/* The MoE layer for a small group of tokens (1 <= T <= MOEQ4_SMALL_MAX_T), such
+ * as the two to five rows of a speculative-decoding verification step
+ * (section "Limits of further optimization": that shape suits neither the
+ * matrix path nor the one-row path, and its rows often select different
+ * experts).  Same result, token by token, as moe_decode_ffn_q4 and as
+ * moe_route + moe_expert_ffn_q4 (up to fp32 summation order):
+ *
+ *   ids[t], w[t] = top-k of logits[t] and softmax over the k selected
+ *   out[t]       = bf16( sum_j w[t][j] * D_{ids[t][j]} h[t][j]  +  D_sh h_sh[t] )
+ *   h[t][j]      = bf16( silu(G x[t]) * (U x[t]) ) with expert ids[t][j]'s gate
+ *                  and up rows (the shared expert's for h_sh)
+ *
+ * in two kernels, with every distinct selected expert's weights read once for
+ * all the tokens that selected it (and the shared expert's once for all T).
+ * The routing stays on the GPU: nothing is copied to the host.  The result is
+ * the same for the same inputs, run after run.
+ *
+ * In:  logits  float  [T, E]        router logits (finite).
+ *      x       uint16 (bf16) [T, H] activations.
+ *      gu_*, dn_*, sh_*              as moe_decode_ffn_q4 (tiled layout of
+ *                                   moe_prepack_q4; the six sh_* all given or
+ *                                   all NULL).
+ *      workspace  device scratch of moe_small_batch_workspace_bytes(T, E, k,
+ *              H, I, shared) bytes, 16-byte aligned; no initial contents needed.
+ * Out: out     uint16 (bf16) [T, H].
+ *      topk_ids int32 [T, k], topk_w float [T, k]   the routing (each may be NULL).
+ * Sizes: 1 <= T <= MOEQ4_SMALL_MAX_T, 1 <= k <= min(E, MOEQ4_MAX_TOPK),
+ *        E <= MOEQ4_MAX_EXPERTS, H and I multiples of 64 and at least 128,
+ *        T*H <= 16384, T*(k+1)*I <= 49152 (the activations and the gated
+ *        outputs are staged in LDS), E*2I*H/2 below 2^31.  Larger sizes give
+ *        MOEQ4_ERR_UNSUPPORTED (use moe_route + moe_expert_ffn_q4).
+ * Errors: MOEQ4_ERR_NULL, MOEQ4_ERR_SHAPE, MOEQ4_ERR_UNSUPPORTED,
+ *         MOEQ4_ERR_ALIGN, MOEQ4_ERR_WORKSPACE, MOEQ4_ERR_HIP; on error nothing
+ *         is enqueued. */
+int moe_small_batch_ffn_q4(const float* logits, const uint16_t* x, int T, int E, int k, int H, int I,
+                           const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                           const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                           const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                           const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                           const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                           const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                           int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /* Measured MFMA ceiling (measurement only, not a step of the method): each of
  * `workgroups` workgroups of 4 waves issues iters x 8 independent

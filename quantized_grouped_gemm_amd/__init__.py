@@ -27,6 +27,9 @@ MOEQ4_ERR_ALIGN = -3
 MOEQ4_ERR_WORKSPACE = -4
 MOEQ4_ERR_UNSUPPORTED = -5
 MOEQ4_ERR_HIP = -6
+MOEQ4_MAX_EXPERTS = 1024
+MOEQ4_MAX_TOPK = 64
+MOEQ4_SMALL_MAX_T = 8
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -48,6 +51,8 @@ SIGNATURES = {
                                                                        _vp]),
     "moe_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_decode_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_small_batch_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "moe_small_batch_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_calibrate_mfma": (_i, [_i, _i, _vp, _vp]),
     "moe_dequant_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
 }
@@ -176,6 +181,21 @@ def moe_decode_ffn_q4(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_
         _p(workspace), int(ws_bytes), _stream(stream)))
 
 
+def moe_small_batch_workspace_bytes(T: int, E: int, k: int, H: int, I: int, shared: bool) -> int:
+    return int(lib().moe_small_batch_workspace_bytes(T, E, k, H, I, int(bool(shared))))
+
+
+def moe_small_batch_ffn_q4(logits, x, T, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t,
+                           dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                           sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, topk_ids, topk_w, out, workspace,
+                           ws_bytes, stream=None):
+    _ok("moe_small_batch_ffn_q4", lib().moe_small_batch_ffn_q4(
+        _p(logits), _p(x), T, E, k, H, I, _p(gu_codes_t), _p(gu_scales_t), _p(gu_biases_t), _p(dn_codes_t),
+        _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
+        _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), _p(topk_ids), _p(topk_w), _p(out),
+        _p(workspace), int(ws_bytes), _stream(stream)))
+
+
 def moe_dequant_q4(codes_t, scales_t, biases_t, E, N, K, out, stream=None):
     _ok("moe_dequant_q4", lib().moe_dequant_q4(_p(codes_t), _p(scales_t), _p(biases_t), E, N, K, _p(out),
                                                _stream(stream)))
@@ -271,6 +291,34 @@ def decode_ffn(logits, x, k: int, gu, dn, sh_gu=None, sh_dn=None, bufs=None, str
     sd = sh_dn if shared else (None, None, None)
     moe_decode_ffn_q4(logits, x, E, k, H, I, *gu, *dn, *sg, *sd, b["topk_ids"], b["topk_w"], b["out"],
                       b["workspace"], b["ws_bytes"], stream)
+    return b
+
+
+def alloc_small(T: int, E: int, k: int, H: int, I: int, shared: bool = True, device="cuda"):
+    """Output and workspace tensors for moe_small_batch_ffn_q4."""
+    ws = moe_small_batch_workspace_bytes(T, E, k, H, I, shared)
+    if ws == 0:
+        raise MoeQ4Error("moe_small_batch_workspace_bytes", MOEQ4_ERR_SHAPE)
+    return dict(
+        out=torch.empty(T, H, dtype=torch.int16, device=device),
+        topk_ids=torch.empty(T, k, dtype=torch.int32, device=device),
+        topk_w=torch.empty(T, k, dtype=torch.float32, device=device),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=device), ws_bytes=ws)
+
+
+def small_batch_ffn(logits, x, k: int, gu, dn, sh_gu=None, sh_dn=None, bufs=None, stream=None):
+    """The layer for a few tokens (moe_small_batch_ffn_q4).  ``logits`` float32
+    [T, E], ``x`` bf16 bits [T, H], 1 <= T <= 8; weights as decode_ffn.  Returns
+    the buffer dict (``out`` holds bf16 bits [T, H])."""
+    T, E = logits.shape
+    H = x.shape[-1]
+    I = gu[0].shape[1] // 2
+    shared = sh_gu is not None
+    b = bufs or alloc_small(T, E, k, H, I, shared, device=x.device)
+    sg = sh_gu if shared else (None, None, None)
+    sd = sh_dn if shared else (None, None, None)
+    moe_small_batch_ffn_q4(logits, x, T, E, k, H, I, *gu, *dn, *sg, *sd, b["topk_ids"], b["topk_w"], b["out"],
+                           b["workspace"], b["ws_bytes"], stream)
     return b
 
 

@@ -209,6 +209,55 @@ int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int 
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 
+static int check_small_shape(int T, int E, int k, int H, int I) {
+  if (T < 1 || E < 1 || E > MOEQ4_MAX_EXPERTS || k < 1 || k > E) return MOEQ4_ERR_SHAPE;
+  if (k > MOEQ4_MAX_TOPK || T > MOEQ4_SMALL_MAX_T) return MOEQ4_ERR_UNSUPPORTED;
+  if (H < 128 || H % 64 != 0 || I < 128 || I % 64 != 0) return MOEQ4_ERR_SHAPE;
+  if ((long long)E * 2 * I * (H / 2) >= (1LL << 31)) return MOEQ4_ERR_SHAPE;
+  if (!small_fits(T, E, k, H, I)) return MOEQ4_ERR_UNSUPPORTED;
+  return MOEQ4_OK;
+}
+
+size_t moe_small_batch_workspace_bytes(int T, int E, int k, int H, int I, int shared) {
+  (void)shared;
+  if (check_small_shape(T, E, k, H, I) != MOEQ4_OK) return 0;
+  return small_plan(T, E, k, H, I).ws_bytes;
+}
+
+int moe_small_batch_ffn_q4(const float* logits, const uint16_t* x, int T, int E, int k, int H, int I,
+                           const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                           const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                           const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                           const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                           const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                           const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                           int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  const void* sh[] = {sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                      sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t};
+  int nsh = 0;
+  for (const void* p : sh) nsh += p != nullptr;
+  if (nsh != 0 && nsh != 6) return MOEQ4_ERR_NULL;
+  const int rc = check_small_shape(T, E, k, H, I);
+  if (rc != MOEQ4_OK) return rc;
+  if (!logits || !x || !gu_codes_t || !gu_scales_t || !gu_biases_t || !dn_codes_t || !dn_scales_t ||
+      !dn_biases_t || !out || !workspace)
+    return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {logits, x, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
+                        dn_biases_t, out, workspace, topk_ids, topk_w};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
+  for (const void* p : sh)
+    if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
+  const SmallPlan plan = small_plan(T, E, k, H, I);
+  if (ws_bytes < plan.ws_bytes) return MOEQ4_ERR_WORKSPACE;
+  const hipError_t err = small_launch(plan, logits, x, T, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t,
+                                      dn_codes_t, dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t,
+                                      sh_gu_biases_t, sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, topk_ids,
+                                      topk_w, out, workspace, (hipStream_t)stream);
+  return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
 static int check_ffn_shape(int T, int H, int I, int E, int k) {
   const int rc = check_routing_shape(T, E, k);
   if (rc != MOEQ4_OK) return rc;

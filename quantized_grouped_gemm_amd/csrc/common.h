@@ -310,6 +310,30 @@ hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_
                          const uint16_t* sh_dn_s, const uint16_t* sh_dn_b, int32_t* ids_out, float* w_out,
                          uint16_t* out, void* workspace, hipStream_t stream);
 
+// small.hip: the layer for 1..MOEQ4_SMALL_MAX_T tokens, every distinct
+// selected expert read once for all the tokens that chose it
+struct SmallPlan {
+  int umax;            // slots for distinct experts: min(E, T*k)
+  int nsplit;          // parts the down projection splits the slots into (1 or 2)
+  size_t ws_plan;      // int32 [1 + umax]: the distinct-expert count, then the experts in ascending order
+  size_t ws_jt;        // uint32 [1 + umax][2]: per slot, byte i = token i's choice (slot umax: shared expert)
+  size_t ws_ids, ws_w;  // int32 / fp32 [T][k]: the routing of every token
+  size_t ws_h;         // bf16 [T][k+1][I]: SwiGLU output per (token, choice); choice k = shared expert
+  size_t ws_part;      // fp32 [nsplit][T][H]: partial sums of the down projection (nsplit > 1)
+  size_t ws_bytes;
+  size_t lds_gateup, lds_down;  // dynamic LDS bytes per kernel
+};
+
+SmallPlan small_plan(int T, int E, int k, int H, int I);
+bool small_fits(int T, int E, int k, int H, int I);  // staging and LDS limits of the two kernels
+
+hipError_t small_launch(const SmallPlan& p, const float* logits, const uint16_t* x, int T, int E, int k, int H,
+                        int I, const uint8_t* gu_q, const uint16_t* gu_s, const uint16_t* gu_b,
+                        const uint8_t* dn_q, const uint16_t* dn_s, const uint16_t* dn_b, const uint8_t* sh_gu_q,
+                        const uint16_t* sh_gu_s, const uint16_t* sh_gu_b, const uint8_t* sh_dn_q,
+                        const uint16_t* sh_dn_s, const uint16_t* sh_dn_b, int32_t* ids_out, float* w_out,
+                        uint16_t* out, void* workspace, hipStream_t stream);
+
 struct FfnPlan {
   // workspace: routed h [T*k][I], shared h [T][I], routed terms [T*k][H], shared term [T][H]
   size_t ws_h, ws_hs, ws_dw, ws_dsh, ws_bytes;

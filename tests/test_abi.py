@@ -28,6 +28,13 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(q.SIGNATURES), "binding and header disagree"
 
 
+def test_limits_match_header():
+    src = open(HDR).read()
+    for name in ("MOEQ4_MAX_EXPERTS", "MOEQ4_MAX_TOPK", "MOEQ4_SMALL_MAX_T"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
+        assert m and int(m.group(1)) == getattr(q, name), name
+
+
 def test_strerror_covers_codes():
     for c in range(0, -7, -1):
         assert q.strerror(c) != "unknown status"
@@ -151,6 +158,41 @@ def test_decode_validation():
     assert _decode(x=FAKE + 4) == q.MOEQ4_ERR_ALIGN
     assert _decode(ws_bytes=16) == q.MOEQ4_ERR_WORKSPACE
     assert _decode(E=128, k=64, I=1088) == q.MOEQ4_ERR_UNSUPPORTED      # h of 32 experts: beyond LDS
+
+
+def _small(**kw):
+    # every call below carries one invalid argument: rejected before any launch
+    a = dict(logits=FAKE, x=FAKE, T=3, E=16, k=2, H=256, I=128, gu_q=FAKE, gu_s=FAKE, gu_b=FAKE, dn_q=FAKE,
+             dn_s=FAKE, dn_b=FAKE, sh_gu_q=None, sh_gu_s=None, sh_gu_b=None, sh_dn_q=None, sh_dn_s=None,
+             sh_dn_b=None, topk_ids=None, topk_w=None, out=FAKE, workspace=FAKE,
+             ws_bytes=q.moe_small_batch_workspace_bytes(3, 16, 2, 256, 128, False), stream=None)
+    a.update(kw)
+    return q.lib().moe_small_batch_ffn_q4(*a.values())
+
+
+def test_small_batch_validation():
+    assert q.moe_small_batch_workspace_bytes(5, 256, 8, 2048, 512, True) > 0
+    assert q.moe_small_batch_workspace_bytes(8, 256, 8, 2048, 512, True) > 0   # the decode shapes, 8 tokens
+    # the plan, the routing and the gated outputs: grows with T and with the distinct-expert slots
+    assert (q.moe_small_batch_workspace_bytes(8, 256, 8, 2048, 512, True) >
+            q.moe_small_batch_workspace_bytes(2, 256, 8, 2048, 512, True))
+    assert q.moe_small_batch_workspace_bytes(0, 256, 8, 2048, 512, True) == 0    # T = 0
+    assert q.moe_small_batch_workspace_bytes(9, 256, 8, 2048, 512, True) == 0    # T above 8
+    assert q.moe_small_batch_workspace_bytes(8, 256, 8, 4096, 512, True) == 0    # x of 8 tokens beyond LDS
+    assert q.moe_small_batch_workspace_bytes(8, 256, 16, 2048, 512, True) == 0   # h beyond LDS
+    assert q.moe_small_batch_workspace_bytes(2, 256, 8, 2048, 96, True) == 0     # I not a multiple of 64
+    assert _small(T=0) == q.MOEQ4_ERR_SHAPE
+    assert _small(T=q.MOEQ4_SMALL_MAX_T + 1) == q.MOEQ4_ERR_UNSUPPORTED
+    assert _small(k=17) == q.MOEQ4_ERR_SHAPE                            # k > E
+    assert _small(E=128, k=65) == q.MOEQ4_ERR_UNSUPPORTED                # k > 64
+    assert _small(H=192 + 8) == q.MOEQ4_ERR_SHAPE
+    assert _small(T=8, H=4096) == q.MOEQ4_ERR_UNSUPPORTED
+    assert _small(logits=None) == q.MOEQ4_ERR_NULL
+    assert _small(out=None) == q.MOEQ4_ERR_NULL
+    assert _small(sh_dn_b=FAKE) == q.MOEQ4_ERR_NULL                     # shared: all six or none
+    assert _small(x=FAKE + 4) == q.MOEQ4_ERR_ALIGN
+    assert _small(topk_w=FAKE + 8) == q.MOEQ4_ERR_ALIGN
+    assert _small(ws_bytes=16) == q.MOEQ4_ERR_WORKSPACE
 
 
 def _ffn(**kw):
