@@ -328,24 +328,40 @@ def bench_ffn(args, torch, q, W, w, d):
     rt = q.alloc_route(T, E, k, args.block_rows, device=X.device)
     bufs = q.alloc_ffn(T, H, I, E, k, True, device=X.device)
     stream = torch.cuda.current_stream()
+    chunked = None
+    if args.chunk:  # the same step as a sequence of bounded chunks (moe_prefill_ffn_chunked_q4)
+        chunked = q.alloc_chunked(T, args.chunk, H, I, E, k, args.block_rows, True, device=X.device)
 
     def step(i, ev):
         if ev is not None:
             ev[0].record(stream)
-        q.route(logits, k, bufs=rt, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        q.expert_ffn(X, k, rt, *packs[i % layers], bufs=bufs, stream=stream)
+        if chunked is not None:
+            if ev is not None:
+                ev[1].record(stream)
+            q.prefill_ffn_chunked(logits, X, k, *packs[i % layers], bufs=chunked, stream=stream)
+        else:
+            q.route(logits, k, bufs=rt, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            q.expert_ffn(X, k, rt, *packs[i % layers], bufs=bufs, stream=stream)
         if ev is not None:
             ev[2].record(stream)
+
+    def graph_step(l):
+        s = torch.cuda.current_stream()
+        if chunked is not None:
+            q.prefill_ffn_chunked(logits, X, k, *packs[l], bufs=chunked, stream=s)
+        else:
+            q.route(logits, k, bufs=rt, stream=s)
+            q.expert_ffn(X, k, rt, *packs[l], bufs=bufs, stream=s)
 
     eager_ms, (route_all, ffn_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
     ffn_ms = float(ffn_all.mean())
     ms_per_step = eager_ms
     if not args.no_graph:
-        ms_per_step = graph_ms_per_step(torch, args, lambda l: (
-            q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
-            q.expert_ffn(X, k, rt, *packs[l], bufs=bufs, stream=torch.cuda.current_stream())), layers)
+        ms_per_step = graph_ms_per_step(torch, args, graph_step, layers)
+    if chunked is not None:
+        q.route(logits, k, bufs=rt, stream=stream)   # expert counts of the whole batch, for the byte count
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     flops = ffn_flops(T, H, I, k, True)
@@ -353,8 +369,9 @@ def bench_ffn(args, torch, q, W, w, d):
     alg_bytes = w_bytes + T * H * 2 * 2   # weights, X once, out once
     out = base_line(args, w, flops / (ms_per_step * 1e-3) / 1e12, ms_per_step,
                     {"workload": w.name, "T": T, "E": E, "top_k": k, "H": H, "I": I, "shared_expert": True,
-                     "block_rows": rt["block_rows"], "group": 64, "parallelism": "single GPU"},
-                    roofline(flops, alg_bytes, ffn_ms, "expert_ffn", w.name))
+                     "block_rows": rt["block_rows"], "group": 64, "parallelism": "single GPU",
+                     **({"chunk_tokens": args.chunk} if args.chunk else {})},
+                    roofline(flops, alg_bytes, ffn_ms, "expert_ffn" + ("_chunked" if args.chunk else ""), w.name))
     out.update({
         "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
         "ffn": {"us": ffn_ms * 1e3, "TFLOP/s": flops / (ffn_ms * 1e-3) / 1e12, "experts_touched": touched,
@@ -362,6 +379,10 @@ def bench_ffn(args, torch, q, W, w, d):
                            "shared down in one launch, combine"},
         "route_us": float(route_all.mean()) * 1e3,
         "eager_ms_per_step": eager_ms,
+        "scratch_bytes": (chunked["ws_bytes"] if chunked is not None else
+                          rt["ws_bytes"] + bufs["ws_bytes"] + sum(rt[n].numel() * rt[n].element_size() for n in
+                                                                 ("topk_ids", "topk_w", "counts", "offsets", "perm",
+                                                                  "inv_perm", "blocks", "num_blocks"))),
         "timing": f"steps back to back, wall clock between two synchronisations" +
                   ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
                    "(route + FFN launches, one weight copy each)") +
@@ -640,6 +661,8 @@ def main():
                     help="T: run the fused / unfused-dequant / host-synced-routing comparison at T tokens instead")
     ap.add_argument("--crossover", action="store_true",
                     help="time groups of 1..8 rows on the few-token, prefill and decode paths instead")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="expert-FFN workload: run the step as chunks of this many tokens (moe_prefill_ffn_chunked_q4)")
     ap.add_argument("--crossover-rows", default="", help="comma-separated T values for --crossover (default 1..8)")
     ap.add_argument("--cpu-reps", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,

@@ -236,6 +236,49 @@ int moe_expert_ffn_q4(const uint16_t* X, int T, int H, int I, int E, int k, cons
                       const int32_t* blocks, const int32_t* num_blocks, int max_blocks, int block_rows,
                       uint16_t* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of device scratch moe_prefill_ffn_chunked_q4 needs for T tokens in
+ * chunks of chunk_tokens (0 on invalid sizes).  It is that of one chunk, not
+ * of the whole prompt.  shared: 1 when a shared expert is given, else 0. */
+size_t moe_prefill_ffn_chunked_workspace_bytes(int T, int chunk_tokens, int H, int I, int E, int k,
+                                               int block_rows, int shared);
+
+/* The routed expert FFN (+ shared expert) of a long prompt, run as a sequence
+ * of bounded chunks (section "Limit scratch memory with prompt chunking": the
+ * temporary matrices of one chunk at a time, reused for the next, so the
+ * scratch no longer grows with the prompt while the weights stay resident;
+ * the output is unchanged).  For each chunk of chunk_tokens tokens (the last
+ * one shorter), in order on the stream: moe_route over its logits, then
+ * moe_expert_ffn_q4 over its rows, into the chunk's rows of out.  Every token's
+ * result is the one moe_route + moe_expert_ffn_q4 give for it (the per-token
+ * arithmetic does not depend on the other tokens of the call; the kernels
+ * chosen for a chunk size may sum in another fp32 order than those for T).
+ *
+ * In:  logits float [T, E]; X uint16 (bf16) [T, H]; weights as moe_expert_ffn_q4.
+ *      chunk_tokens  tokens per chunk: a multiple of 4, at least 4 (a chunk
+ *                    longer than T means one chunk).
+ *      block_rows    0 (the default for a full chunk) or 16/32/64/128/256; the
+ *                    same for every chunk.
+ *      workspace     device scratch of moe_prefill_ffn_chunked_workspace_bytes(
+ *                    T, chunk_tokens, H, I, E, k, block_rows, shared) bytes,
+ *                    16-byte aligned; no initial contents needed.
+ * Out: out uint16 (bf16) [T, H].
+ *      topk_ids int32 [T, k], topk_w float [T, k]: the routing (each may be
+ *                    NULL; then it lives in the workspace, one chunk at a time).
+ * Sizes: as moe_expert_ffn_q4 for one chunk.
+ * Errors: MOEQ4_ERR_NULL, MOEQ4_ERR_SHAPE (also chunk_tokens not a positive
+ *         multiple of 4), MOEQ4_ERR_UNSUPPORTED, MOEQ4_ERR_ALIGN,
+ *         MOEQ4_ERR_WORKSPACE, MOEQ4_ERR_HIP; every check runs before the first
+ *         chunk is enqueued. */
+int moe_prefill_ffn_chunked_q4(const float* logits, const uint16_t* X, int T, int H, int I, int E, int k,
+                               const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                               const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                               const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                               const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                               const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                               const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                               int chunk_tokens, int block_rows, int32_t* topk_ids, float* topk_w,
+                               uint16_t* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of device scratch moe_decode_ffn_q4 needs (0 on invalid sizes).
  * shared: 1 when a shared expert is given, else 0. */
 size_t moe_decode_workspace_bytes(int E, int k, int H, int I, int shared);

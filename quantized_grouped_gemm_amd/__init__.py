@@ -51,6 +51,9 @@ SIGNATURES = {
                                                                        _vp]),
     "moe_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_decode_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_prefill_ffn_chunked_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "moe_prefill_ffn_chunked_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_i, _i, _vp, _vp, _vp, _vp,
+                                                                                      _sz, _vp]),
     "moe_small_batch_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "moe_small_batch_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_calibrate_mfma": (_i, [_i, _i, _vp, _vp]),
@@ -181,6 +184,23 @@ def moe_decode_ffn_q4(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_
         _p(workspace), int(ws_bytes), _stream(stream)))
 
 
+def moe_prefill_ffn_chunked_workspace_bytes(T: int, chunk_tokens: int, H: int, I: int, E: int, k: int,
+                                            block_rows: int, shared: bool) -> int:
+    return int(lib().moe_prefill_ffn_chunked_workspace_bytes(T, chunk_tokens, H, I, E, k, block_rows,
+                                                             int(bool(shared))))
+
+
+def moe_prefill_ffn_chunked_q4(logits, X, T, H, I, E, k, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t,
+                               dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                               sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, chunk_tokens, block_rows, topk_ids,
+                               topk_w, out, workspace, ws_bytes, stream=None):
+    _ok("moe_prefill_ffn_chunked_q4", lib().moe_prefill_ffn_chunked_q4(
+        _p(logits), _p(X), T, H, I, E, k, _p(gu_codes_t), _p(gu_scales_t), _p(gu_biases_t), _p(dn_codes_t),
+        _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
+        _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), int(chunk_tokens), int(block_rows),
+        _p(topk_ids), _p(topk_w), _p(out), _p(workspace), int(ws_bytes), _stream(stream)))
+
+
 def moe_small_batch_workspace_bytes(T: int, E: int, k: int, H: int, I: int, shared: bool) -> int:
     return int(lib().moe_small_batch_workspace_bytes(T, E, k, H, I, int(bool(shared))))
 
@@ -291,6 +311,38 @@ def decode_ffn(logits, x, k: int, gu, dn, sh_gu=None, sh_dn=None, bufs=None, str
     sd = sh_dn if shared else (None, None, None)
     moe_decode_ffn_q4(logits, x, E, k, H, I, *gu, *dn, *sg, *sd, b["topk_ids"], b["topk_w"], b["out"],
                       b["workspace"], b["ws_bytes"], stream)
+    return b
+
+
+def alloc_chunked(T: int, chunk_tokens: int, H: int, I: int, E: int, k: int, block_rows: int = 0,
+                  shared: bool = True, device="cuda"):
+    """Output and workspace tensors for moe_prefill_ffn_chunked_q4."""
+    ws = moe_prefill_ffn_chunked_workspace_bytes(T, chunk_tokens, H, I, E, k, block_rows, shared)
+    if ws == 0:
+        raise MoeQ4Error("moe_prefill_ffn_chunked_workspace_bytes", MOEQ4_ERR_SHAPE)
+    return dict(
+        out=torch.empty(max(T, 1), H, dtype=torch.int16, device=device),
+        topk_ids=torch.empty(max(T, 1), k, dtype=torch.int32, device=device),
+        topk_w=torch.empty(max(T, 1), k, dtype=torch.float32, device=device),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=device), ws_bytes=ws,
+        chunk_tokens=chunk_tokens, block_rows=block_rows)
+
+
+def prefill_ffn_chunked(logits, X, k: int, gu, dn, sh_gu=None, sh_dn=None, chunk_tokens: int = 1024,
+                        block_rows: int = 0, bufs=None, stream=None):
+    """The routed FFN (+ shared expert) of T tokens in chunks of ``chunk_tokens``
+    (moe_prefill_ffn_chunked_q4).  ``logits`` float32 [T, E], ``X`` bf16 bits
+    [T, H]; weights as expert_ffn.  Returns the buffer dict (``out`` bf16 bits
+    [T, H], ``topk_ids`` / ``topk_w`` [T, k])."""
+    T, E = logits.shape
+    H = X.shape[-1]
+    I = gu[0].shape[1] // 2
+    shared = sh_gu is not None
+    b = bufs or alloc_chunked(T, chunk_tokens, H, I, E, k, block_rows, shared, device=X.device)
+    sg = sh_gu if shared else (None, None, None)
+    sd = sh_dn if shared else (None, None, None)
+    moe_prefill_ffn_chunked_q4(logits, X, T, H, I, E, k, *gu, *dn, *sg, *sd, b["chunk_tokens"], b["block_rows"],
+                               b["topk_ids"], b["topk_w"], b["out"], b["workspace"], b["ws_bytes"], stream)
     return b
 
 

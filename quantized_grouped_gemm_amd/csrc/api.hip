@@ -28,6 +28,48 @@ int resolve_block_rows(int T, int E, int k, int block_rows) {
   return valid_block_rows(block_rows) ? block_rows : MOEQ4_ERR_SHAPE;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the chunked prefill: the routing outputs and scratch of one
+// chunk, then the FFN scratch of one chunk (each sized for the larger of a full
+// chunk and the last, shorter one).
+struct ChunkLayout {
+  int tc, bm;  // chunk tokens in effect, block rows
+  size_t ids, w, counts, offsets, perm, inv_perm, blocks, nblk, route_ws, ffn_ws, total;
+};
+
+int chunk_layout(int T, int chunk, int H, int I, int E, int k, int block_rows, int shared, ChunkLayout& L) {
+  if (T < 0 || chunk < 4 || chunk % 4 != 0) return MOEQ4_ERR_SHAPE;
+  L.tc = T > 0 && chunk > T ? T : chunk;
+  int rc = check_routing_shape(L.tc, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return MOEQ4_ERR_SHAPE;
+  if ((long long)E * 2 * I * (H / 2) >= (1LL << 31) || (long long)E * H * (I / 2) >= (1LL << 31))
+    return MOEQ4_ERR_SHAPE;
+  const long long A = (long long)L.tc * k;
+  if (A * I * 2 >= (1LL << 31) || (long long)L.tc * H * 2 >= (1LL << 31)) return MOEQ4_ERR_SHAPE;
+  L.bm = resolve_block_rows(L.tc, E, k, block_rows);
+  if (L.bm <= 0) return L.bm;
+  const int last = T > 0 && T % L.tc != 0 ? T % L.tc : L.tc;
+  const int mb = moe_max_blocks(L.tc, E, k, L.bm);
+  if (mb < 0) return mb;
+  size_t o = 0;
+  L.ids = o;      o += align256(sizeof(int32_t) * (size_t)A);
+  L.w = o;        o += align256(sizeof(float) * (size_t)A);
+  L.counts = o;   o += align256(sizeof(int32_t) * (size_t)E);
+  L.offsets = o;  o += align256(sizeof(int32_t) * (size_t)(E + 1));
+  L.perm = o;     o += align256(sizeof(int32_t) * (size_t)A);
+  L.inv_perm = o; o += align256(sizeof(int32_t) * (size_t)A);
+  L.blocks = o;   o += align256(sizeof(int32_t) * 4 * (size_t)mb);
+  L.nblk = o;     o += align256(sizeof(int32_t));
+  const size_t rws0 = route_plan(L.tc, E, k).ws_bytes, rws1 = route_plan(last, E, k).ws_bytes;
+  L.route_ws = o; o += align256(rws0 > rws1 ? rws0 : rws1);
+  const size_t fws0 = ffn_plan(L.tc, H, I, k, shared != 0).ws_bytes, fws1 = ffn_plan(last, H, I, k, shared != 0).ws_bytes;
+  L.ffn_ws = o;   o += align256(fws0 > fws1 ? fws0 : fws1);
+  L.total = o;
+  return MOEQ4_OK;
+}
+
 }  // namespace
 
 namespace moeq4 {
@@ -272,6 +314,70 @@ static int check_ffn_shape(int T, int H, int I, int E, int k) {
 size_t moe_expert_ffn_workspace_bytes(int T, int H, int I, int E, int k, int shared) {
   if (check_ffn_shape(T, H, I, E, k) != MOEQ4_OK) return 0;
   return ffn_plan(T, H, I, k, shared != 0).ws_bytes;
+}
+
+size_t moe_prefill_ffn_chunked_workspace_bytes(int T, int chunk_tokens, int H, int I, int E, int k,
+                                               int block_rows, int shared) {
+  ChunkLayout L;
+  if (chunk_layout(T, chunk_tokens, H, I, E, k, block_rows, shared, L) != MOEQ4_OK) return 0;
+  return L.total;
+}
+
+int moe_prefill_ffn_chunked_q4(const float* logits, const uint16_t* X, int T, int H, int I, int E, int k,
+                               const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                               const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                               const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                               const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                               const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                               const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                               int chunk_tokens, int block_rows, int32_t* topk_ids, float* topk_w,
+                               uint16_t* out, void* workspace, size_t ws_bytes, void* stream) {
+  const void* sh[] = {sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                      sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t};
+  int nsh = 0;
+  for (const void* p : sh) nsh += p != nullptr;
+  if (nsh != 0 && nsh != 6) return MOEQ4_ERR_NULL;
+  const int shared = nsh == 6;
+  ChunkLayout L;
+  const int rc = chunk_layout(T, chunk_tokens, H, I, E, k, block_rows, shared, L);
+  if (rc != MOEQ4_OK) return rc;
+  if (T == 0) return MOEQ4_OK;
+  if (!logits || !X || !gu_codes_t || !gu_scales_t || !gu_biases_t || !dn_codes_t || !dn_scales_t ||
+      !dn_biases_t || !out || !workspace)
+    return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {logits, X, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
+                        dn_biases_t, out, workspace, topk_ids, topk_w};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
+  for (const void* p : sh)
+    if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
+  if (ws_bytes < L.total) return MOEQ4_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  int32_t* inv_perm = (int32_t*)(ws + L.inv_perm);
+  int32_t* blocks = (int32_t*)(ws + L.blocks);
+  int32_t* nblk = (int32_t*)(ws + L.nblk);
+  const hipStream_t st = (hipStream_t)stream;
+  // Every chunk: route its tokens, then run the FFN on them, reusing the same
+  // scratch (stream order keeps a chunk's reads before the next chunk's
+  // writes).  Chunk starts are multiples of chunk_tokens (a multiple of 4), so
+  // every per-chunk pointer stays 16-byte aligned.
+  for (int t0 = 0; t0 < T; t0 += L.tc) {
+    const int tn = T - t0 < L.tc ? T - t0 : L.tc;
+    int32_t* ids = topk_ids ? topk_ids + (size_t)t0 * k : (int32_t*)(ws + L.ids);
+    float* w = topk_w ? topk_w + (size_t)t0 * k : (float*)(ws + L.w);
+    hipError_t err = route_launch(route_plan(tn, E, k), logits + (size_t)t0 * E, tn, E, k, L.bm, ids, w, counts,
+                                  offsets, perm, inv_perm, blocks, nblk, ws + L.route_ws, st);
+    if (err != hipSuccess) return MOEQ4_ERR_HIP;
+    err = ffn_launch(ffn_plan(tn, H, I, k, shared), X + (size_t)t0 * H, tn, H, I, E, k, gu_codes_t, gu_scales_t,
+                     gu_biases_t, dn_codes_t, dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t,
+                     sh_gu_biases_t, sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, w, perm, blocks, nblk,
+                     moe_max_blocks(tn, E, k, L.bm), L.bm, out + (size_t)t0 * H, ws + L.ffn_ws, st);
+    if (err != hipSuccess) return MOEQ4_ERR_HIP;
+  }
+  return MOEQ4_OK;
 }
 
 int moe_expert_ffn_q4(const uint16_t* X, int T, int H, int I, int E, int k, const uint8_t* gu_codes_t,

@@ -195,6 +195,41 @@ def test_small_batch_validation():
     assert _small(ws_bytes=16) == q.MOEQ4_ERR_WORKSPACE
 
 
+def _chunked(**kw):
+    # every call below carries one invalid argument: rejected before any launch
+    a = dict(logits=FAKE, X=FAKE, T=1000, H=256, I=128, E=16, k=2, gu_q=FAKE, gu_s=FAKE, gu_b=FAKE, dn_q=FAKE,
+             dn_s=FAKE, dn_b=FAKE, sh_gu_q=None, sh_gu_s=None, sh_gu_b=None, sh_dn_q=None, sh_dn_s=None,
+             sh_dn_b=None, chunk_tokens=256, block_rows=0, topk_ids=None, topk_w=None, out=FAKE, workspace=FAKE,
+             ws_bytes=q.moe_prefill_ffn_chunked_workspace_bytes(1000, 256, 256, 128, 16, 2, 0, False), stream=None)
+    a.update(kw)
+    return q.lib().moe_prefill_ffn_chunked_q4(*a.values())
+
+
+def test_chunked_validation():
+    ws = q.moe_prefill_ffn_chunked_workspace_bytes
+    assert ws(16384, 1024, 2048, 512, 256, 8, 0, True) > 0
+    # the scratch is that of one chunk: it does not grow with the prompt
+    assert ws(16384, 1024, 2048, 512, 256, 8, 0, True) == ws(4096, 1024, 2048, 512, 256, 8, 0, True)
+    assert ws(16384, 1024, 2048, 512, 256, 8, 0, True) < q.moe_expert_ffn_workspace_bytes(16384, 2048, 512, 256, 8,
+                                                                                          True)
+    assert ws(1000, 6, 256, 128, 16, 2, 0, False) == 0       # chunk not a multiple of 4
+    assert ws(1000, 0, 256, 128, 16, 2, 0, False) == 0
+    assert ws(1000, 256, 256, 96, 16, 2, 0, False) == 0      # I not a multiple of 64
+    assert ws(1000, 256, 256, 128, 16, 2, 24, False) == 0    # block rows
+    assert _chunked(chunk_tokens=0) == q.MOEQ4_ERR_SHAPE
+    assert _chunked(chunk_tokens=130) == q.MOEQ4_ERR_SHAPE
+    assert _chunked(T=-1) == q.MOEQ4_ERR_SHAPE
+    assert _chunked(k=17) == q.MOEQ4_ERR_SHAPE
+    assert _chunked(block_rows=48) == q.MOEQ4_ERR_SHAPE
+    assert _chunked(logits=None) == q.MOEQ4_ERR_NULL
+    assert _chunked(out=None) == q.MOEQ4_ERR_NULL
+    assert _chunked(sh_gu_b=FAKE) == q.MOEQ4_ERR_NULL
+    assert _chunked(X=FAKE + 2) == q.MOEQ4_ERR_ALIGN
+    assert _chunked(topk_ids=FAKE + 4) == q.MOEQ4_ERR_ALIGN
+    assert _chunked(ws_bytes=1024) == q.MOEQ4_ERR_WORKSPACE
+    assert _chunked(T=0, logits=None, X=None, out=None) == q.MOEQ4_OK   # nothing to do: no launch
+
+
 def _ffn(**kw):
     a = dict(X=FAKE, T=8, H=256, I=128, E=16, k=2, gu_q=FAKE, gu_s=FAKE, gu_b=FAKE, dn_q=FAKE, dn_s=FAKE,
              dn_b=FAKE, sh_gu_q=None, sh_gu_s=None, sh_gu_b=None, sh_dn_q=None, sh_dn_s=None, sh_dn_b=None,
