@@ -189,12 +189,8 @@ struct EpiRow {
       y[n] = f32_to_bf16_bits(v);
     }
   }
-  // values v[0..3] (and u[0..3] for kEpiSwiglu) of output columns n..n+3 (n % 4 == 0),
-  // written with one 8-byte store
-  __device__ __forceinline__ void store4(int n, f32x4 v, f32x4 u) const {
-    if constexpr (EPI == kEpiScale) {
-      if (!y) return;
-    }
+  // the 16-bit outputs of values v[0..3] (and u[0..3] for kEpiSwiglu), packed
+  __device__ __forceinline__ uint2 pack4(f32x4 v, f32x4 u) const {
     uint32_t b[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -203,7 +199,21 @@ struct EpiRow {
       else if constexpr (EPI == kEpiTerm) b[q] = term_bits(v[q]);
       else b[q] = f32_to_bf16_bits(v[q]);
     }
-    *(uint2*)(y + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  }
+  // values of output columns n..n+3 (n % 4 == 0), written with one 8-byte store
+  __device__ __forceinline__ void store4(int n, f32x4 v, f32x4 u) const {
+    if constexpr (EPI == kEpiScale) {
+      if (!y) return;
+    }
+    *(uint2*)(y + n) = pack4(v, u);
+  }
+  // 8 packed outputs of columns n..n+7 (n % 8 == 0), one 16-byte store
+  __device__ __forceinline__ void store8(int n, uint4 bits) const {
+    if constexpr (EPI == kEpiScale) {
+      if (!y) return;
+    }
+    *(uint4*)(y + n) = bits;
   }
 };
 
@@ -552,7 +562,6 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
     tile16[f] = min(n >> 4, NT - 1);
   }
   const int r16 = col & 15;
-  const int nf_live = min(NFO, max(0, (NOUT - n_wave + OUTF - 1) / OUTF));
 
   const int x_oob = a.xrows * K * 2;  // rows past the block: the load returns zeros, no traffic
   // this lane's DMA source per instruction: row rb + lane/16, 16-byte column
@@ -735,37 +744,51 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   // epilogue: the MFMAs take the weights as the A operand, so each 32x32
   // accumulator tile is transposed: lane l holds block row r*32 + l%32 and tile
   // rows 8*(i/4) + 4*(l/32) + i%4 (i = 0..15), i.e. four runs of 4 adjacent
-  // columns, each written with one 8-byte store.  Paired SwiGLU: runs 0 and 1
-  // are gate columns whose up partners are runs 2 and 3.
+  // columns.  Paired SwiGLU: runs 0 and 1 are gate columns whose up partners
+  // are runs 2 and 3.  Each wave converts its outputs of one 32-row tile into
+  // its own staging rows in LDS (the activation buffers, free after the
+  // loop), then reads them back row-wise: a lane stores 16 contiguous bytes
+  // and WCOLS/8 lanes one contiguous row segment, so a store instruction
+  // covers 64*8/WCOLS rows instead of 32 rows of 16 bytes each.  Only this
+  // wave touches its staging rows, and a wave's LDS operations complete in
+  // order, so the waits between writes and reads are the wave's own.
+  constexpr int WCOLS = NFO * OUTF;  // output columns of a wave
+  constexpr int SROW = WCOLS + 8;    // staged row, 16-byte pad
+  constexpr int LPR = WCOLS / 8;     // lanes per staged row
+  constexpr int RPI = 64 / LPR;      // rows per store instruction
+  static_assert(WAVES * 32 * SROW * 2 <= (int)sizeof(xs), "staging fits in the activation buffers");
+  __syncthreads();  // every wave is done with the activation buffers
+  uint16_t* const stg = &xs[0][0] + wave * 32 * SROW;
 #pragma unroll
   for (int r = 0; r < MF32; ++r) {
     if (r >= mfa) break;
-    const int row = r * 32 + col;
-    if (row < rows) {
-      const EpiRow<EPI> er(Yout, ldy, row0, row, &ep_tab);
+    {
+      const EpiRow<EPI> er(Yout, ldy, row0, min(r * 32 + col, rows - 1), &ep_tab);
       if constexpr (PAIRED) {
-        if (nf_live > 0) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int n = n_wave + 8 * j + 4 * half;
-            if (n < NOUT) er.store4(n, quad(acc[r][0], j), quad(acc[r][0], j + 2));
-          }
-        }
+        for (int j = 0; j < 2; ++j)
+          *(uint2*)&stg[col * SROW + 8 * j + 4 * half] = er.pack4(quad(acc[r][0], j), quad(acc[r][0], j + 2));
       } else {
 #pragma unroll
-        for (int f = 0; f < NFO; ++f) {
-          if (f >= nf_live) break;
+        for (int f = 0; f < NFO; ++f)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int n = n_wave + f * 32 + 8 * j + 4 * half;
-            if (n >= NOUT) continue;
             const f32x4 v = quad(acc[r][f], j);
-            if constexpr (EPI == kEpiSwiglu) er.store4(n, v, quad(acc[r][f + NFO], j));
-            else er.store4(n, v, v);
+            f32x4 u = v;
+            if constexpr (EPI == kEpiSwiglu) u = quad(acc[r][f + NFO], j);
+            *(uint2*)&stg[col * SROW + f * 32 + 8 * j + 4 * half] = er.pack4(v, u);
           }
-        }
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int rr = i * RPI + lane / LPR, cq = lane % LPR;
+      const int row = r * 32 + rr, n = n_wave + 8 * cq;
+      const uint4 bits = *(const uint4*)&stg[rr * SROW + 8 * cq];
+      if (row < rows && n < NOUT) EpiRow<EPI>(Yout, ldy, row0, row, &ep_tab).store8(n, bits);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads back before the next tile's writes
   }
 }
 
