@@ -222,6 +222,7 @@ struct GemmArgs {
   const int32_t* gather;      // non-null: row p reads X[gather[p] / k]; null: X[p]
   const int32_t* blocks;      // block map; null: dense BM-row blocks over A rows of expert 0
   const int32_t* num_blocks;  // device count of block-map entries
+  int max_blocks;             // entries blocks[] holds (the launch grid's bound)
   uint16_t* Y;                // output, row stride ldy
   int ldy;
   const int32_t* perm;        // kEpiScale; null: row p goes to row p with weight 1

@@ -111,9 +111,55 @@ __device__ __forceinline__ int gemm_nblocks(const GemmArgs& a, int BM) {
   return a.blocks ? *a.num_blocks : (a.A + BM - 1) / BM;
 }
 
+// gemm_task + gemm_block in one: the task slot does not depend on the routed
+// block count, so the count and the block-map entry (at a clamped index) are
+// read together instead of one after the other.  Returns false when the
+// workgroup has no task or the entry is malformed.
+__device__ __forceinline__ bool gemm_task_entry(const GemmArgs& a0, int BM, int ntiles, bool& dense, int& blk,
+                                                int& ntile, int& e, int& row0, int& rows) {
+  const int dblocks = (a0.d_rows + BM - 1) / BM;
+  gemm_task(dblocks, 0x7FFFFFFF, ntiles, dense, blk, ntile);
+  int nb, A = a0.A, E = a0.E;
+  if (dense || !a0.blocks) {
+    A = dense ? a0.d_rows : a0.A;
+    E = dense ? 1 : a0.E;
+    nb = dense ? dblocks : (A + BM - 1) / BM;
+    e = 0;
+    row0 = blk * BM;
+    rows = min(BM, A - row0);
+  } else {
+    const int cb = min(blk, max(a0.max_blocks, 1) - 1);
+    nb = *a0.num_blocks;
+    e = a0.blocks[4 * cb + 0];
+    row0 = a0.blocks[4 * cb + 1];
+    rows = min(a0.blocks[4 * cb + 2], BM);
+  }
+  if (blk >= nb) return false;
+  return !(e < 0 || e >= E || row0 < 0 || rows <= 0 || row0 + rows > A);
+}
+
 // byte offset of sorted row p's activations in X
 __device__ __forceinline__ int gemm_xrow(const GemmArgs& a, int p) {
   return (a.gather ? a.gather[p] / a.k : p) * a.K * 2;
+}
+
+// Byte offsets in X of block rows r[i] (clamped into the block: rows past it
+// get their offset replaced by the caller) for the N rows a thread stages.  The
+// gather branch is outside the loop, so the N index loads go out back to back
+// and are waited for once (a load inside a per-row branch is waited for before
+// the branch rejoins).
+template <int N>
+__device__ __forceinline__ void gemm_xrows(const GemmArgs& a, int row0, int rows, const int (&r)[N], int (&g)[N]) {
+  if (a.gather) {
+    int v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = a.gather[row0 + min(r[i], rows - 1)];
+#pragma unroll
+    for (int i = 0; i < N; ++i) g[i] = v[i] / a.k * a.K * 2;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) g[i] = (row0 + min(r[i], rows - 1)) * a.K * 2;
+  }
 }
 
 // Per-workgroup table of the kEpiScale rows: the assignment each sorted row
@@ -286,12 +332,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   // Rows past the block get an offset past the buffer: the buffer load returns
   // zeros without touching memory.
   const int x_oob = a.xrows * K * 2;
-  int xoff[XP];
+  int xoff[XP], xr[XP], xg[XP];
+#pragma unroll
+  for (int i = 0; i < XP; ++i) xr[i] = (tid + i * NTHR) >> 4;
+  gemm_xrows(a, row0, rows, xr, xg);
 #pragma unroll
   for (int i = 0; i < XP; ++i) {
     const int p = tid + i * NTHR;
     const int r = p >> 4, col = p & 15;
-    xoff[i] = (r < rows && p < BM * 16) ? gemm_xrow(a, row0 + r) + col * 16 : x_oob;
+    xoff[i] = (r < rows && p < BM * 16) ? xg[i] + col * 16 : x_oob;
   }
 
   Stage<NF, XP> st[S];
@@ -513,22 +562,25 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   const int NOUT = EPI == kEpiSwiglu ? a0.N / 2 : a0.N;
   const int ntiles = (NOUT + TILE_N - 1) / TILE_N;
   bool dense;
-  int blk, ntile;
-  if (!gemm_task((a0.d_rows + BM - 1) / BM, gemm_nblocks(a0, BM), ntiles, dense, blk, ntile)) return;
+  int blk, ntile, e, row0, rows;
+  if (!gemm_task_entry(a0, BM, ntiles, dense, blk, ntile, e, row0, rows)) return;
   const GemmArgs a = dense ? gemm_dense(a0) : a0;
   const int K = a.K, N = a.N;
   const uint8_t* __restrict__ Wt = a.Wt;
   const uint16_t* __restrict__ St = a.St;
   const uint16_t* __restrict__ Bt = a.Bt;
-  int e, row0, rows;
-  if (!gemm_block(a, BM, blk, e, row0, rows)) return;  // malformed entry
-  static_assert(BM <= 256, "the epilogue table holds 256 rows");
+  static_assert(BM <= 256 && BM <= WAVES * 64, "the epilogue table holds 256 rows, one per thread");
   __shared__ EpiTab ep_tab;
-  epi_fill<EPI>(a, row0, rows, &ep_tab);
   uint16_t* const Yout = a.Y;
   const int ldy = a.ldy;
 
   const int tid = threadIdx.x;
+  // kEpiScale: thread tid's row of the epilogue table (assignment and routing
+  // weight of block row tid).  The assignment is read first, the weight once
+  // the main loop's first loads are out, and the table is written to LDS only
+  // before the epilogue, so neither read delays the first MFMAs.
+  int ep_as = row0 + tid;
+  float ep_w = 1.f;
   const int lane = tid & 63;
   const int half = lane >> 5;   // K half inside a K-step
   const int col = lane & 31;    // column inside a 32-column tile
@@ -566,13 +618,26 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   const int x_oob = a.xrows * K * 2;  // rows past the block: the load returns zeros, no traffic
   // this lane's DMA source per instruction: row rb + lane/16, 16-byte column
   // (lane & 15) ^ (row & 15) of it
-  int xoff[IPW];
+  int xoff[IPW], xr[IPW], xg[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) xr[i] = 4 * (wave * IPW + i) + (lane >> 4);
+  gemm_xrows(a, row0, rows, xr, xg);
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int r = 4 * (wave * IPW + i) + (lane >> 4);
+    const int r = xr[i];
     const int c16 = (lane & 15) ^ (r & 15);
-    xoff[i] = r < rows ? gemm_xrow(a, row0 + r) + c16 * 16 : x_oob;
+    xoff[i] = r < rows ? xg[i] + c16 * 16 : x_oob;
   }
+  if constexpr (EPI == kEpiScale)
+    if (a.perm) ep_as = a.perm[row0 + min(tid, rows - 1)];
+  // the routing weight of the row, read behind the main loop's first loads
+  auto ep_weight = [&]() __attribute__((always_inline)) {
+    if constexpr (EPI == kEpiScale) {
+      const bool ok = ep_as >= 0 && ep_as < a.A;  // a malformed permutation entry writes nothing
+      if (a.perm) ep_w = a.topk_w[ok ? ep_as : 0];
+      if (!ok) ep_as = -1;
+    }
+  };
   typedef __attribute__((address_space(3))) void lds_void;
   // activations of chunk c (K values [128c, 128c + 128)) into LDS buffer buf.
   // The tail chunk of an odd G has only 8 columns: the other slots get the
@@ -682,6 +747,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
       for (int s = 0; s < S - 1; ++s) load(st[s], s);
 #pragma unroll
       for (int b = 0; b < kAhead; ++b) dma_x(min(b, nfull - 1), b, false);
+      ep_weight();
       __syncthreads();
       for (int c0 = 0; c0 < nfull; c0 += S) {
 #pragma unroll
@@ -726,6 +792,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
       // workgroup's LDS may still be in flight when it moves on (or ends)
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
     }
+    if (nfull == 0) ep_weight();
     if (odd_tail) {
       load_tail(st[0]);
       dma_x(nfull, 0, true);
@@ -757,7 +824,13 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   constexpr int LPR = WCOLS / 8;     // lanes per staged row
   constexpr int RPI = 64 / LPR;      // rows per store instruction
   static_assert(WAVES * 32 * SROW * 2 <= (int)sizeof(xs), "staging fits in the activation buffers");
-  __syncthreads();  // every wave is done with the activation buffers
+  if constexpr (EPI == kEpiScale) {
+    if (tid < rows) {
+      ep_tab.as[tid] = ep_as;
+      ep_tab.w[tid] = ep_as >= 0 ? ep_w : 0.f;
+    }
+  }
+  __syncthreads();  // every wave is done with the activation buffers; the table is written
   uint16_t* const stg = &xs[0][0] + wave * 32 * SROW;
 #pragma unroll
   for (int r = 0; r < MF32; ++r) {
@@ -854,11 +927,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a0, 
   // ---- the block's activations, all chunks, by DMA (rows past the block: zeros)
   typedef __attribute__((address_space(3))) void lds_void;
   const int x_oob = a.xrows * K * 2;
+  int xr[IPW], xg[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) xr[i] = 4 * (wave * IPW + i) + (lane >> 4);
+  gemm_xrows(a, row0, rows, xr, xg);
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int r = 4 * (wave * IPW + i) + (lane >> 4);
+    const int r = xr[i];
     const int c16 = (lane & 15) ^ (r & 15);
-    const int off = r < rows ? gemm_xrow(a, row0 + r) + c16 * 16 : x_oob;
+    const int off = r < rows ? xg[i] + c16 * 16 : x_oob;
     for (int c = 0; c < nch; ++c)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xsrc, (lds_void*)&xk[((size_t)c * BM + 4 * (wave * IPW + i)) * kKC], 16, off, c * kKC * 2, 0, 0);
@@ -1122,9 +1199,11 @@ static dim3 task_grid(long long dense_blocks, long long max_blocks, long long nt
   return dim3((unsigned)(((dense_blocks + kXcds - 1) / kXcds + (max_blocks + kXcds - 1) / kXcds) * ntiles * kXcds));
 }
 
-hipError_t gemm_launch(const GemmArgs& a, int epi, int BM, int max_blocks, hipStream_t stream) {
+hipError_t gemm_launch(const GemmArgs& a_in, int epi, int BM, int max_blocks, hipStream_t stream) {
   max_blocks = max(max_blocks, 0);
-  if (max_blocks == 0 && a.d_rows <= 0) return hipSuccess;
+  if (max_blocks == 0 && a_in.d_rows <= 0) return hipSuccess;
+  GemmArgs a = a_in;
+  a.max_blocks = max_blocks;
   const long long dense_blocks = a.d_rows > 0 ? (a.d_rows + BM - 1) / BM : 0;
   static const bool no_kres = getenv("MOEQ4_NO_KRES") != nullptr;  // for comparisons
   if (!no_kres && a.K <= kKResMax && a.K % kKC == 0) {
