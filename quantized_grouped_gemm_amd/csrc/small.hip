@@ -14,7 +14,7 @@
 //                    the distinct selected experts (a bit set and prefix
 //                    popcounts) and, per list entry ("slot"), one 8-byte word
 //                    holding each token's choice of that expert.
-//   k_small_gateup   workgroup (slot u, tpw 16-row tiles of I): gate and up
+//   k_small_gateup   workgroup (slot u, 16-row tile of I): gate and up
 //                    tiles of the u-th distinct expert (or of the shared
 //                    expert, in the last slot) rebuilt once per block and
 //                    applied to the x of each token that chose it:
@@ -43,9 +43,7 @@ constexpr int kSbDownThreads = kSbDownWaves * 64;
 constexpr int kSbDownBatch = 6;  // weight blocks a down wave keeps in flight
 constexpr int kSbXPieces = 4;    // 16-byte pieces of x per gate/up thread: T*H <= 8 * 4 * 512
 constexpr int kSbHPieces = 6;    // 16-byte pieces of h per down thread: T*(k+1)*I <= 8 * 6 * 1024
-constexpr int kSbMinGroups = 1024;      // gate/up workgroups to keep at least (four per CU)
 constexpr int kSbSplitSlots = 16;       // slots from which the down projection splits them in two
-constexpr int kSbMaxTilesPerGroup = 8;  // 16-row tiles one gate/up workgroup takes at most
 constexpr int kSbMaxT = MOEQ4_SMALL_MAX_T;
 constexpr int kSbMaxSlots = kSbMaxT * MOEQ4_MAX_TOPK;
 static_assert(kSbMaxT <= kSbWaves, "one routing wave per token");
@@ -148,18 +146,17 @@ __device__ __forceinline__ int sb_choice(uint32_t w0, uint32_t w1, int i) {
 
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(kSbThreads) void k_small_gateup(
-    const uint16_t* __restrict__ x, int T, int k, int H, int I, int umax, int tpw,
+    const uint16_t* __restrict__ x, int T, int k, int H, int I, int umax,
     const uint8_t* __restrict__ gu_q, const uint16_t* __restrict__ gu_s, const uint16_t* __restrict__ gu_b,
     const uint8_t* __restrict__ sh_q, const uint16_t* __restrict__ sh_s, const uint16_t* __restrict__ sh_b,
     const int32_t* __restrict__ plan_ws, const uint2* __restrict__ jt_ws, uint16_t* __restrict__ h_ws) {
   extern __shared__ uint4 dsm[];
   uint4* xl = dsm;  // x of the T tokens, [T][H] bf16
-  __shared__ float red[2][kSbWaves][kSbMaxT][16];
+  __shared__ float red[kSbWaves][kSbMaxT][16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int IT = I / 16;
-  const int ngroups = IT / tpw;  // a workgroup takes tpw consecutive tiles of one slot
-  const int slot = blockIdx.x / ngroups, t0 = (blockIdx.x % ngroups) * tpw;
+  const int slot = blockIdx.x / IT, t = blockIdx.x % IT;
   const bool sh_slot = slot == umax;  // the last slot: the shared expert
 
   // x of every token, in flight while the plan is read (a slot's tokens are
@@ -182,70 +179,57 @@ __global__ __launch_bounds__(kSbThreads) void k_small_gateup(
 
   // waves 0..3: gate tile t, waves 4..7: up tile t + I/16; wave w & 3 takes
   // chunks w&3, (w&3)+4, ...  Loads are unconditional (chunk index clamped,
-  // surplus results unused).  The first batch of the next tile's loads is
-  // issued before the current tile's reduction.
+  // surplus results unused).
   constexpr int WPT = kSbWaves / 2;
   const int c_first = wv % WPT;
-  auto tile_of = [&](int t) { return wv < WPT ? t : t + IT; };
+  const int tile = wv < WPT ? t : t + IT;
   FullBlock f[kSbBatch];
-  auto load_batch = [&](int tile, int c0) __attribute__((always_inline)) {
+  auto load_batch = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kSbBatch; ++i) f[i] = load_full(m, tile, min(c0 + WPT * i, nfull - 1), lane);
   };
-  load_batch(tile_of(t0), c_first);
+  load_batch(c_first);
   stage_store(xr, T * (H / 8), xl);
   __syncthreads();
-  for (int ti = 0; ti < tpw; ++ti) {
-    const int t = t0 + ti, tile = tile_of(t);
-    float acc[kSbMaxT];
+  float acc[kSbMaxT];
 #pragma unroll
-    for (int i = 0; i < kSbMaxT; ++i) acc[i] = 0.f;
-    auto apply = [&](const Rebuilt& rb, int c, bool tail) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < kSbMaxT; ++i)
-        if (sb_choice(w0, w1, i) >= 0) {
-          const uint4* xt = xl + (size_t)i * (H / 8);
-          acc[i] += tail ? gemv_tail_rebuilt(rb, c, lane, xt) : gemv_rebuilt(rb, c, lane, xt);
-        }
-    };
-#pragma unroll
-    for (int i = 0; i < kSbBatch; ++i) {
-      const int c = c_first + WPT * i;
-      if (c < nfull) apply(rebuild_full(f[i]), c, false);
-    }
-    for (int c0 = c_first + WPT * kSbBatch; c0 < nfull; c0 += kSbBatch * WPT) {
-      load_batch(tile, c0);
-#pragma unroll
-      for (int i = 0; i < kSbBatch; ++i) {
-        const int c = c0 + WPT * i;
-        if (c < nfull) apply(rebuild_full(f[i]), c, false);
-      }
-    }
-    if ((G & 1) && c_first == nfull % WPT) apply(rebuild_tail(m, tile, nfull, lane), nfull, true);
-    if (ti + 1 < tpw) load_batch(tile_of(t + 1), c_first);
-    // reduction buffers alternate between tiles: a buffer is written again
-    // only after the next tile's barrier, which follows every read of it
-    const int p = ti & 1;
+  for (int i = 0; i < kSbMaxT; ++i) acc[i] = 0.f;
+  auto apply = [&](const Rebuilt& rb, int c, bool tail) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kSbMaxT; ++i)
       if (sb_choice(w0, w1, i) >= 0) {
-        const float v = sum_quarters(acc[i]);
-        if (lane < 16) red[p][wv][i][lane] = v;
+        const uint4* xt = xl + (size_t)i * (H / 8);
+        acc[i] += tail ? gemv_tail_rebuilt(rb, c, lane, xt) : gemv_rebuilt(rb, c, lane, xt);
       }
-    __syncthreads();
-    if (tid < 16 * T) {
-      const int tok = tid >> 4, r = tid & 15;
-      const int j = (int)(int8_t)((((tok < 4) ? jw.x : jw.y) >> (8 * (tok & 3))) & 0xFFu);
-      if (j >= 0) {
-        float g = 0.f, u = 0.f;
+  };
+  for (int c0 = c_first; c0 < nfull; c0 += kSbBatch * WPT) {
+    if (c0 != c_first) load_batch(c0);
 #pragma unroll
-        for (int w = 0; w < WPT; ++w) {
-          g += red[p][w][tok][r];
-          u += red[p][WPT + w][tok][r];
-        }
-        const float silu = g / (1.f + expf(-g));
-        h_ws[((size_t)tok * (k + 1) + j) * I + 16 * t + r] = f32_to_bf16_bits(silu * u);
+    for (int i = 0; i < kSbBatch; ++i) {
+      const int c = c0 + WPT * i;
+      if (c < nfull) apply(rebuild_full(f[i]), c, false);
+    }
+  }
+  if ((G & 1) && c_first == nfull % WPT) apply(rebuild_tail(m, tile, nfull, lane), nfull, true);
+#pragma unroll
+  for (int i = 0; i < kSbMaxT; ++i)
+    if (sb_choice(w0, w1, i) >= 0) {
+      const float v = sum_quarters(acc[i]);
+      if (lane < 16) red[wv][i][lane] = v;
+    }
+  __syncthreads();
+  if (tid < 16 * T) {
+    const int tok = tid >> 4, r = tid & 15;
+    const int j = (int)(int8_t)((((tok < 4) ? jw.x : jw.y) >> (8 * (tok & 3))) & 0xFFu);
+    if (j >= 0) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) {
+        g += red[w][tok][r];
+        u += red[WPT + w][tok][r];
       }
+      const float silu = g / (1.f + expf(-g));
+      h_ws[((size_t)tok * (k + 1) + j) * I + 16 * t + r] = f32_to_bf16_bits(silu * u);
     }
   }
 }
@@ -402,13 +386,10 @@ hipError_t small_launch(const SmallPlan& p, const float* logits, const uint16_t*
   hipError_t err = launch("k_small_route", fn, dim3(1), dim3(kSbThreads), 0, stream, logits, T, E, k, p.umax,
                           has_shared, plan_ws, jt_ws, ids_ws, w_ws, ids_out, w_out);
   if (err != hipSuccess) return err;
-  // tiles per gate/up workgroup: as many as keep at least kSbMinGroups workgroups
   const int slots = p.umax + has_shared, IT = I / 16;
-  int tpw = 1;
-  while (tpw < kSbMaxTilesPerGroup && IT % (2 * tpw) == 0 && slots * (IT / (2 * tpw)) >= kSbMinGroups) tpw *= 2;
-  err = launch("k_small_gateup", (const void*)&k_small_gateup, dim3(slots * (IT / tpw)), dim3(kSbThreads),
-               p.lds_gateup, stream, x, T, k, H, I, p.umax, tpw, gu_q, gu_s, gu_b, sh_gu_q, sh_gu_s, sh_gu_b,
-               (const int32_t*)plan_ws, (const uint2*)jt_ws, h_ws);
+  err = launch("k_small_gateup", (const void*)&k_small_gateup, dim3(slots * IT), dim3(kSbThreads), p.lds_gateup,
+               stream, x, T, k, H, I, p.umax, gu_q, gu_s, gu_b, sh_gu_q, sh_gu_s, sh_gu_b, (const int32_t*)plan_ws,
+               (const uint2*)jt_ws, h_ws);
   if (err != hipSuccess) return err;
   err = launch("k_small_down", (const void*)&k_small_down, dim3((H / 16) * p.nsplit), dim3(kSbDownThreads),
                p.lds_down, stream, T, k, H, I, p.umax, has_shared, p.nsplit, dn_q, dn_s, dn_b, sh_dn_q, sh_dn_s,
