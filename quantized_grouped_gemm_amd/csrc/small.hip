@@ -391,6 +391,15 @@ hipError_t small_launch(const SmallPlan& p, const float* logits, const uint16_t*
                stream, x, T, k, H, I, p.umax, gu_q, gu_s, gu_b, sh_gu_q, sh_gu_s, sh_gu_b, (const int32_t*)plan_ws,
                (const uint2*)jt_ws, h_ws);
   if (err != hipSuccess) return err;
+  // the down kernel stages up to kSbHPieces * 16 bytes per thread of h in LDS
+  // (96 KB): raise its dynamic LDS limit once
+  static const hipError_t lds_err = hipFuncSetAttribute((const void*)&k_small_down,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                        kSbHPieces * kSbDownThreads * 16);
+  if (lds_err != hipSuccess) {
+    note_hip_error(lds_err, "hipFuncSetAttribute(k_small_down)");
+    return lds_err;
+  }
   err = launch("k_small_down", (const void*)&k_small_down, dim3((H / 16) * p.nsplit), dim3(kSbDownThreads),
                p.lds_down, stream, T, k, H, I, p.umax, has_shared, p.nsplit, dn_q, dn_s, dn_b, sh_dn_q, sh_dn_s,
                sh_dn_b, (const int32_t*)plan_ws, (const uint2*)jt_ws, (const float*)w_ws, (const uint16_t*)h_ws,

@@ -112,6 +112,7 @@ def test_small_batch_deterministic(decode_model):
     (7, 8, 1, 256, 128, False),     # more rows than distinct experts can be
     (2, 1024, 64, 256, 128, True),  # the largest expert count and top-k
     (8, 128, 6, 1024, 640, True),   # other sizes, eight rows
+    (8, 64, 11, 2048, 512, True),   # the largest staged h: 8 x 12 x 512 values, 96 KB of LDS
 ])
 def test_small_batch_shapes(T, E, k, H, I, shared):
     w = W.custom(70 + T, T, E, k, H, I, ffn=True)
