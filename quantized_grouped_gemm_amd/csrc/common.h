@@ -223,6 +223,7 @@ struct GemmArgs {
   const int32_t* blocks;      // block map; null: dense BM-row blocks over A rows of expert 0
   const int32_t* num_blocks;  // device count of block-map entries
   int max_blocks;             // entries blocks[] holds (the launch grid's bound)
+  const int32_t* order;       // non-null: routed task i takes block-map entry order[i] (a permutation)
   uint16_t* Y;                // output, row stride ldy
   int ldy;
   const int32_t* perm;        // kEpiScale; null: row p goes to row p with weight 1
@@ -274,6 +275,7 @@ __device__ __forceinline__ GemmArgs gemm_dense(const GemmArgs& a) {
   d.gather = nullptr;
   d.blocks = nullptr;
   d.num_blocks = nullptr;
+  d.order = nullptr;
   d.Y = a.dY;
   d.perm = nullptr;
   d.topk_w = nullptr;
@@ -336,8 +338,9 @@ hipError_t small_launch(const SmallPlan& p, const float* logits, const uint16_t*
                         uint16_t* out, void* workspace, hipStream_t stream);
 
 struct FfnPlan {
-  // workspace: routed h [T*k][I], shared h [T][I], routed terms [T*k][H], shared term [T][H]
-  size_t ws_h, ws_hs, ws_dw, ws_dsh, ws_bytes;
+  // workspace: routed h [T*k][I], shared h [T][I], routed terms [T*k][H], shared term [T][H],
+  // task order of the routed blocks [T*k]
+  size_t ws_h, ws_hs, ws_dw, ws_dsh, ws_order, ws_bytes;
   int bm_shared;                        // dense block height of the shared expert's gate+up
   int bm_shared_dn;                     // ... and of its down projection
 };

@@ -59,6 +59,39 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const uint16_t* __r
   *(uint4*)(out + (size_t)t * H + c8) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Task order of the routed blocks for the tall-block kernels: taller blocks
+// (more filled 32-row tiles) first, so that the last workgroups a launch
+// dispatches are the short tail blocks and the GPU does not idle behind a few
+// full-length ones.  Blocks are independent, so any order gives the same
+// outputs; inside a class the order comes from LDS atomics.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderClasses = 9;  // 8 - (filled 32-row tiles) for 1..8 tiles; 8: malformed entries
+
+__global__ __launch_bounds__(kOrderThreads) void k_block_order(const int32_t* __restrict__ blocks,
+                                                               const int32_t* __restrict__ num_blocks, int max_blocks,
+                                                               int32_t* __restrict__ order) {
+  __shared__ int cnt[kOrderClasses], base[kOrderClasses];
+  const int tid = threadIdx.x;
+  const int nb = min(*num_blocks, max_blocks);
+  if (tid < kOrderClasses) cnt[tid] = 0;
+  __syncthreads();
+  auto cls = [&](int b) {
+    const int rows = blocks[4 * b + 2];
+    return rows >= 1 ? 8 - min(8, (rows + 31) >> 5) : 8;
+  };
+  for (int b = tid; b < nb; b += kOrderThreads) atomicAdd(&cnt[cls(b)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int c = 0; c < kOrderClasses; ++c) {
+      base[c] = run;
+      run += cnt[c];
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < nb; b += kOrderThreads) order[atomicAdd(&base[cls(b)], 1)] = b;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 FfnPlan ffn_plan(int T, int H, int I, int k, bool shared) {
@@ -68,7 +101,8 @@ FfnPlan ffn_plan(int T, int H, int I, int k, bool shared) {
   p.ws_hs = align256(A * I * 2);
   p.ws_dw = p.ws_hs + (shared ? align256((size_t)T * I * 2) : 0);
   p.ws_dsh = p.ws_dw + align256(A * H * 2);
-  p.ws_bytes = p.ws_dsh + (shared ? align256((size_t)T * H * 2) : 0);
+  p.ws_order = p.ws_dsh + (shared ? align256((size_t)T * H * 2) : 0);
+  p.ws_bytes = p.ws_order + align256((2 * A + 1) * 4);  // >= moe_max_blocks for any block height
   // dense block height of the shared expert: as for one expert holding all T rows
   int bm = 16;
   while (bm < 128 && bm < (5LL * T + 3) / 4) bm <<= 1;
@@ -98,6 +132,15 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   // kernels that take one); otherwise they are launches of their own.
   const bool fuse = shared && BM >= 64;
 
+  // 0. tall-block launches take the routed blocks tallest first
+  int32_t* order = nullptr;
+  if (BM >= 64 && max_blocks > 0) {
+    order = (int32_t*)(ws + p.ws_order);
+    hipError_t oerr = launch("k_block_order", (const void*)&k_block_order, dim3(1), dim3(kOrderThreads), 0, stream,
+                             blocks, num_blocks, max_blocks, order);
+    if (oerr != hipSuccess) return oerr;
+  }
+
   // 1. routed gate+up with SwiGLU (+ shared gate+up)
   GemmArgs g{};
   g.X = X;
@@ -113,6 +156,7 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   g.gather = perm;
   g.blocks = blocks;
   g.num_blocks = num_blocks;
+  g.order = order;
   g.Y = h;
   g.ldy = I;
   if (fuse) {
@@ -138,6 +182,7 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
     s.gather = nullptr;
     s.blocks = nullptr;
     s.num_blocks = nullptr;
+    s.order = nullptr;
     s.Y = hs;
     err = gemm_launch(s, kEpiSwiglu, p.bm_shared, sh_blocks, stream);
     if (err != hipSuccess) return err;
@@ -158,6 +203,7 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   d.gather = nullptr;
   d.blocks = blocks;
   d.num_blocks = num_blocks;
+  d.order = order;
   d.Y = Dw;
   d.ldy = H;
   d.perm = perm;

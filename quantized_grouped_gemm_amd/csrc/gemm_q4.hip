@@ -128,8 +128,10 @@ __device__ __forceinline__ bool gemm_task_entry(const GemmArgs& a0, int BM, int 
     row0 = blk * BM;
     rows = min(BM, A - row0);
   } else {
-    const int cb = min(blk, max(a0.max_blocks, 1) - 1);
+    const int cap = max(a0.max_blocks, 1) - 1;
+    int cb = min(blk, cap);
     nb = *a0.num_blocks;
+    if (a0.order) cb = min(max(a0.order[cb], 0), cap);  // past the count: unwritten, never used
     e = a0.blocks[4 * cb + 0];
     row0 = a0.blocks[4 * cb + 1];
     rows = min(a0.blocks[4 * cb + 2], BM);
