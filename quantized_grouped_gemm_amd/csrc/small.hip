@@ -22,12 +22,13 @@
 //                    the shared expert).  The grid holds min(E, T*k) routed
 //                    slots; those past the distinct-expert count end at once,
 //                    so nothing waits on the host.
-//   k_small_down     workgroup (16-row tile of H, half of the slots): every
-//                    down block rebuilt once and applied to the h of each token
-//                    that chose the slot's expert, times its routing weight (1
-//                    for the shared expert); with two halves, fp32 partial sums
-//                    that k_small_combine adds in a fixed order, so that all
-//                    CUs take part and the result is the same run after run.
+//   k_small_down     workgroup (16-row tile of H, half of the slots; all of
+//                    them below kSbSplitSlots slots): every down block rebuilt
+//                    once and applied to the h of each token that chose the
+//                    slot's expert, times its routing weight (1 for the shared
+//                    expert); with two halves, fp32 partial sums that
+//                    k_small_combine adds in a fixed order, so that all CUs
+//                    take part and the result is the same run after run.
 // The plan a kernel reads (counts, expert ids, choice words, weights) is the
 // same for every lane of a wave: it is read with uniform loads into scalar
 // registers, and the branches on it are scalar.
