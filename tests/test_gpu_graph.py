@@ -113,3 +113,50 @@ def test_graph_decode_step():
 
     g = _capture(run)
     _check_replays(g, set_inputs, run, [lambda: host(bufs["out"]).copy(), lambda: host(bufs["topk_ids"]).copy()])
+
+
+def _ffn_weights(p):
+    return (q.prepack(dev(p.gu_q), dev(p.gu_s), dev(p.gu_b)), q.prepack(dev(p.dn_q), dev(p.dn_s), dev(p.dn_b)),
+            q.prepack(dev(p.sh_gu_q), dev(p.sh_gu_s), dev(p.sh_gu_b)),
+            q.prepack(dev(p.sh_dn_q), dev(p.sh_dn_s), dev(p.sh_dn_b)))
+
+
+@pytest.mark.parametrize("T", [2, 5])
+def test_graph_small_batch(T):
+    # the few-token layer: routing, distinct-expert plan, gate/up, split down
+    # and combine, all on the device
+    w = W.custom(83, T, 64, 4, 256, 128, ffn=True)
+    p = W.make_problem(w)
+    gu, dn, sg, sd = _ffn_weights(p)
+    lg, x = dev(p.logits), dev(p.X)
+    bufs = q.alloc_small(T, w.E, w.k, w.K, w.N, True)
+
+    def run():
+        q.small_batch_ffn(lg, x, w.k, gu, dn, sg, sd, bufs=bufs, stream=torch.cuda.current_stream())
+
+    def set_inputs(r):
+        lg.copy_(dev(W.gen_logits(83, T, w.E, step=r + 1)))
+        x.copy_(dev(W.gen_acts(83, T, w.K, step=r + 1)))
+
+    g = _capture(run)
+    _check_replays(g, set_inputs, run, [lambda: host(bufs["out"]).copy(), lambda: host(bufs["topk_ids"]).copy()])
+
+
+def test_graph_chunked_prefill():
+    # route + FFN per chunk (with the tallest-first block order of 64-row blocks)
+    w = W.custom(84, 300, 32, 4, 256, 128, ffn=True)
+    p = W.make_problem(w)
+    gu, dn, sg, sd = _ffn_weights(p)
+    lg, X = dev(p.logits), dev(p.X)
+    bufs = q.alloc_chunked(w.T, 128, w.K, w.N, w.E, w.k, 64, True)
+
+    def run():
+        q.prefill_ffn_chunked(lg, X, w.k, gu, dn, sg, sd, bufs=bufs, stream=torch.cuda.current_stream())
+
+    def set_inputs(r):
+        lg.copy_(dev(W.gen_logits(84, w.T, w.E, step=r + 1)))
+        X.copy_(dev(W.gen_acts(84, w.T, w.K, step=r + 1)))
+
+    g = _capture(run)
+    _check_replays(g, set_inputs, run, [lambda: host(bufs["out"])[: w.T].copy(),
+                                        lambda: host(bufs["topk_ids"])[: w.T].copy()])
