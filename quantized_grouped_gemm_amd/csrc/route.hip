@@ -121,11 +121,15 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    // all NW counters first (independent LDS reads), then the bases
+    int c[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c[w] = cnt[w * E + e];
     int run = 0;
+#pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w * E + e];
       cnt[w * E + e] = (uint16_t)run;
-      run += c;
+      run += c[w];
     }
     chunk_counts[(size_t)chunk * E + e] = run;
   }
@@ -252,12 +256,21 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
     }
   }
 
-  // ---- counts, offsets, block offsets
-  int total;
-  const int off = block_exclusive_scan(tid < E ? cnt_e : 0, scratch, &total);
+  // ---- counts, offsets, block offsets.  Below 2^16 assignments both scans
+  // run as one over (count | blocks << 16): the block total stays below
+  // E + A / BM < 2^15, so neither field carries into the other.
+  int total, nb_total, off, boff;
   const int nb = tid < E ? (cnt_e + BM - 1) / BM : 0;
-  int nb_total;
-  const int boff = block_exclusive_scan(nb, scratch, &nb_total);
+  if (A < 65536) {
+    const int pk = block_exclusive_scan(tid < E ? cnt_e | (nb << 16) : 0, scratch, &total);
+    off = pk & 0xFFFF;
+    boff = pk >> 16;
+    nb_total = total >> 16;
+    total &= 0xFFFF;
+  } else {
+    off = block_exclusive_scan(tid < E ? cnt_e : 0, scratch, &total);
+    boff = block_exclusive_scan(nb, scratch, &nb_total);
+  }
   if (tid < E) {
     counts[tid] = cnt_e;
     offsets[tid] = off;
@@ -290,12 +303,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
   // ---- small inputs: the scatter too (chunk bases were written to LDS above,
   // before the barriers of the scans)
   if (fuse_scatter) {
+    const int ktpc = k * tpc;
 #pragma unroll
     for (int i = 0; i < kFusedPerThread; ++i) {
       const int a = tid + i * kScanThreads;
       if (a < A) {
         const int e = pf_e[i];
-        const int c = (a / k) / tpc;
+        const int c = a / ktpc;  // the chunk of token a / k
         const int p = offs_s[e] + cb_s[c * E + e] + pf_r[i];
         if (p >= 0 && p < A) perm[p] = a;
         inv_perm[a] = p;
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids
   const int a = blockIdx.x * 256 + threadIdx.x;
   if (a >= A) return;
   const int e = ids[a];
-  const int c = (a / k) / tpc;
+  const int c = a / (k * tpc);  // the chunk of token a / k
   const int p = offsets[e] + chunk_base[(size_t)c * E + e] + local_rank[a];
   if (p >= 0 && p < A) perm[p] = a;
   inv_perm[a] = p;
