@@ -60,6 +60,8 @@ ROUTE_CASES = [
     ("ties", 300, 256, 8), ("ties", 77, 16, 4), ("hot", 1000, 256, 8), ("hot", 50, 64, 1),
     ("constant", 40, 32, 5), ("normal", 3, 1, 1), ("normal", 33, 8, 8), ("normal", 129, 1024, 64),
     ("normal", 200, 300, 6), ("normal", 5, 256, 8), ("normal", 1000, 128, 3), ("normal", 2500, 512, 16),
+    # T*k on both sides of 2^16: the scan kernel's packed single scan stops at 65535
+    ("normal", 13107, 64, 5), ("normal", 8192, 256, 8),
 ]
 
 
