@@ -268,7 +268,9 @@ size_t moe_prefill_ffn_chunked_workspace_bytes(int T, int chunk_tokens, int H, i
  * Errors: MOEQ4_ERR_NULL, MOEQ4_ERR_SHAPE (also chunk_tokens not a positive
  *         multiple of 4), MOEQ4_ERR_UNSUPPORTED, MOEQ4_ERR_ALIGN,
  *         MOEQ4_ERR_WORKSPACE, MOEQ4_ERR_HIP; every check runs before the first
- *         chunk is enqueued. */
+ *         chunk is enqueued.  MOEQ4_ERR_HIP (a kernel launch the runtime
+ *         refused) stops the sequence at that chunk: the chunks before it are
+ *         already enqueued and write their rows of out. */
 int moe_prefill_ffn_chunked_q4(const float* logits, const uint16_t* X, int T, int H, int I, int E, int k,
                                const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
                                const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
