@@ -1098,7 +1098,7 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 8, kEpiPlain),
     MOEQ4_GEMM_VARIANT(32, 2, true, 3, 0, 8, kEpiPlain),
     MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiPlain),
     // FFN: gate+up with SwiGLU, down scaled by the routing weight, shared down + combine
     MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiSwiglu),
     MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiSwiglu),
@@ -1123,7 +1123,7 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 8, kEpiPlain),
     MOEQ4_GEMM_VARIANT(32, 2, true, 4, 0, 8, kEpiPlain),
     MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiPlain),
+    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiPlain),
     MOEQ4_GEMM_W32(64, 2, 2, 8, kEpiPlain),
     MOEQ4_GEMM_W32(128, 1, 3, 8, kEpiPlain),
     MOEQ4_GEMM_W32(128, 1, 4, 8, kEpiPlain),
