@@ -11,12 +11,13 @@
 
     python -m quantized_grouped_gemm_amd.profiling traffic --kernel REGEX --workload NAME
             --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-mib M
-            --cmd CMD --out profiles/traffic.json
+            [--per-step N] --cmd CMD --out profiles/traffic.json
         Averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernels
         matching REGEX, scales each by (known bytes / counted bytes) of the
-        copy kernel, and records the HBM bytes per launch together with a hash
-        of the kernel source, so that a later change to the kernel makes the
-        figure stale.
+        copy kernel, and records the HBM bytes per launch (times N when one
+        step is N dispatches of the matching kernels, each once per step)
+        together with a hash of the kernel sources, so that a later change to
+        a kernel makes the figure stale.
 
 This module only reads CSV files and launches one torch copy; it is not on
 the compute path.
@@ -32,7 +33,7 @@ import re
 import sys
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("gemm_q4.hip", "common.h")
+KERNEL_SOURCES = ("gemm_q4.hip", "common.h", "ffn.hip", "decode.hip", "gemv.h")
 
 
 def kernel_source_hash(files=KERNEL_SOURCES) -> str:
@@ -98,7 +99,8 @@ def _traffic(a) -> None:
         "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": [n1, n2],
         "copy_mib": a.copy_mib, "copy_fetch_kib": cf, "copy_write_kib": cw,
         "fetch_scale": f_fac, "write_scale": w_fac,
-        "bytes_per_launch": kf * 1024.0 * f_fac + kw * 1024.0 * w_fac,
+        "dispatches_per_step": a.per_step,
+        "bytes_per_launch": a.per_step * (kf * 1024.0 * f_fac + kw * 1024.0 * w_fac),
         "command": a.cmd,
     }
     d = {}
@@ -133,6 +135,7 @@ def main(argv=None):
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--copy-regex", default="elementwise")
+    t.add_argument("--per-step", type=int, default=1, help="dispatches of the matching kernels per step")
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
     a = ap.parse_args(argv)
