@@ -64,6 +64,10 @@ def lib():
                                            _u8p, _u16p, _u16p, _u8p, _u16p, _u16p,
                                            _vp, _vp, _vp, _vp, _vp, _vp,
                                            _i32p, _f64p, _i32p, _int, _f64p]
+        L.oracle_expert_ffn_grouped_q4.argtypes = [_u16p, _int, _int, _int, _int, _int,
+                                                   _u8p, _u16p, _u16p, _u8p, _u16p, _u16p,
+                                                   _vp, _vp, _vp, _vp, _vp, _vp,
+                                                   _i32p, _f64p, _f64p]
         L.oracle_num_threads.restype = _int
         _lib = L
     return _lib
@@ -186,4 +190,27 @@ def expert_ffn_q4(X, ids, w, gu_q, gu_s, gu_b, dn_q, dn_s, dn_b, sh=None, tokens
         *[_ptr(a) for a in shp],
         np.ascontiguousarray(ids, np.int32), np.ascontiguousarray(w, np.float64), tokens,
         len(tokens), out), "oracle_expert_ffn_q4")
+    return out
+
+
+def expert_ffn_grouped_q4(X, ids, w, gu_q, gu_s, gu_b, dn_q, dn_s, dn_b, sh=None) -> np.ndarray:
+    """out [T, H] float64 for every token, expert by expert: each expert's
+    matrices are rebuilt once and applied to all rows routed to it.  Bit for
+    bit the same values as expert_ffn_q4 (same term order), in a fraction of
+    its time at full size."""
+    X = np.ascontiguousarray(X, np.uint16)
+    T, H = X.shape
+    E, I2, _ = gu_q.shape
+    I = I2 // 2
+    k = ids.shape[1]
+    out = np.empty((T, H), np.float64)
+    shp = [None] * 6 if sh is None else [np.ascontiguousarray(a) for a in sh]
+    _check(lib().oracle_expert_ffn_grouped_q4(
+        X, T, H, I, E, k,
+        np.ascontiguousarray(gu_q, np.uint8), np.ascontiguousarray(gu_s, np.uint16),
+        np.ascontiguousarray(gu_b, np.uint16), np.ascontiguousarray(dn_q, np.uint8),
+        np.ascontiguousarray(dn_s, np.uint16), np.ascontiguousarray(dn_b, np.uint16),
+        *[_ptr(a) for a in shp],
+        np.ascontiguousarray(ids, np.int32), np.ascontiguousarray(w, np.float64), out),
+        "oracle_expert_ffn_grouped_q4")
     return out

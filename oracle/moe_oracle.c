@@ -352,6 +352,139 @@ int oracle_expert_ffn_q4(const uint16_t* X, int T, int H, int I, int E, int k,
   return fail ? ORC_ENOMEM : ORC_OK;
 }
 
+/* The same layer output, computed expert by expert ("dequantize, then
+ * matmul"): each expert's two matrices are rebuilt once (reading R6), then
+ * applied to every assignment routed to it, and the combine runs per token
+ * afterwards.  Every dot product and the combine take their terms in the same
+ * order as oracle_expert_ffn_q4 (kk ascending; routed terms j ascending, then
+ * the shared term), so the two functions agree bit for bit; this one rebuilds
+ * each weight once instead of once per (token, expert) and so finishes the
+ * full-size workloads in seconds.  out [T, H] fp64. */
+static void rebuild_matrix(const uint8_t* q, const uint16_t* s, const uint16_t* b, int N, int K, double* W) {
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    const uint8_t* cr = q + (size_t)n * (K / 2);
+    for (int kk = 0; kk < K; ++kk) {
+      size_t g = (size_t)n * (K / GROUP) + kk / GROUP;
+      W[(size_t)n * K + kk] = oracle_dequant_one(s[g], b[g], code_at(cr, kk));
+    }
+  }
+}
+
+/* FFN of one row x through rebuilt matrices Wgu [2I, H] and Wdn [H, I]:
+ * d = Wdn . bf16(silu(g) * u), [g; u] = Wgu . x (reading R7). */
+static void ffn_rebuilt(const double* x, int H, int I, const double* Wgu, const double* Wdn, double* gu,
+                        double* h, double* d) {
+  for (int n = 0; n < 2 * I; ++n) {
+    const double* wr = Wgu + (size_t)n * H;
+    double acc = 0.0;
+    for (int kk = 0; kk < H; ++kk) acc += x[kk] * wr[kk];
+    gu[n] = acc;
+  }
+  for (int i = 0; i < I; ++i) {
+    double gt = gu[i], up = gu[I + i];
+    double silu = gt / (1.0 + exp(-gt));
+    h[i] = bf16_value(oracle_bf16_round(silu * up));
+  }
+  for (int n = 0; n < H; ++n) {
+    const double* wr = Wdn + (size_t)n * I;
+    double acc = 0.0;
+    for (int kk = 0; kk < I; ++kk) acc += h[kk] * wr[kk];
+    d[n] = acc;
+  }
+}
+
+/* rows[r] of X through one expert's rebuilt matrices into D[dst[r]] */
+static int ffn_rows(const uint16_t* X, int H, int I, const double* Wgu, const double* Wdn, const int32_t* rows,
+                    const int32_t* dst, int nrows, double* D) {
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)H);
+    double* gu = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    if (!x || !gu || !h) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int r = 0; r < nrows; ++r) {
+      if (!x || !gu || !h) continue;
+      for (int kk = 0; kk < H; ++kk) x[kk] = bf16_value(X[(size_t)rows[r] * H + kk]);
+      ffn_rebuilt(x, H, I, Wgu, Wdn, gu, h, D + (size_t)dst[r] * H);
+    }
+    free(x);
+    free(gu);
+    free(h);
+  }
+  return fail;
+}
+
+int oracle_expert_ffn_grouped_q4(const uint16_t* X, int T, int H, int I, int E, int k,
+                                 const uint8_t* gu_q, const uint16_t* gu_s, const uint16_t* gu_b,
+                                 const uint8_t* dn_q, const uint16_t* dn_s, const uint16_t* dn_b,
+                                 const uint8_t* sh_gu_q, const uint16_t* sh_gu_s, const uint16_t* sh_gu_b,
+                                 const uint8_t* sh_dn_q, const uint16_t* sh_dn_s, const uint16_t* sh_dn_b,
+                                 const int32_t* ids, const double* w, double* out) {
+  if (T < 0 || H <= 0 || H % GROUP || I <= 0 || I % GROUP || E <= 0 || k <= 0) return ORC_EINVAL;
+  if (T > 0 && (!X || !gu_q || !gu_s || !gu_b || !dn_q || !dn_s || !dn_b || !ids || !w || !out))
+    return ORC_EINVAL;
+  const long A = (long)T * k;
+  for (long a = 0; a < A; ++a)
+    if (ids[a] < 0 || ids[a] >= E) return ORC_EINVAL;
+  int has_shared = sh_gu_q && sh_gu_s && sh_gu_b && sh_dn_q && sh_dn_s && sh_dn_b;
+  double* Wgu = (double*)malloc(sizeof(double) * 2 * (size_t)I * H);
+  double* Wdn = (double*)malloc(sizeof(double) * (size_t)H * I);
+  double* D = (double*)malloc(sizeof(double) * (size_t)(A > 0 ? A : 1) * H);          /* routed terms */
+  double* Dsh = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * H);        /* shared term */
+  int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A > T ? A : (T > 0 ? T : 1)));
+  int32_t* dst = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A > T ? A : (T > 0 ? T : 1)));
+  int fail = !Wgu || !Wdn || !D || !Dsh || !rows || !dst;
+  for (int e = 0; e < E && !fail && A > 0; ++e) {
+    int n = 0;
+    for (long a = 0; a < A; ++a)
+      if (ids[a] == e) {
+        rows[n] = (int32_t)(a / k);
+        dst[n] = (int32_t)a;
+        ++n;
+      }
+    if (n == 0) continue;
+    const size_t gm = (size_t)e * 2 * I, dm = (size_t)e * H;
+    rebuild_matrix(gu_q + gm * (H / 2), gu_s + gm * (H / GROUP), gu_b + gm * (H / GROUP), 2 * I, H, Wgu);
+    rebuild_matrix(dn_q + dm * (I / 2), dn_s + dm * (I / GROUP), dn_b + dm * (I / GROUP), H, I, Wdn);
+    fail |= ffn_rows(X, H, I, Wgu, Wdn, rows, dst, n, D);
+  }
+  if (!fail && has_shared && T > 0) {
+    for (int t = 0; t < T; ++t) rows[t] = dst[t] = t;
+    rebuild_matrix(sh_gu_q, sh_gu_s, sh_gu_b, 2 * I, H, Wgu);
+    rebuild_matrix(sh_dn_q, sh_dn_s, sh_dn_b, H, I, Wdn);
+    fail |= ffn_rows(X, H, I, Wgu, Wdn, rows, dst, T, Dsh);
+  }
+  if (!fail) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+      double* o = out + (size_t)t * H;
+      for (int n = 0; n < H; ++n) o[n] = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const double wj = w[(size_t)t * k + j];
+        const double* d = D + ((size_t)t * k + j) * H;
+        for (int n = 0; n < H; ++n) o[n] += wj * d[n];
+      }
+      if (has_shared) {
+        const double* d = Dsh + (size_t)t * H;
+        for (int n = 0; n < H; ++n) o[n] += 1.0 * d[n];
+      }
+    }
+  }
+  free(Wgu);
+  free(Wdn);
+  free(D);
+  free(Dsh);
+  free(rows);
+  free(dst);
+  return fail ? ORC_ENOMEM : ORC_OK;
+}
+
 int oracle_num_threads(void) {
   int n = 1;
 #pragma omp parallel
