@@ -3,7 +3,9 @@
 Default (the prefill-chunk workload: T=512 tokens, E=256 experts, top-8,
 K=2048 -> N=512, group-64 affine 4-bit weights): one step = moe_route (top-k,
 histogram, scan, block map, scatter) followed by moe_grouped_gemm_q4 over the
-routed rows.  Other workloads:
+routed rows; the same JSON line also carries, under "c3", the expert-FFN
+step at T=4096 below (the metric is quoted at T=512 and T=4096), with its own
+roofline and CPU baseline (--no-c3 leaves it out).  Other workloads:
   --workload 4   the same step at T=16384 with Zipf-skewed routing
   --workload 3   one step = moe_route + moe_expert_ffn_q4 (gate+up, SwiGLU,
                  down, weighted combine, shared expert) at T=4096, H=2048, I=512
@@ -391,17 +393,17 @@ def bench_ffn(args, torch, q, W, w, d):
     })
     if not args.no_cpu_baseline:
         import oracle
-        ids, wts = oracle.topk_softmax(p.logits, k)
         sh = (p.sh_gu_q, p.sh_gu_s, p.sh_gu_b, p.sh_dn_q, p.sh_dn_s, p.sh_dn_b)
-        ntok = 192
-        tokens = np.arange(ntok, dtype=np.int32)
         t0 = time.perf_counter()
-        oracle.expert_ffn_q4(p.X, ids, wts, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b, sh=sh, tokens=tokens)
+        ids, wts = oracle.topk_softmax(p.logits, k)
+        oracle.expert_ffn_grouped_q4(p.X, ids, wts, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b, sh=sh)
         ts = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": ffn_flops(ntok, H, I, k, True) / ts / 1e12, "unit": "TFLOP/s",
+        print(f"cpu baseline (expert FFN): {ts:.2f} s", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = {"value": flops / ts / 1e12, "unit": "TFLOP/s",
                                "cores": oracle.num_threads(), "kind": "oracle",
-                               "sample": f"the FFN of the first {ntok} tokens of the same batch (all 9 experts "
-                                         f"per token), {ts:.2f} s"}
+                               "sample": f"the whole step of the same workload (top-k + softmax, then every "
+                                         f"token's FFN expert by expert, shared expert included), one run, "
+                                         f"{ts:.2f} s"}
     return out
 
 
@@ -468,6 +470,41 @@ def bench_crossover(args, torch, q, W, d):
 
 
 # ------------------------------------------------------------------ ablations
+def unfused_layout(counts, offsets, perm, k, T):
+    """Row sources of the unfused arm's batched GEMM: per expert, its routed
+    tokens (perm order) padded with row T (a zero row) to a common multiple of 16."""
+    E = len(counts)
+    mmax = int(counts.max()) if E else 0
+    mpad = max(16, -(-mmax // 16) * 16)
+    src_row = np.full((E, mpad), T, np.int64)
+    for e in range(E):
+        c = int(counts[e])
+        src_row[e, :c] = perm[offsets[e]: offsets[e] + c] // k
+    return src_row
+
+
+def unfused_gemm(torch, Wbf, Xz, src_row):
+    """The unfused arm's GEMM: every expert's rebuilt bf16 weights [E, N, K]
+    (from moe_dequant_q4) times its gathered rows, one vendor batched GEMM
+    (torch.bmm -> hipBLASLt) with the right operand contiguous.  [E, N, mpad] bf16."""
+    xt = Xz[src_row].transpose(1, 2).contiguous()            # [E, K, mpad]
+    return torch.bmm(Wbf.view(torch.bfloat16), xt)
+
+
+def host_block_map(counts, bm):
+    """The host-synced arm's block map, built on the CPU from the expert counts
+    copied back from the GPU: int32 [nb * 4] entries {expert, first sorted row,
+    rows, block index} and nb."""
+    cnt = np.asarray(counts, np.int64)
+    E = len(cnt)
+    nbe = (cnt + bm - 1) // bm
+    offs = np.concatenate([[0], np.cumsum(cnt)])
+    e_of = np.repeat(np.arange(E), nbe)
+    j = np.arange(int(nbe.sum())) - np.repeat(np.cumsum(nbe) - nbe, nbe)
+    blk = np.stack([e_of, offs[e_of] + j * bm, np.minimum(bm, cnt[e_of] - j * bm), j], 1)
+    return blk.astype(np.int32).reshape(-1), int(nbe.sum())
+
+
 def bench_ablation(args, torch, q, W, T, d):
     """The pages' two prefill mechanisms, each against its unfused alternative,
     on the single-projection shape (E=256, k=8, K=2048, N=512) at T tokens:
@@ -499,12 +536,7 @@ def bench_ablation(args, torch, q, W, T, d):
     offsets = rt["offsets"].cpu().numpy()
     perm = rt["perm"].cpu().numpy()
     mmax = int(counts.max())
-    mpad = max(16, -(-mmax // 16) * 16)
-    src_row = np.full((E, mpad), T, np.int64)   # row T of Xz is zeros
-    for e in range(E):
-        c = int(counts[e])
-        src_row[e, :c] = perm[offsets[e]: offsets[e] + c] // k
-    src_row = torch.from_numpy(src_row).to(X.device)
+    src_row = torch.from_numpy(unfused_layout(counts, offsets, perm, k, T)).to(X.device)   # row T of Xz is zeros
     Xz = torch.cat([X.view(torch.bfloat16), torch.zeros((1, K), dtype=torch.bfloat16, device=X.device)])
     Wbf = torch.empty((E, N, K), dtype=torch.int16, device=X.device)
     blocks_host = torch.empty(rt["blocks"].numel(), dtype=torch.int32).pin_memory()
@@ -528,21 +560,14 @@ def bench_ablation(args, torch, q, W, T, d):
     def unfused(i):
         q.route(logits, k, bufs=rt, stream=stream)
         q.dequant(packs[i % layers], E, N, K, out=Wbf, stream=stream)
-        xt = Xz[src_row].transpose(1, 2).contiguous()            # [E, K, mpad], right operand contiguous
-        torch.bmm(Wbf.view(torch.bfloat16), xt)                  # [E, N, mpad]
+        unfused_gemm(torch, Wbf, Xz, src_row)
 
     def hostsync(i):
         q.route(logits, k, bufs=rt, stream=stream)
-        cnt = rt["counts"].cpu().numpy().astype(np.int64)       # the CPU wait
-        bm = rt["block_rows"]
-        nbe = (cnt + bm - 1) // bm
-        offs = np.concatenate([[0], np.cumsum(cnt)])
-        e_of = np.repeat(np.arange(E), nbe)
-        j = np.arange(int(nbe.sum())) - np.repeat(np.cumsum(nbe) - nbe, nbe)
-        blk = np.stack([e_of, offs[e_of] + j * bm, np.minimum(bm, cnt[e_of] - j * bm), j], 1)
-        blk = blk.astype(np.int32).reshape(-1)
+        cnt = rt["counts"].cpu().numpy()                        # the CPU wait
+        blk, nb = host_block_map(cnt, rt["block_rows"])
         blocks_host[: blk.size] = torch.from_numpy(blk)
-        nb_host[0] = int(nbe.sum())
+        nb_host[0] = nb
         rt["blocks"][: blk.size].copy_(blocks_host[: blk.size], non_blocking=True)
         rt["num_blocks"][:1].copy_(nb_host[:1], non_blocking=True)
         q.grouped_gemm_q4(X, k, packs[i % layers], rt, Y=Y, stream=stream)
@@ -558,7 +583,7 @@ def bench_ablation(args, torch, q, W, T, d):
         e3[0].record()
         q.dequant(packs[i % layers], E, N, K, out=Wbf, stream=stream)
         e3[1].record()
-        torch.bmm(Wbf.view(torch.bfloat16), Xz[src_row].transpose(1, 2).contiguous())
+        unfused_gemm(torch, Wbf, Xz, src_row)
         e3[2].record()
         torch.cuda.synchronize()
         dq.append(e3[0].elapsed_time(e3[1]))
@@ -633,17 +658,16 @@ def bench_decode(args, torch, q, W, w, d):
         import oracle
         sh = (p.sh_gu_q, p.sh_gu_s, p.sh_gu_b, p.sh_dn_q, p.sh_dn_s, p.sh_dn_b)
         n = 20
+        inputs = [(W.gen_logits(w.cid, 1, E, s), W.gen_acts(w.cid, 1, H, s)) for s in range(n)]
         t0 = time.perf_counter()
-        for s in range(n):
-            lgs = W.gen_logits(w.cid, 1, E, s)
+        for lgs, xs1 in inputs:
             ids, wts = oracle.topk_softmax(lgs, k)
-            oracle.expert_ffn_q4(W.gen_acts(w.cid, 1, H, s), ids, wts, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s,
-                                 p.dn_b, sh=sh)
+            oracle.expert_ffn_q4(xs1, ids, wts, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b, sh=sh)
         ts = (time.perf_counter() - t0) / n
         out["cpu_baseline"] = {"value": flops / ts / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
                                "kind": "oracle",
-                               "sample": f"{n} decode steps of the same workload (input generation included), "
-                                         f"{ts * 1e3:.1f} ms each"}
+                               "sample": f"the first {n} decode steps of the same workload (inputs generated "
+                                         f"before the clock starts), {ts * 1e3:.1f} ms each"}
     return out
 
 
@@ -664,6 +688,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0,
                     help="expert-FFN workload: run the step as chunks of this many tokens (moe_prefill_ffn_chunked_q4)")
     ap.add_argument("--crossover-rows", default="", help="comma-separated T values for --crossover (default 1..8)")
+    ap.add_argument("--no-c3", action="store_true",
+                    help="default workload: leave out the expert-FFN step at T=4096 that rides in the same line")
+    ap.add_argument("--c3-steps", type=int, default=20, help="timed steps of that expert-FFN step")
     ap.add_argument("--cpu-reps", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="stop repeating the CPU oracle once this much time is spent (at least one run)")
@@ -702,6 +729,15 @@ def main():
         out = bench_ffn(args, torch, q, W, w, d)
     else:
         out = bench_gemm(args, torch, q, W, w, d)
+        if args.workload == 2 and not args.no_c3:
+            # the metric is quoted at T=512 and T=4096: the expert-FFN step at
+            # T=4096 rides in the same line, with its own roofline and baseline
+            c3 = argparse.Namespace(**vars(args))
+            c3.steps, c3.warmup, c3.block_rows, c3.chunk = args.c3_steps, min(args.warmup, 5), 0, 0
+            r = bench_ffn(c3, torch, q, W, W.WORKLOADS[3], d)
+            out["c3"] = {key: r[key] for key in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
+                                                "roofline", "ffn", "route_us", "cpu_baseline", "timing")
+                         if key in r}
     out["measured_ceilings"] = ceilings
     print(json.dumps(out), flush=True)
 

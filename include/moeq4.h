@@ -164,12 +164,9 @@ int moe_dequant_q4(const uint8_t* codes_t, const uint16_t* scales_t, const uint1
  * For every block-map entry b < *num_blocks with expert e and sorted rows
  * [r0, r0 + rows):
  *   Y[p, n] = bf16( sum_kk X[perm[p] / k, kk] * weight_e(n, kk) ),  p in [r0, r0+rows)
- * with fp32 accumulation.  Weights are rebuilt on chip, tile by tile, and never
- * written back to memory.  Blocks of up to 32 rows feed the MFMA with the codes
- * and apply each group's scale and bias to the fp32 partial sums (the weight
- * enters as scale*code + bias exactly); taller blocks rebuild every weight as
- * bf16(scale*code + bias) first.  Both agree with the row-major definition
- * within fp32 rounding of the sums and the bf16 rounding of the weights.
+ * with fp32 accumulation.  Weights are rebuilt on chip, tile by tile, as
+ * bf16(scale*code + bias) and never written back to memory; the result agrees
+ * with the definition within the fp32 rounding of the sums.
  *
  * In:  X        uint16 (bf16) [T, K]  token activations (rows gathered via perm).
  *      codes_t, scales_t, biases_t   the experts' weights [E, N, K] in the tiled
@@ -243,7 +240,7 @@ size_t moe_prefill_ffn_chunked_workspace_bytes(int T, int chunk_tokens, int H, i
                                                int block_rows, int shared);
 
 /* The routed expert FFN (+ shared expert) of a long prompt, run as a sequence
- * of bounded chunks (section "Limit scratch memory with prompt chunking": the
+ * of bounded chunks (section "Bound temporary memory with prompt chunking": the
  * temporary matrices of one chunk at a time, reused for the next, so the
  * scratch no longer grows with the prompt while the weights stay resident;
  * the output is unchanged).  For each chunk of chunk_tokens tokens (the last
@@ -286,9 +283,10 @@ int moe_prefill_ffn_chunked_q4(const float* logits, const uint16_t* X, int T, in
 size_t moe_decode_workspace_bytes(int E, int k, int H, int I, int shared);
 
 /* One batch-1 decode step of the MoE layer: routing, the selected experts'
- * FFNs and the shared expert, fused into two kernels (sections "Decode is a
- * bandwidth problem" and "Reduce intermediate and state traffic": the step is
- * bound by the weight bytes it reads; the two input projections run with their
+ * FFNs and the shared expert, fused into two kernels (sections "Decode:
+ * minimize bytes moved per token", "Optimize the single-row weight path" and
+ * "Reduce intermediate and state traffic": the step is bound by the bytes it
+ * moves, a row-parallel GEMV reads the weights; the two input projections run with their
  * gated activation, the output projection with the routing scores and the
  * shared expert's result).
  *
@@ -375,6 +373,55 @@ int moe_small_batch_ffn_q4(const float* logits, const uint16_t* x, int T, int E,
                            const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
                            int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
                            size_t ws_bytes, void* stream);
+
+/* Paths of moe_layer_ffn_q4, chosen from the number of rows T. */
+#define MOEQ4_PATH_DECODE 1     /* T = 1: moe_decode_ffn_q4 */
+#define MOEQ4_PATH_FEW_ROWS 2   /* 2 <= T <= MOEQ4_SMALL_MAX_T: moe_small_batch_ffn_q4 */
+#define MOEQ4_PATH_PREFILL 3    /* otherwise: moe_route + moe_expert_ffn_q4 */
+
+/* Which path moe_layer_ffn_q4 takes for these sizes: MOEQ4_PATH_DECODE for
+ * T = 1, MOEQ4_PATH_FEW_ROWS for 2 <= T <= MOEQ4_SMALL_MAX_T, else
+ * MOEQ4_PATH_PREFILL; a shape beyond a smaller path's limits (see those calls)
+ * takes the next one.  Negative error code when no path takes the sizes.
+ * shared: 1 when a shared expert is given, else 0. */
+int moe_layer_ffn_path(int T, int E, int k, int H, int I, int shared);
+
+/* Bytes of device scratch moe_layer_ffn_q4 needs for these sizes (that of
+ * the path it takes; 0 on invalid sizes). */
+size_t moe_layer_ffn_workspace_bytes(int T, int H, int I, int E, int k, int block_rows, int shared);
+
+/* The MoE layer from router logits to output for T tokens, with the kernels
+ * chosen from the shape (section "Optimization strategy": the runtime selects
+ * kernels by row count and shape; section "Apple silicon provides different
+ * paths for different workloads": one row is a bandwidth-bound matrix-vector
+ * product, many rows a matrix product that reuses each weight):
+ *   T = 1          the batch-1 decode step (moe_decode_ffn_q4);
+ *   2 <= T <= 8    the few-row step (moe_small_batch_ffn_q4);
+ *   otherwise      moe_route + moe_expert_ffn_q4 over all T rows, the routing
+ *                  tables held in the workspace.
+ * Every path computes, per token t:
+ *   ids[t], w[t] = top-k of logits[t] (descending, ties by ascending expert id)
+ *                  and softmax over the k selected
+ *   out[t] = bf16( sum_j w[t][j] * D_{ids[t][j]} h[t][j]  +  D_sh h_sh[t] )
+ *   h[t][j] = bf16( silu(G x_t) * (U x_t) ) with expert ids[t][j]'s gate/up rows
+ * (as moe_expert_ffn_q4; the paths differ only in fp32 summation order).
+ * In:  logits float [T, E]; X uint16 (bf16) [T, H]; weights as moe_expert_ffn_q4
+ *      (tiled layout of moe_prepack_q4; the six sh_* all given or all NULL).
+ *      block_rows  0 (default) or 16/32/64/128/256: the block height of the
+ *                  routed path (unused by the other two).
+ *      workspace   moe_layer_ffn_workspace_bytes(...) bytes, 16-byte aligned;
+ *                  no initial contents needed.
+ * Out: out uint16 (bf16) [T, H]; topk_ids int32 [T, k] and topk_w float [T, k]
+ *      (each may be NULL).
+ * Errors: those of the call the path makes (every check runs before anything
+ * is enqueued); T = 0 enqueues nothing. */
+int moe_layer_ffn_q4(const float* logits, const uint16_t* X, int T, int H, int I, int E, int k,
+                     const uint8_t* gu_codes_t, const uint16_t* gu_scales_t, const uint16_t* gu_biases_t,
+                     const uint8_t* dn_codes_t, const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                     const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t, const uint16_t* sh_gu_biases_t,
+                     const uint8_t* sh_dn_codes_t, const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                     int block_rows, int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
+                     size_t ws_bytes, void* stream);
 
 /* Measured MFMA ceiling (measurement only, not a step of the method): each of
  * `workgroups` workgroups of 4 waves issues iters x 8 independent

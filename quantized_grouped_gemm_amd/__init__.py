@@ -30,6 +30,9 @@ MOEQ4_ERR_HIP = -6
 MOEQ4_MAX_EXPERTS = 1024
 MOEQ4_MAX_TOPK = 64
 MOEQ4_SMALL_MAX_T = 8
+MOEQ4_PATH_DECODE = 1
+MOEQ4_PATH_FEW_ROWS = 2
+MOEQ4_PATH_PREFILL = 3
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -58,6 +61,9 @@ SIGNATURES = {
     "moe_small_batch_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_calibrate_mfma": (_i, [_i, _i, _vp, _vp]),
     "moe_dequant_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "moe_layer_ffn_path": (_i, [_i, _i, _i, _i, _i, _i]),
+    "moe_layer_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "moe_layer_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_i, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -396,4 +402,53 @@ def expert_ffn(X, k: int, rt, gu, dn, sh_gu=None, sh_dn=None, bufs=None, stream=
     moe_expert_ffn_q4(X, T, H, I, E, k, *gu, *dn, *sg, *sd, rt["topk_w"], rt["perm"], rt["blocks"],
                       rt["num_blocks"], rt["max_blocks"], rt["block_rows"], b["out"], b["workspace"],
                       b["ws_bytes"], stream)
+    return b
+
+
+def moe_layer_ffn_path(T: int, E: int, k: int, H: int, I: int, shared: bool) -> int:
+    r = lib().moe_layer_ffn_path(T, E, k, H, I, int(bool(shared)))
+    _ok("moe_layer_ffn_path", min(r, 0))
+    return r
+
+
+def moe_layer_ffn_workspace_bytes(T: int, H: int, I: int, E: int, k: int, block_rows: int, shared: bool) -> int:
+    return int(lib().moe_layer_ffn_workspace_bytes(T, H, I, E, k, block_rows, int(bool(shared))))
+
+
+def moe_layer_ffn_q4(logits, X, T, H, I, E, k, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
+                     dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t, sh_dn_codes_t, sh_dn_scales_t,
+                     sh_dn_biases_t, block_rows, topk_ids, topk_w, out, workspace, ws_bytes, stream=None):
+    _ok("moe_layer_ffn_q4", lib().moe_layer_ffn_q4(
+        _p(logits), _p(X), T, H, I, E, k, _p(gu_codes_t), _p(gu_scales_t), _p(gu_biases_t), _p(dn_codes_t),
+        _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
+        _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), int(block_rows), _p(topk_ids), _p(topk_w),
+        _p(out), _p(workspace), int(ws_bytes), _stream(stream)))
+
+
+def alloc_layer(T: int, H: int, I: int, E: int, k: int, block_rows: int = 0, shared: bool = True, device="cuda"):
+    """Output and workspace tensors for moe_layer_ffn_q4."""
+    ws = moe_layer_ffn_workspace_bytes(T, H, I, E, k, block_rows, shared)
+    if ws == 0 and T > 0:
+        raise MoeQ4Error("moe_layer_ffn_workspace_bytes", MOEQ4_ERR_SHAPE)
+    return dict(
+        out=torch.empty((max(T, 1), H), dtype=torch.int16, device=device),
+        topk_ids=torch.empty((max(T, 1), k), dtype=torch.int32, device=device),
+        topk_w=torch.empty((max(T, 1), k), dtype=torch.float32, device=device),
+        workspace=torch.empty(max(ws, 1), dtype=torch.uint8, device=device), ws_bytes=ws,
+        block_rows=block_rows, path=moe_layer_ffn_path(T, E, k, H, I, shared))
+
+
+def layer_ffn(logits, X, k: int, gu, dn, sh_gu=None, sh_dn=None, block_rows: int = 0, bufs=None, stream=None):
+    """The MoE layer from logits to output (moe_layer_ffn_q4), its path chosen
+    from T.  ``logits`` float32 [T, E], ``X`` bf16 bits [T, H]; weights as
+    expert_ffn.  Returns the buffer dict (``out`` bf16 bits [T, H], ``path``)."""
+    T, E = logits.shape
+    H = X.shape[-1]
+    I = gu[0].shape[1] // 2
+    shared = sh_gu is not None
+    b = bufs or alloc_layer(T, H, I, E, k, block_rows, shared, device=X.device)
+    sg = sh_gu if shared else (None, None, None)
+    sd = sh_dn if shared else (None, None, None)
+    moe_layer_ffn_q4(logits, X, T, H, I, E, k, *gu, *dn, *sg, *sd, b["block_rows"], b["topk_ids"], b["topk_w"],
+                     b["out"], b["workspace"], b["ws_bytes"], stream)
     return b

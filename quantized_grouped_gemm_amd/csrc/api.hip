@@ -420,6 +420,58 @@ int moe_expert_ffn_q4(const uint16_t* X, int T, int H, int I, int E, int k, cons
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 
+// ---- the layer call: the path is chosen from the number of rows
+static int layer_chunk(int T) { return T < 4 ? 4 : (T + 3) / 4 * 4; }  // the whole batch as one chunk
+
+int moe_layer_ffn_path(int T, int E, int k, int H, int I, int shared) {
+  if (T < 0) return MOEQ4_ERR_SHAPE;
+  if (T == 1 && check_decode_shape(E, k, H, I, shared != 0) == MOEQ4_OK) return MOEQ4_PATH_DECODE;
+  if (T >= 1 && T <= MOEQ4_SMALL_MAX_T && check_small_shape(T, E, k, H, I) == MOEQ4_OK) return MOEQ4_PATH_FEW_ROWS;
+  ChunkLayout L;
+  const int rc = chunk_layout(T, layer_chunk(T), H, I, E, k, 0, shared != 0, L);
+  return rc == MOEQ4_OK ? MOEQ4_PATH_PREFILL : rc;
+}
+
+size_t moe_layer_ffn_workspace_bytes(int T, int H, int I, int E, int k, int block_rows, int shared) {
+  const int path = moe_layer_ffn_path(T, E, k, H, I, shared);
+  if (path == MOEQ4_PATH_DECODE) return moe_decode_workspace_bytes(E, k, H, I, shared);
+  if (path == MOEQ4_PATH_FEW_ROWS) return moe_small_batch_workspace_bytes(T, E, k, H, I, shared);
+  if (path == MOEQ4_PATH_PREFILL)
+    return moe_prefill_ffn_chunked_workspace_bytes(T, layer_chunk(T), H, I, E, k, block_rows, shared);
+  return 0;
+}
+
+int moe_layer_ffn_q4(const float* logits, const uint16_t* X, int T, int H, int I, int E, int k,
+                     const uint8_t* gu_codes_t, const uint16_t* gu_scales_t, const uint16_t* gu_biases_t,
+                     const uint8_t* dn_codes_t, const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                     const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t, const uint16_t* sh_gu_biases_t,
+                     const uint8_t* sh_dn_codes_t, const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                     int block_rows, int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  const void* sh[] = {sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                      sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t};
+  int nsh = 0;
+  for (const void* p : sh) nsh += p != nullptr;
+  if (nsh != 0 && nsh != 6) return MOEQ4_ERR_NULL;
+  const int shared = nsh == 6;
+  if (block_rows != 0 && !valid_block_rows(block_rows)) return MOEQ4_ERR_SHAPE;
+  const int path = moe_layer_ffn_path(T, E, k, H, I, shared);
+  if (path < 0) return path;
+  if (path == MOEQ4_PATH_DECODE)
+    return moe_decode_ffn_q4(logits, X, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
+                             dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t, sh_dn_codes_t,
+                             sh_dn_scales_t, sh_dn_biases_t, topk_ids, topk_w, out, workspace, ws_bytes, stream);
+  if (path == MOEQ4_PATH_FEW_ROWS)
+    return moe_small_batch_ffn_q4(logits, X, T, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t,
+                                  dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                                  sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, topk_ids, topk_w, out, workspace,
+                                  ws_bytes, stream);
+  return moe_prefill_ffn_chunked_q4(logits, X, T, H, I, E, k, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t,
+                                    dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                                    sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, layer_chunk(T), block_rows,
+                                    topk_ids, topk_w, out, workspace, ws_bytes, stream);
+}
+
 int moe_calibrate_mfma(int workgroups, int iters, float* out, void* stream) {
   if (!out) return MOEQ4_ERR_NULL;
   if (workgroups < 1 || workgroups > (1 << 20) || iters < 0) return MOEQ4_ERR_SHAPE;

@@ -1,9 +1,13 @@
 // decode.hip -- batch-1 decode step of the MoE layer (one token), gfx950.
 //
 // Perplexity Engineering, "Optimizing on-device inference for Apple Silicon":
-//   section "Decode is a bandwidth problem": with one token per step each
-//   expert GEMV reads every selected weight once, so the step is bound by the
-//   weight bytes, and matrix-vector work suits the vector ALUs;
+//   section "Decode: minimize bytes moved per token": with one token per step
+//   there is almost no weight reuse, so the step is bound by the bytes it
+//   moves; section "Apple silicon provides different paths for different
+//   workloads": a matrix-vector product is limited mainly by memory bandwidth;
+//   section "Optimize the single-row weight path": a row-parallel GEMV in which
+//   a group of lanes shares each output while reading different parts of the
+//   weight matrix;
 //   section "Reduce intermediate and state traffic": the two input projections
 //   run together with their gated activation, and the output projection
 //   together with the routing score and the shared expert's result;

@@ -8,10 +8,12 @@
 // expert load": each output tile of an expert maps to one workgroup, and the
 // tile height follows the rows per expert.
 //
-// One workgroup = one block-map entry (<= BM routed rows of one expert) x one
-// N tile of 4*NF*16 columns.  Its 4 waves split the N tile; each wave owns NF
-// 16-column fragments and every row of the block, so a rebuilt weight is used
-// by all rows of the block without leaving the wave's registers.
+// Blocks of up to 32 rows (k_gemm_q4): one workgroup = one block-map entry
+// (<= BM routed rows of one expert) x one N tile of WAVES*NF*16 columns.  Its
+// waves split the N tile; each wave owns NF 16-column fragments and every row
+// of the block, so a rebuilt weight is used by all rows of the block without
+// leaving the wave's registers.  Taller blocks: k_gemm_q4_w32 and
+// k_gemm_q4_kres below.
 //
 // Data flow per pipeline stage (128 K values = two scale groups):
 //   * codes: weights are in the tiled layout of moe_prepack_q4, so one
@@ -24,36 +26,23 @@
 //   * bf16 MFMA 16x16x32 with fp32 accumulation; empty 16-row sub-tiles of a
 //     partial block are skipped.
 //
-// Two ways to feed the rebuilt weights to the MFMA (chosen by block height):
-//   DQ (blocks of 64/128 rows): each weight is rebuilt exactly as
-//      bf16(scale*code + bias) (fp32 fma, then v_cvt_pk_bf16_f32) and used as
-//      the B operand; one rebuild serves BM rows.
-//   CQ (blocks of 16/32 rows): the codes themselves go to the MFMA as the
-//      exact bf16 values 128+code (one v_and_or per two codes), and the affine
-//      part is applied once per 64-K group in fp32:
-//        sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k,
-//      where the per-row group sums of the activations come from two more
-//      MFMAs against an all-ones operand.  Rebuilding costs ~1 VALU op per
-//      weight instead of ~3, which is what a 16-row block needs to keep up
-//      with HBM.  The weight is used unrounded (s*q + b exactly), not rounded
-//      to bf16.
+// Every weight is rebuilt exactly as bf16(scale*code + bias) (one fp32 fma,
+// then v_cvt_pk_bf16_f32) and used as the B operand; one rebuild serves every
+// row of the block.
 //
 // K slot mapping inside one MFMA: lane quarter q (lanes 16q..16q+15) supplies
 // K indices g*64 + q*16 + j*8 + [0, 8) for K-step j of group g, in natural
 // order, for A and B alike.
 // The grid is sized from the host bound max_blocks; workgroups past the
 // device-side *num_blocks exit at once, so no count goes to the host.
-#include <stdlib.h>
-#include <string.h>
-
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
 
 namespace moeq4 {
 
-constexpr int kGemmWaves = 4;
-constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kKC = 128;           // K values per pipeline stage
 constexpr int kXRow = kKC + 8;     // staged activation row: 128 bf16 + 16 B pad
 constexpr int kBufFlags = 0x00020000;  // raw buffer descriptor word 3 (32-bit data format)
@@ -73,14 +62,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
 __device__ __forceinline__ bf16x8 rebuild_dq(uint32_t wd, float s, float b) {
   const uint4 w = rebuild_words(wd, s, b);
   return as_bf16x8(w.x, w.y, w.z, w.w);
-}
-
-// 8 codes as the exact bf16 values 128+q, natural K order; `one28` holds
-// 0x43004300 (bf16 128.0 twice) in a VGPR so each pair is one v_and_or_b32
-__device__ __forceinline__ bf16x8 rebuild_cq(uint32_t wd, uint32_t one28) {
-  const uint32_t m = 0x000F000Fu;
-  return as_bf16x8((wd & m) | one28, ((wd >> 4) & m) | one28, ((wd >> 8) & m) | one28,
-                   ((wd >> 12) & m) | one28);
 }
 
 template <int NF, int XP>
@@ -265,12 +246,12 @@ struct EpiRow {
   }
 };
 
-template <int BM, int NF, bool CQ, int S, int WAUX, int WAVES, int EPI>
+template <int BM, int NF, int S, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   static_assert(EPI != kEpiSwiglu || NF % 2 == 0, "SwiGLU pairs gate and up fragments");
   constexpr int MF = BM / 16;
   constexpr int NFO = EPI == kEpiSwiglu ? NF / 2 : NF;  // output fragments per wave
-  const int K = a.K, N = a.N, E = a.E;
+  const int K = a.K, N = a.N;
   const uint8_t* __restrict__ Wt = a.Wt;
   const uint16_t* __restrict__ St = a.St;
   const uint16_t* __restrict__ Bt = a.Bt;
@@ -304,9 +285,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   const bool odd_tail = (G & 1) != 0;  // one more chunk with a single group
   const int mfa = (rows + 15) >> 4;
   const int NT = N / 16;
-  uint32_t one28;  // kept in a VGPR: see rebuild_cq
-  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(one28));
-  const bf16x8 ones = as_bf16x8(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
   // ---- buffer resources: one expert's weights (chunk-major tiled layout); the activations
   const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -354,9 +332,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
     for (int f = 0; f < NF; ++f) {
       const int soff = (cl * NT + tile[f]) * 1024;
       const int goff = (cl * NT + tile[f]) * 64;
-      s.w[f] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, lane * 16, soff, WAUX);
-      s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, (lane & 15) * 4, goff, WAUX);
-      s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, (lane & 15) * 4, goff, WAUX);
+      s.w[f] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, lane * 16, soff, 0);
+      s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, (lane & 15) * 4, goff, 0);
+      s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, (lane & 15) * 4, goff, 0);
     }
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -411,21 +389,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
     for (int gi = 0; gi < 2; ++gi) {
       if (gi >= ngroups) break;
       bf16x8 bfr[NF][2];
-      float sc[NF], cc[NF];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const float sv = gi ? __uint_as_float(s.s[f] & 0xFFFF0000u) : __uint_as_float(s.s[f] << 16);
         const float bv = gi ? __uint_as_float(s.b[f] & 0xFFFF0000u) : __uint_as_float(s.b[f] << 16);
-        const uint32_t w0 = s.w[f][2 * gi], w1 = s.w[f][2 * gi + 1];
-        if constexpr (CQ) {
-          sc[f] = sv;
-          cc[f] = __builtin_fmaf(-128.f, sv, bv);
-          bfr[f][0] = rebuild_cq(w0, one28);
-          bfr[f][1] = rebuild_cq(w1, one28);
-        } else {
-          bfr[f][0] = rebuild_dq(w0, sv, bv);
-          bfr[f][1] = rebuild_dq(w1, sv, bv);
-        }
+        bfr[f][0] = rebuild_dq(s.w[f][2 * gi], sv, bv);
+        bfr[f][1] = rebuild_dq(s.w[f][2 * gi + 1], sv, bv);
       }
       const uint16_t* xb = &xs[buf][(lane & 15) * kXRow + gi * 64 + quarter * 16];
 #pragma unroll
@@ -433,34 +402,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
         if (MFA == 0 && r >= mfa) break;
         const bf16x8 a0 = *(const bf16x8*)(xb + r * 16 * kXRow);
         const bf16x8 a1 = *(const bf16x8*)(xb + r * 16 * kXRow + 8);
-        if constexpr (CQ) {
-          // group sums of the activation rows: an MFMA against all-ones puts
-          // sum_k x[row][k] of this lane's 4 rows into every column
-          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-          f32x4 xsv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, zero, 0, 0, 0);
-          xsv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, xsv, 0, 0, 0);
-          f32x4 p[NF];
 #pragma unroll
-          for (int f = 0; f < NF; ++f) p[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bfr[f][0], zero, 0, 0, 0);
+        for (int f = 0; f < NF; ++f)
+          acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bfr[f][0], acc[r][f], 0, 0, 0);
 #pragma unroll
-          for (int f = 0; f < NF; ++f) p[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bfr[f][1], p[f], 0, 0, 0);
-#pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            f32x4 t = acc[r][f];
-            t[0] = __builtin_fmaf(xsv[0], cc[f], __builtin_fmaf(p[f][0], sc[f], t[0]));
-            t[1] = __builtin_fmaf(xsv[1], cc[f], __builtin_fmaf(p[f][1], sc[f], t[1]));
-            t[2] = __builtin_fmaf(xsv[2], cc[f], __builtin_fmaf(p[f][2], sc[f], t[2]));
-            t[3] = __builtin_fmaf(xsv[3], cc[f], __builtin_fmaf(p[f][3], sc[f], t[3]));
-            acc[r][f] = t;
-          }
-        } else {
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bfr[f][0], acc[r][f], 0, 0, 0);
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bfr[f][1], acc[r][f], 0, 0, 0);
-        }
+        for (int f = 0; f < NF; ++f)
+          acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bfr[f][1], acc[r][f], 0, 0, 0);
       }
     }
   };
@@ -1071,8 +1018,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4_kres(const GemmArgs a0, 
 
 namespace {
 
+// One kernel instance per (block height, epilogue), chosen from sweeps on
+// MI355X.  Blocks of 16/32 rows use the 16x16x32 kernel (8 waves, NF
+// 16-column fragments per wave, an S-stage register ring), taller ones the
+// 32x32x16 kernel (4 waves sized for two workgroups per CU, or 8 waves for
+// 256-row blocks and the dense 128-row down projection).
 struct GemmVariant {
-  const char* name;
   int bm;
   int epi;
   int tile_n;  // output columns per workgroup
@@ -1081,118 +1032,94 @@ struct GemmVariant {
   bool dense;  // runs a dense second problem (GemmArgs::d_rows)
 };
 
-#define MOEQ4_GEMM_VARIANT(BM, NF, CQ, S, WAUX, WAVES, EPI)                                      \
-  {"bm" #BM "_nf" #NF "_" #CQ "_s" #S "_a" #WAUX "_w" #WAVES, BM, EPI,                         \
-   WAVES * NF * 16 / (EPI == kEpiSwiglu ? 2 : 1), WAVES, (const void*)&k_gemm_q4<BM, NF, CQ, S, WAUX, WAVES, EPI>, \
+#define MOEQ4_GEMM16(BM, NF, S, WAVES, EPI)                                                       \
+  {BM, EPI, WAVES * NF * 16 / (EPI == kEpiSwiglu ? 2 : 1), WAVES, (const void*)&k_gemm_q4<BM, NF, S, WAVES, EPI>, \
    false}
-#define MOEQ4_GEMM_W32(BM, NF32, S, WAVES, EPI)                                                  \
-  {"w32_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, EPI, WAVES * NF32 * 32 / (EPI == kEpiSwiglu ? 2 : 1), \
-   WAVES, (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES, EPI, (WAVES == 4 ? 2 : 1)>, true}
+#define MOEQ4_GEMM32(BM, NF32, S, WAVES, EPI)                                                     \
+  {BM, EPI, WAVES * NF32 * 32 / (EPI == kEpiSwiglu ? 2 : 1), WAVES,                              \
+   (const void*)&k_gemm_q4_w32<BM, NF32, S, WAVES, EPI, (WAVES == 4 ? 2 : 1)>, true}
 
-// The first entry of each (block height, epilogue) is its default, from sweeps
-// on MI355X.  WAUX is the cache policy of the weight loads.  The single
-// projection (kEpiPlain) feeds short blocks with the codes (CQ); the FFN
-// epilogues rebuild every weight exactly (DQ), as the FFN chains two
-// projections and the rebuilt weights' bf16 rounding then matters.
 const GemmVariant kVariants[] = {
-    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 8, kEpiPlain),
-    MOEQ4_GEMM_VARIANT(32, 2, true, 3, 0, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiPlain),
+    MOEQ4_GEMM16(16, 2, 4, 8, kEpiPlain),
+    MOEQ4_GEMM16(32, 2, 3, 8, kEpiPlain),
+    MOEQ4_GEMM32(64, 2, 2, 4, kEpiPlain),
+    MOEQ4_GEMM32(128, 2, 2, 4, kEpiPlain),
+    MOEQ4_GEMM32(256, 1, 2, 8, kEpiPlain),
     // FFN: gate+up with SwiGLU, down scaled by the routing weight, shared down + combine
-    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiSwiglu),
-    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiSwiglu),
-    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiSwiglu),
-    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiSwiglu),
-    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiScale),
-    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiScale),
-    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiScale),
-    MOEQ4_GEMM_W32(128, 2, 2, 4, kEpiScale),
-    MOEQ4_GEMM_VARIANT(16, 2, false, 4, 0, 8, kEpiTerm),
-    MOEQ4_GEMM_VARIANT(32, 2, false, 3, 0, 8, kEpiTerm),
-    MOEQ4_GEMM_W32(64, 2, 2, 4, kEpiTerm),
-    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiTerm),
-    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiSwiglu),
-    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiScale),
-    MOEQ4_GEMM_W32(256, 1, 2, 8, kEpiTerm),
-    // alternatives for tuning sweeps
-    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiSwiglu),
-    MOEQ4_GEMM_VARIANT(16, 2, true, 4, 0, 4, kEpiPlain),
-    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 4, kEpiPlain),
-    MOEQ4_GEMM_VARIANT(32, 4, true, 3, 0, 8, kEpiPlain),
-    MOEQ4_GEMM_VARIANT(32, 2, true, 4, 0, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(64, 2, 2, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 1, 3, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 1, 4, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 3, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 1, 3, 4, kEpiPlain),
-    MOEQ4_GEMM_W32(64, 2, 3, 4, kEpiPlain),
-    MOEQ4_GEMM_W32(64, 2, 4, 4, kEpiPlain),
-    MOEQ4_GEMM_W32(64, 1, 3, 8, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 2, 2, 8, kEpiSwiglu),
-    MOEQ4_GEMM_W32(128, 2, 3, 8, kEpiSwiglu),
-    MOEQ4_GEMM_W32(128, 1, 2, 8, kEpiScale),
-    MOEQ4_GEMM_W32(128, 1, 2, 4, kEpiPlain),
-    MOEQ4_GEMM_W32(128, 1, 2, 4, kEpiSwiglu),
+    MOEQ4_GEMM16(16, 2, 4, 8, kEpiSwiglu),
+    MOEQ4_GEMM16(32, 2, 3, 8, kEpiSwiglu),
+    MOEQ4_GEMM32(64, 2, 2, 4, kEpiSwiglu),
+    MOEQ4_GEMM32(128, 2, 2, 4, kEpiSwiglu),
+    MOEQ4_GEMM32(256, 1, 2, 8, kEpiSwiglu),
+    MOEQ4_GEMM16(16, 2, 4, 8, kEpiScale),
+    MOEQ4_GEMM16(32, 2, 3, 8, kEpiScale),
+    MOEQ4_GEMM32(64, 2, 2, 4, kEpiScale),
+    MOEQ4_GEMM32(128, 2, 2, 4, kEpiScale),
+    MOEQ4_GEMM32(256, 1, 2, 8, kEpiScale),
+    MOEQ4_GEMM16(16, 2, 4, 8, kEpiTerm),
+    MOEQ4_GEMM16(32, 2, 3, 8, kEpiTerm),
+    MOEQ4_GEMM32(64, 2, 2, 4, kEpiTerm),
+    MOEQ4_GEMM32(128, 1, 2, 8, kEpiTerm),
+    MOEQ4_GEMM32(256, 1, 2, 8, kEpiTerm),
 };
-#undef MOEQ4_GEMM_VARIANT
-#undef MOEQ4_GEMM_W32
+#undef MOEQ4_GEMM16
+#undef MOEQ4_GEMM32
 
-// Tile choice by block height and epilogue; MOEQ4_GEMM_VARIANT=<name> (same
-// block height and epilogue) overrides it for tuning sweeps.
 const GemmVariant* pick_variant(int bm, int epi) {
-  static const char* forced = getenv("MOEQ4_GEMM_VARIANT");
-  if (forced)
-    for (const GemmVariant& v : kVariants)
-      if (v.bm == bm && v.epi == epi && strcmp(v.name, forced) == 0) return &v;
   for (const GemmVariant& v : kVariants)
     if (v.bm == bm && v.epi == epi) return &v;
   return nullptr;
 }
 
-}  // namespace
-
-namespace {
-// the short-K kernel for the FFN's down projections (blocks of 64 or 128 rows);
-// the first entry of each (block height, epilogue, chunks) is its default and
-// MOEQ4_KRES_VARIANT=<name> picks another for tuning sweeps
+// The short-K kernel for the FFN's down projections, 64-row blocks (for
+// 128-row blocks two 4-wave tall-block workgroups per CU measured faster).
 struct KresVariant {
-  const char* name;
   int bm, epi, nch, waves, tile_n;
   const void* fn;
 };
-#define MOEQ4_KRES(BM, NF32, NCH, S, WAVES, EPI)                                                   \
-  {"kres_bm" #BM "_nf" #NF32 "_s" #S "_w" #WAVES, BM, EPI, NCH, WAVES, WAVES * NF32 * 32,           \
-   (const void*)&k_gemm_q4_kres<BM, NF32, NCH, S, WAVES, EPI>}
+#define MOEQ4_KRES(BM, NF32, NCH, S, WAVES, EPI) \
+  {BM, EPI, NCH, WAVES, WAVES * NF32 * 32, (const void*)&k_gemm_q4_kres<BM, NF32, NCH, S, WAVES, EPI>}
 const KresVariant kKres[] = {
     MOEQ4_KRES(64, 1, 4, 4, 8, kEpiScale),
     MOEQ4_KRES(64, 1, 4, 4, 8, kEpiTerm),
     MOEQ4_KRES(64, 1, 2, 2, 8, kEpiScale),
     MOEQ4_KRES(64, 1, 2, 2, 8, kEpiTerm),
-    // alternatives for tuning sweeps (128-row blocks: two 4-wave tall-block
-    // workgroups per CU measured faster on MI355X)
-    MOEQ4_KRES(128, 1, 4, 4, 8, kEpiScale),
-    MOEQ4_KRES(128, 1, 2, 2, 8, kEpiScale),
-    MOEQ4_KRES(128, 2, 4, 2, 8, kEpiScale),
-    MOEQ4_KRES(128, 2, 4, 2, 4, kEpiScale),
-    MOEQ4_KRES(64, 2, 4, 2, 8, kEpiTerm),
-    MOEQ4_KRES(64, 2, 4, 2, 4, kEpiTerm),
-    MOEQ4_KRES(128, 1, 4, 2, 8, kEpiScale),
 };
 #undef MOEQ4_KRES
-const KresVariant* pick_kres(int bm, int epi, int nch) {
-  static const char* forced = getenv("MOEQ4_KRES_VARIANT");
-  if (forced)
-    for (const KresVariant& v : kKres)
-      if (v.bm == bm && v.epi == epi && v.nch == nch && strcmp(v.name, forced) == 0) return &v;
-  if (bm != 64) return nullptr;  // defaults: 64-row blocks only
-  for (const KresVariant& v : kKres)
-    if (v.bm == bm && v.epi == epi && v.nch == nch) return &v;
-  return nullptr;
+constexpr int kNumKres = sizeof(kKres) / sizeof(kKres[0]);
+static_assert(kNumKres <= 32, "one bit per variant");
+
+int pick_kres(int bm, int epi, int nch) {
+  for (int i = 0; i < kNumKres; ++i)
+    if (kKres[i].bm == bm && kKres[i].epi == epi && kKres[i].nch == nch) return i;
+  return -1;
 }
+
+// Per device, one bit per short-K variant whose dynamic-LDS limit has been
+// raised.  Two threads may both raise it (the call is idempotent); the bit
+// only saves later calls the runtime round trip.
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t> g_kres_raised[kMaxDevices];
+
+hipError_t raise_kres_lds(int vi, int bytes) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) {
+    note_hip_error(err, "hipGetDevice");
+    return err;
+  }
+  const uint32_t bit = 1u << vi;
+  std::atomic<uint32_t>* flag = dev >= 0 && dev < kMaxDevices ? &g_kres_raised[dev] : nullptr;
+  if (flag && (flag->load(std::memory_order_acquire) & bit)) return hipSuccess;
+  err = hipFuncSetAttribute(kKres[vi].fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err != hipSuccess) {
+    note_hip_error(err, "hipFuncSetAttribute(k_gemm_q4_kres)");
+    return err;
+  }
+  if (flag) flag->fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
+
 }  // namespace
 
 // grid of a launch with dense_blocks dense blocks and at most max_blocks routed
@@ -1201,42 +1128,38 @@ static dim3 task_grid(long long dense_blocks, long long max_blocks, long long nt
   return dim3((unsigned)(((dense_blocks + kXcds - 1) / kXcds + (max_blocks + kXcds - 1) / kXcds) * ntiles * kXcds));
 }
 
+// The most block-map entries any routing of A assignments over E experts can
+// produce with BM-row blocks (each expert's last block may be partial).
+static long long routed_block_bound(long long A, long long E, int BM) {
+  const long long m = A < E ? A : E;
+  return (A + m * (BM - 1)) / BM;
+}
+
 hipError_t gemm_launch(const GemmArgs& a_in, int epi, int BM, int max_blocks, hipStream_t stream) {
-  max_blocks = max(max_blocks, 0);
+  // The routed grid never needs more than the bound: a larger max_blocks
+  // (buffers sized for another T) only adds workgroups that would index past
+  // the routing tables of this launch.
+  long long mb = max(max_blocks, 0);
+  if (a_in.blocks) mb = std::min(mb, routed_block_bound(a_in.A, a_in.E, BM));
+  else mb = std::min(mb, (long long)(a_in.A + BM - 1) / BM);
+  max_blocks = (int)mb;
   if (max_blocks == 0 && a_in.d_rows <= 0) return hipSuccess;
   GemmArgs a = a_in;
   a.max_blocks = max_blocks;
   const long long dense_blocks = a.d_rows > 0 ? (a.d_rows + BM - 1) / BM : 0;
-  static const bool no_kres = getenv("MOEQ4_NO_KRES") != nullptr;  // for comparisons
-  if (!no_kres && a.K <= kKResMax && a.K % kKC == 0) {
-    const KresVariant* kv = pick_kres(BM, epi, a.K / kKC);
-    if (kv) {
-      const void* fn = kv->fn;
-      const int waves = kv->waves, tile_n = kv->tile_n;
-      // columns per workgroup: all of N, or fewer when there are too few blocks
-      // to fill the GPU (the dense shared expert)
-      int nsplit = max(1, min(a.N / tile_n, 512 / max(1, max_blocks)));
-      const int NR = (a.N / nsplit + tile_n - 1) / tile_n * tile_n;
-      nsplit = (a.N + NR - 1) / NR;
-      const dim3 grid = task_grid(dense_blocks, max_blocks, nsplit);
-      const size_t lds = (size_t)BM * a.K * 2;  // up to 128 KB of the 160 KB a workgroup may use
-      static const void* raised[16] = {};
-      bool done = false;
-      for (const void* r : raised) done |= r == fn;
-      if (!done) {
-        const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(BM * kKResMax * 2));
-        if (err != hipSuccess) {
-          note_hip_error(err, "hipFuncSetAttribute(k_gemm_q4_kres)");
-          return err;
-        }
-        for (const void*& r : raised)
-          if (!r) {
-            r = fn;
-            break;
-          }
-      }
-      return launch("k_gemm_q4_kres", fn, grid, dim3(waves * 64), lds, stream, a, NR);
-    }
+  const int kv = a.K <= kKResMax && a.K % kKC == 0 ? pick_kres(BM, epi, a.K / kKC) : -1;
+  if (kv >= 0) {
+    const KresVariant& v = kKres[kv];
+    // columns per workgroup: all of N, or fewer when there are too few blocks
+    // to fill the GPU (the dense shared expert)
+    int nsplit = max(1, min(a.N / v.tile_n, 512 / max(1, max_blocks)));
+    const int NR = (a.N / nsplit + v.tile_n - 1) / v.tile_n * v.tile_n;
+    nsplit = (a.N + NR - 1) / NR;
+    const dim3 grid = task_grid(dense_blocks, max_blocks, nsplit);
+    const size_t lds = (size_t)BM * a.K * 2;  // up to 64 KB of the 160 KB a workgroup may use
+    const hipError_t err = raise_kres_lds(kv, (int)(BM * kKResMax * 2));
+    if (err != hipSuccess) return err;
+    return launch("k_gemm_q4_kres", v.fn, grid, dim3(v.waves * 64), lds, stream, a, NR);
   }
   const GemmVariant* v = pick_variant(BM, epi);
   if (!v || (dense_blocks > 0 && !v->dense)) return hipErrorInvalidValue;

@@ -2,9 +2,11 @@
 // by the one-token decode step (decode.hip) and the few-token step (small.hip).
 //
 // Perplexity Engineering, "Optimizing on-device inference for Apple Silicon",
-// section "Decode is a bandwidth problem": a one-row product reads every
-// selected weight once and suits the vector ALUs; section "Dequantize weights
-// during matrix multiplication": weights are rebuilt on chip, never stored.
+// section "Optimize the single-row weight path": a row-parallel GEMV for one
+// activation row; section "Apple silicon provides different paths for
+// different workloads": with little weight reuse it is bound by memory
+// bandwidth; section "Dequantize weights during matrix multiplication":
+// weights are rebuilt on chip, never stored.
 //
 // A wave reads one 1 KB block of the tiled layout (16 rows x 128 K values;
 // lane 16q+r holds 32 codes of row r, K quarters q), rebuilds each weight

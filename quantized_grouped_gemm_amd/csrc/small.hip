@@ -5,8 +5,9 @@
 // hands the layer groups of two to five rows, a shape that suits neither the
 // matrix path nor the one-row path, and those rows often select different
 // experts, so more expert weights are read.  Here such a group runs as the
-// decode design (sections "Decode is a bandwidth problem" and "Reduce
-// intermediate and state traffic") widened to T tokens, with every distinct
+// decode design (sections "Decode: minimize bytes moved per token",
+// "Optimize the single-row weight path" and "Reduce intermediate and state
+// traffic") widened to T tokens, with every distinct
 // selected expert read once for all the tokens that chose it.
 //
 //   k_small_route    one workgroup: wave w routes token w (top-k over the E

@@ -45,12 +45,21 @@ def gpu_route(logits: np.ndarray, k: int, block_rows: int):
     return out
 
 
+NAN_BF16 = 0x7FC0  # quiet NaN: an output the kernels never write stays NaN and fails every comparison
+
+
+def nan_filled(shape, device="cuda") -> torch.Tensor:
+    """int16 tensor (bf16 bit patterns) filled with NaN."""
+    return torch.full(shape, NAN_BF16, dtype=torch.int16, device=device)
+
+
 def gpu_gemm(X: np.ndarray, k: int, Wq, S, B, rt_dev: dict, reps: int = 1) -> np.ndarray:
     """moe_prepack_q4 + moe_grouped_gemm_q4 with routing tables already on the
-    device; Y as bf16 bits [T*k, N]."""
+    device; Y as bf16 bits [T*k, N], poisoned with NaN before the call."""
     Xd = dev(X)
     packed = q.prepack(dev(Wq), dev(S), dev(B))
-    Y = None
+    T = X.shape[0]
+    Y = nan_filled((max(T * k, 1), Wq.shape[1]))
     for _ in range(reps):
         Y = q.grouped_gemm_q4(Xd, k, packed, rt_dev, Y=Y)
     torch.cuda.synchronize()

@@ -39,6 +39,20 @@ def compare_bf16(gpu_bits: np.ndarray, ref: np.ndarray, tol: float | None = None
     err = np.abs(g - ref)
     bound = tol + 0.5 * ulp_bf16(g)
     bad = ~(err <= bound)  # NaN fails
+    # margin used: the worst error as a fraction of the element's own bound,
+    # and the worst error of the rounded result beyond bf16's own rounding
+    # of the oracle value (|gpu - bf16(ref)|, in units of tol)
+    used = float(np.nanmax(err / bound)) if g.size else 0.0
+    excess = np.maximum(err - 0.5 * ulp_bf16(ref), 0.0)
     stats = dict(n=int(g.size), tol=tol, max_err=float(err.max()) if g.size else 0.0,
-                 n_bad=int(bad.sum()), rms_ref=float(np.sqrt(np.mean(ref * ref))) if g.size else 0.0)
+                 n_bad=int(bad.sum()), rms_ref=float(np.sqrt(np.mean(ref * ref))) if g.size else 0.0,
+                 worst_err_over_bound=used,
+                 worst_excess_over_tol=float(np.nanmax(excess) / tol) if g.size else 0.0)
     return (not bad.any()), stats
+
+
+def report(name: str, st: dict) -> None:
+    """One line per full-size comparison: the worst error against its bound."""
+    print(f"PARITY {name}: n={st['n']} max_err={st['max_err']:.4g} tol={st['tol']:.4g} "
+          f"worst err/bound={st['worst_err_over_bound']:.3f} "
+          f"worst excess over bf16(ref)/tol={st['worst_excess_over_tol']:.3f} n_bad={st['n_bad']}", flush=True)

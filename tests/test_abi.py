@@ -269,3 +269,42 @@ def test_dequant_validation():
     assert L.moe_dequant_q4(None, FAKE, FAKE, 2, 32, 128, FAKE, None) == q.MOEQ4_ERR_NULL
     assert L.moe_dequant_q4(FAKE, FAKE, FAKE, 2, 32, 128, None, None) == q.MOEQ4_ERR_NULL
     assert L.moe_dequant_q4(FAKE, FAKE, FAKE, 2, 32, 128, FAKE + 2, None) == q.MOEQ4_ERR_ALIGN
+
+
+def test_layer_path_follows_row_count():
+    # decode shapes: 8 of 256 experts, H=2048, I=512, shared expert
+    E, k, H, I = 256, 8, 2048, 512
+    assert q.moe_layer_ffn_path(1, E, k, H, I, True) == q.MOEQ4_PATH_DECODE
+    for T in (2, 3, 5, 8):
+        assert q.moe_layer_ffn_path(T, E, k, H, I, True) == q.MOEQ4_PATH_FEW_ROWS
+    for T in (0, 9, 64, 512, 4096):
+        assert q.moe_layer_ffn_path(T, E, k, H, I, True) == q.MOEQ4_PATH_PREFILL
+    # past the decode kernels' limits (H > 8192) one row takes the few-row path;
+    # past the few-row staging limit (T*(k+1)*I > 49152) rows take the routed path
+    assert q.moe_layer_ffn_path(1, 16, 2, 16384, 128, False) == q.MOEQ4_PATH_FEW_ROWS
+    assert q.moe_layer_ffn_path(8, 256, 8, 2048, 1024, True) == q.MOEQ4_PATH_PREFILL
+    assert q.lib().moe_layer_ffn_path(-1, E, k, H, I, 1) == q.MOEQ4_ERR_SHAPE
+    assert q.lib().moe_layer_ffn_path(4, E, 300, H, I, 1) < 0
+    # the workspace is that of the path taken
+    assert q.moe_layer_ffn_workspace_bytes(1, H, I, E, k, 0, True) == q.moe_decode_workspace_bytes(E, k, H, I, True)
+    assert q.moe_layer_ffn_workspace_bytes(5, H, I, E, k, 0, True) == \
+        q.moe_small_batch_workspace_bytes(5, E, k, H, I, True)
+    assert q.moe_layer_ffn_workspace_bytes(64, H, I, E, k, 0, True) == \
+        q.moe_prefill_ffn_chunked_workspace_bytes(64, 64, H, I, E, k, 0, True)
+
+
+def test_layer_call_rejects_on_host():
+    L = q.lib()
+    args = [FAKE, FAKE, 4, 2048, 512, 256, 8] + [FAKE] * 6 + [None] * 6 + [0, None, None, FAKE, FAKE, 1 << 30, None]
+    bad = list(args)
+    bad[13] = FAKE                                   # one shared pointer of six
+    assert L.moe_layer_ffn_q4(*bad) == q.MOEQ4_ERR_NULL
+    bad = list(args)
+    bad[19] = 24                                     # block_rows
+    assert L.moe_layer_ffn_q4(*bad) == q.MOEQ4_ERR_SHAPE
+    bad = list(args)
+    bad[24] = 16                                     # workspace too small
+    assert L.moe_layer_ffn_q4(*bad) == q.MOEQ4_ERR_WORKSPACE
+    bad = list(args)
+    bad[1] = FAKE + 8                                # misaligned X
+    assert L.moe_layer_ffn_q4(*bad) == q.MOEQ4_ERR_ALIGN

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads as W
-from parity import compare_bf16
+from parity import compare_bf16, report
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # collected on CPU hosts only to be skipped
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from gpu_util import dev, host  # noqa: E402
+from gpu_util import dev, host, nan_filled  # noqa: E402
 import quantized_grouped_gemm_amd as q  # noqa: E402
 
 
@@ -37,8 +37,11 @@ class Layer:
         self.Ld, self.Xd = dev(p.logits), dev(p.X)
 
     def chunked(self, chunk, bm=0):
+        T, H, I, E, k = self.w.T, self.w.K, self.w.N, self.w.E, self.w.k
+        bufs = q.alloc_chunked(T, chunk, H, I, E, k, bm, self.shared)
+        bufs["out"] = nan_filled((max(T, 1), H))   # rows the kernels skip stay NaN
         b = q.prefill_ffn_chunked(self.Ld, self.Xd, self.w.k, self.gu, self.dn, self.sh_gu, self.sh_dn,
-                                  chunk_tokens=chunk, block_rows=bm)
+                                  chunk_tokens=chunk, block_rows=bm, bufs=bufs)
         torch.cuda.synchronize()
         T = self.w.T
         return host(b["topk_ids"])[:T], host(b["topk_w"])[:T], host(b["out"], np.uint16)[:T]
@@ -53,15 +56,17 @@ class Layer:
             outs.append(host(b["out"], np.uint16)[: min(chunk, self.w.T - t0)])
         return np.concatenate(outs)
 
-    def check_oracle(self, chunk, bm=0, tokens=None):
+    def check_oracle(self, chunk, bm=0, name=None):
         p, k = self.p, self.w.k
         ids, wts, out = self.chunked(chunk, bm)
         rid, rw = oracle.topk_softmax(p.logits, k)
         np.testing.assert_array_equal(ids, rid)
         assert np.abs(wts.astype(np.float64) - rw).max() <= 1e-6
-        ref = oracle.expert_ffn_q4(p.X, rid, rw, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b, sh=self.sh_host,
-                                   tokens=tokens)
-        ok, st = compare_bf16(out if tokens is None else out[tokens], ref)
+        ref = oracle.expert_ffn_grouped_q4(p.X, rid, rw, p.gu_q, p.gu_s, p.gu_b, p.dn_q, p.dn_s, p.dn_b,
+                                           sh=self.sh_host)
+        ok, st = compare_bf16(out, ref)
+        if name:
+            report(name, st)
         assert ok, (chunk, st)
         return out
 
@@ -90,10 +95,8 @@ def test_chunked_deterministic():
     np.testing.assert_array_equal(L.chunked(128)[2], a)
 
 
-def test_chunked_expert_ffn_workload_sampled():
+def test_chunked_expert_ffn_workload_full_size():
     # the expert-FFN workload (T=4096, 8 of 256 + shared, H=2048, I=512) in
-    # chunks of 1024 tokens; the oracle checks a sample of tokens
+    # chunks of 1024 tokens: every output against the oracle
     w = W.WORKLOADS[3]
-    L = Layer(w)
-    tokens = np.sort(np.random.default_rng(5).choice(w.T, size=40, replace=False).astype(np.int32))
-    L.check_oracle(1024, 0, tokens=tokens)
+    Layer(w).check_oracle(1024, 0, name=f"{w.name} in chunks of 1024")

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as W
-from parity import compare_bf16
+from parity import compare_bf16, report
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -144,25 +144,27 @@ def test_dequant_bit_exact(E, N, K):
         np.testing.assert_array_equal(got[e], _bf16_bits(oracle.dequant_q4(p.Wq[e], p.S[e], p.B[e])))
 
 
-def test_dequant_prefill_weights_sampled():
-    # the 256-expert [512 x 2048] weights of the prefill workload, three experts checked in full
+def test_dequant_prefill_weights_full():
+    # every weight of the 256-expert [512 x 2048] prefill workload
     w = W.WORKLOADS[2]
     p = W.make_problem(w)
     out = q.dequant(q.prepack(dev(p.Wq), dev(p.S), dev(p.B)), w.E, w.N, w.K)
     torch.cuda.synchronize()
-    for e in (0, 127, 255):
+    for e in range(w.E):
         np.testing.assert_array_equal(host(out[e], np.uint16), _bf16_bits(oracle.dequant_q4(p.Wq[e], p.S[e], p.B[e])))
 
 
 # ----------------------------------------------------------- grouped GEMM --
 
-def _gemm_full(w, bm, seed_logits=None):
+def _gemm_full(w, bm, seed_logits=None, name=None):
     p = W.make_problem(w)
     logits = p.logits if seed_logits is None else seed_logits
     g, ids, _, ref = _check_route(logits, w.k, bm)
     Y = gpu_gemm(p.X, w.k, p.Wq, p.S, p.B, g["dev"])
     Yref = oracle.grouped_gemm_q4(p.X, w.k, p.Wq, p.S, p.B, ref["perm"], ref["offsets"])
     ok, st = compare_bf16(Y[: w.T * w.k], Yref)
+    if name:
+        report(name, st)
     assert ok, st
     return Y, g, p
 
@@ -194,32 +196,24 @@ def test_gemm_hot_expert():
     _gemm_full(w, 32, seed_logits=_logits("hot", 300, 16))
 
 
-def _sampled(w, bm, nsamp, seed):
-    """Full-size run; the oracle checks a sample of rows one by one."""
-    p = W.make_problem(w)
-    g, ids, _, ref = _check_route(p.logits, w.k, bm)
-    Y = gpu_gemm(p.X, w.k, p.Wq, p.S, p.B, g["dev"])
-    r = np.random.default_rng(seed)
-    blocks = ref["blocks"]
-    pick = set(r.choice(w.T * w.k, size=nsamp, replace=False).tolist())
-    for b in blocks[r.choice(len(blocks), size=min(len(blocks), nsamp // 4), replace=False)]:
-        pick.update([int(b[1]), int(b[1] + b[2] - 1)])          # first and last row of blocks
-    pos = np.array(sorted(pick), np.int32)
-    a = ref["perm"][pos]
-    Yref = oracle.expert_rows_q4(p.X, p.Wq, p.S, p.B, a // w.k, ids.reshape(-1)[a])
-    ok, st = compare_bf16(Y[pos], Yref)
-    assert ok, st
-    return Y, g
-
-
 def test_gemm_prefill_chunk_full_size():
-    _sampled(W.WORKLOADS[2], 32, 96, 1)
+    # the prefill-chunk workload (T=512, 8 of 256 experts, 2048 -> 512) at its
+    # default block height: every one of the 2,097,152 outputs against the oracle
+    w = W.WORKLOADS[2]
+    Y, g, p = _gemm_full(w, q.moe_default_block_rows(w.T, w.E, w.k), name=w.name)
+
+
+@pytest.mark.parametrize("bm", [32, 64])
+def test_gemm_prefill_chunk_full_size_other_heights(bm):
+    w = W.WORKLOADS[2]
+    _gemm_full(w, bm, name=f"{w.name} BM={bm}")
 
 
 @pytest.mark.parametrize("bm", [128, 256])
 def test_gemm_skewed_full_size(bm):
-    Y, g = _sampled(W.WORKLOADS[4], bm, 96, 2)
-    assert np.isfinite(Y.view(np.int16).astype(np.float32)).all()
+    # the skewed workload (T=16384, Zipf-biased logits): all 67,108,864 outputs
+    w = W.WORKLOADS[4]
+    _gemm_full(w, bm, name=f"{w.name} BM={bm}")
 
 
 def test_gemm_deterministic():
