@@ -326,6 +326,34 @@ int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int 
                       int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
                       size_t ws_bytes, void* stream);
 
+/* Size of the per-GPU static scratch array of moe_decode_ffn_q4_noalloc. */
+#define MOEQ4_DECODE_SCRATCH_BYTES (256 * 1024)
+
+/* moe_decode_ffn_q4 with no workspace argument and no allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (less
+ * workspace and ws_bytes), checks, kernels and results as moe_decode_ffn_q4.
+ * Its scratch is a static device array of MOEQ4_DECODE_SCRATCH_BYTES bytes, one
+ * per GPU, held by the library until the process ends; the first call on a
+ * device looks its address up (hipGetSymbolAddress, with the calling thread's
+ * current device, which must be the device `stream` belongs to).  The call
+ * itself never calls hipMalloc or hipFree.  Every call on one GPU shares that
+ * array: calls that may overlap in time on one GPU (other streams, other
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  The array needs no initial contents (each call writes every byte it
+ * reads).  Sizes whose scratch (moe_decode_workspace_bytes) exceeds
+ * MOEQ4_DECODE_SCRATCH_BYTES return MOEQ4_ERR_UNSUPPORTED (no shape the decode
+ * kernels accept needs that much); a failed address lookup returns
+ * MOEQ4_ERR_HIP. */
+int moe_decode_ffn_q4_noalloc(const float* logits, const uint16_t* x, int E, int k, int H, int I,
+                              const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                              const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                              const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                              const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                              const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                              const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                              int32_t* topk_ids, float* topk_w, uint16_t* out, void* stream);
+
 /* Bytes of device scratch moe_small_batch_ffn_q4 needs (0 on invalid or
  * unsupported sizes).  shared: 1 when a shared expert is given, else 0. */
 size_t moe_small_batch_workspace_bytes(int T, int E, int k, int H, int I, int shared);

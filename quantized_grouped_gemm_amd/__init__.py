@@ -30,6 +30,7 @@ MOEQ4_ERR_HIP = -6
 MOEQ4_MAX_EXPERTS = 1024
 MOEQ4_MAX_TOPK = 64
 MOEQ4_SMALL_MAX_T = 8
+MOEQ4_DECODE_SCRATCH_BYTES = 256 * 1024
 MOEQ4_PATH_DECODE = 1
 MOEQ4_PATH_FEW_ROWS = 2
 MOEQ4_PATH_PREFILL = 3
@@ -61,6 +62,7 @@ SIGNATURES = {
     "moe_small_batch_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_calibrate_mfma": (_i, [_i, _i, _vp, _vp]),
     "moe_dequant_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "moe_decode_ffn_q4_noalloc": (_i, [_vp, _vp, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp]),
     "moe_layer_ffn_path": (_i, [_i, _i, _i, _i, _i, _i]),
     "moe_layer_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moe_layer_ffn_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_i, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -188,6 +190,16 @@ def moe_decode_ffn_q4(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_
         _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
         _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), _p(topk_ids), _p(topk_w), _p(out),
         _p(workspace), int(ws_bytes), _stream(stream)))
+
+
+def moe_decode_ffn_q4_noalloc(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t,
+                              dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
+                              sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, topk_ids, topk_w, out, stream=None):
+    _ok("moe_decode_ffn_q4_noalloc", lib().moe_decode_ffn_q4_noalloc(
+        _p(logits), _p(x), E, k, H, I, _p(gu_codes_t), _p(gu_scales_t), _p(gu_biases_t), _p(dn_codes_t),
+        _p(dn_scales_t), _p(dn_biases_t), _p(sh_gu_codes_t), _p(sh_gu_scales_t), _p(sh_gu_biases_t),
+        _p(sh_dn_codes_t), _p(sh_dn_scales_t), _p(sh_dn_biases_t), _p(topk_ids), _p(topk_w), _p(out),
+        _stream(stream)))
 
 
 def moe_prefill_ffn_chunked_workspace_bytes(T: int, chunk_tokens: int, H: int, I: int, E: int, k: int,

@@ -216,15 +216,16 @@ size_t moe_decode_workspace_bytes(int E, int k, int H, int I, int shared) {
   return decode_plan(E, k, H, I, shared != 0).ws_bytes;
 }
 
-int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int H, int I,
-                      const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
-                      const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
-                      const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
-                      const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
-                      const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
-                      const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
-                      int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
-                      size_t ws_bytes, void* stream) {
+// Checks and launch shared by moe_decode_ffn_q4 and moe_decode_ffn_q4_noalloc;
+// workspace == nullptr with no_alloc: the library's per-device scratch array.
+static int decode_call(const float* logits, const uint16_t* x, int E, int k, int H, int I,
+                       const uint8_t* gu_codes_t, const uint16_t* gu_scales_t, const uint16_t* gu_biases_t,
+                       const uint8_t* dn_codes_t, const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                       const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                       const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                       const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t, int32_t* topk_ids,
+                       float* topk_w, uint16_t* out, void* workspace, size_t ws_bytes, bool no_alloc,
+                       void* stream) {
   const void* sh[] = {sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t,
                       sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t};
   int nsh = 0;
@@ -234,7 +235,7 @@ int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int 
   const int rc = check_decode_shape(E, k, H, I, shared);
   if (rc != MOEQ4_OK) return rc;
   if (!logits || !x || !gu_codes_t || !gu_scales_t || !gu_biases_t || !dn_codes_t || !dn_scales_t ||
-      !dn_biases_t || !out || !workspace)
+      !dn_biases_t || !out || (!no_alloc && !workspace))
     return MOEQ4_ERR_NULL;
   const void* ptrs[] = {logits, x, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
                         dn_biases_t, out, workspace, topk_ids, topk_w};
@@ -243,12 +244,45 @@ int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int 
   for (const void* p : sh)
     if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
   const DecodePlan plan = decode_plan(E, k, H, I, shared);
-  if (ws_bytes < plan.ws_bytes) return MOEQ4_ERR_WORKSPACE;
+  if (no_alloc) {
+    if (plan.ws_bytes > (size_t)MOEQ4_DECODE_SCRATCH_BYTES) return MOEQ4_ERR_UNSUPPORTED;
+    const hipError_t serr = decode_scratch(&workspace);
+    if (serr != hipSuccess) return MOEQ4_ERR_HIP;
+  } else if (ws_bytes < plan.ws_bytes) {
+    return MOEQ4_ERR_WORKSPACE;
+  }
   const hipError_t err = decode_launch(plan, logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t,
                                        dn_codes_t, dn_scales_t, dn_biases_t, sh_gu_codes_t, sh_gu_scales_t,
                                        sh_gu_biases_t, sh_dn_codes_t, sh_dn_scales_t, sh_dn_biases_t, topk_ids,
                                        topk_w, out, workspace, (hipStream_t)stream);
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
+int moe_decode_ffn_q4(const float* logits, const uint16_t* x, int E, int k, int H, int I,
+                      const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                      const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                      const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                      const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                      const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                      const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                      int32_t* topk_ids, float* topk_w, uint16_t* out, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  return decode_call(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
+                     dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t, sh_dn_codes_t, sh_dn_scales_t,
+                     sh_dn_biases_t, topk_ids, topk_w, out, workspace, ws_bytes, false, stream);
+}
+
+int moe_decode_ffn_q4_noalloc(const float* logits, const uint16_t* x, int E, int k, int H, int I,
+                              const uint8_t* gu_codes_t, const uint16_t* gu_scales_t,
+                              const uint16_t* gu_biases_t, const uint8_t* dn_codes_t,
+                              const uint16_t* dn_scales_t, const uint16_t* dn_biases_t,
+                              const uint8_t* sh_gu_codes_t, const uint16_t* sh_gu_scales_t,
+                              const uint16_t* sh_gu_biases_t, const uint8_t* sh_dn_codes_t,
+                              const uint16_t* sh_dn_scales_t, const uint16_t* sh_dn_biases_t,
+                              int32_t* topk_ids, float* topk_w, uint16_t* out, void* stream) {
+  return decode_call(logits, x, E, k, H, I, gu_codes_t, gu_scales_t, gu_biases_t, dn_codes_t, dn_scales_t,
+                     dn_biases_t, sh_gu_codes_t, sh_gu_scales_t, sh_gu_biases_t, sh_dn_codes_t, sh_dn_scales_t,
+                     sh_dn_biases_t, topk_ids, topk_w, out, nullptr, 0, true, stream);
 }
 
 static int check_small_shape(int T, int E, int k, int H, int I) {

@@ -306,6 +306,11 @@ struct DecodePlan {
 
 DecodePlan decode_plan(int E, int k, int H, int I, bool shared);
 
+// decode.hip: the calling thread's current device's copy of the static scratch
+// array that moe_decode_ffn_q4_noalloc uses as its workspace
+// (MOEQ4_DECODE_SCRATCH_BYTES; its address is looked up once per device)
+hipError_t decode_scratch(void** ptr);
+
 hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_t* x, int E, int k, int H, int I,
                          const uint8_t* gu_q, const uint16_t* gu_s, const uint16_t* gu_b, const uint8_t* dn_q,
                          const uint16_t* dn_s, const uint16_t* dn_b, const uint8_t* sh_gu_q,

@@ -36,6 +36,9 @@
 // activation pairs from LDS and accumulates in fp32.  All of a lane's block
 // loads are issued before any math, behind the activation loads, so the waits
 // are exact (loads complete in issue order).
+#include <atomic>
+#include <mutex>
+
 #include "gemv.h"
 
 namespace moeq4 {
@@ -235,6 +238,45 @@ __global__ __launch_bounds__(kDownThreads) void k_decode_down(
 }
 
 // ----------------------------------------------------------------------------
+// Scratch of moe_decode_ffn_q4_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends, so that the call allocates nothing.  In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// address on a device comes from hipGetSymbolAddress, looked up once per device
+// (with that device current) and kept.
+static __device__ __align__(256) uint8_t scratch[MOEQ4_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+static std::mutex g_scratch_mutex;
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) {
+    note_hip_error(err, "hipGetDevice");
+    return err;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    note_hip_error(hipErrorInvalidDevice, "decode scratch: device index");
+    return hipErrorInvalidDevice;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (err != hipSuccess || !p) {
+        note_hip_error(err != hipSuccess ? err : hipErrorInvalidSymbol, "hipGetSymbolAddress(decode scratch)");
+        return err != hipSuccess ? err : hipErrorInvalidSymbol;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 DecodePlan decode_plan(int E, int k, int H, int I, bool shared) {
