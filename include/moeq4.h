@@ -74,8 +74,10 @@ const char* moe_last_error_detail(void);
 
 /* Block-map tile height used when a call passes block_rows = 0: chosen from
  * the mean rows per expert, T*k/E (section "Match tile size to expert load":
- * tile height is matched to the expert load).  Returns 16, 32, 64 or 128, or
- * a negative error code for invalid T, E, k. */
+ * tile height is matched to the expert load): 64 up to a mean of about 51
+ * rows per expert, 128 up to about 102, 160 above (an expert of up to 160 rows
+ * is then one block, its weights streamed and rebuilt once).  Negative error
+ * code for invalid T, E, k. */
 int moe_default_block_rows(int T, int E, int k);
 
 /* Host-side upper bound on the number of block-map entries for any routing of
@@ -110,7 +112,7 @@ size_t moe_route_workspace_bytes(int T, int E, int k, int block_rows);
  * workspace: device scratch of at least moe_route_workspace_bytes(...) bytes
  *            (may be NULL when that is 0).
  * Sizes: T >= 0, 1 <= k <= min(E, MOEQ4_MAX_TOPK), E <= MOEQ4_MAX_EXPERTS,
- *        block_rows in {0 (default), 16, 32, 64, 128, 256}.
+ *        block_rows in {0 (default), 16, 32, 64, 128, 160, 256}.
  * T = 0 writes zero counts and offsets and num_blocks = 0.
  * Output buffers must not overlap each other or the workspace. */
 int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t* topk_ids,
@@ -179,7 +181,7 @@ int moe_dequant_q4(const uint8_t* codes_t, const uint16_t* scales_t, const uint1
  *                            assignment perm[p]); rows not covered by a block
  *                            are not written.
  * Sizes: T >= 0, K % 64 == 0, K >= 64, N % 16 == 0, N >= 16, 1 <= k <= E,
- *        E <= MOEQ4_MAX_EXPERTS, block_rows in {0, 16, 32, 64, 128, 256} and equal
+ *        E <= MOEQ4_MAX_EXPERTS, block_rows in {0, 16, 32, 64, 128, 160, 256} and equal
  *        to the value given to moe_route, max_blocks >= moe_max_blocks(T, E,
  *        k, block_rows), T*K*2 and E*N*K/2 below 2^31.  Y must not overlap the
  *        inputs. */
@@ -253,7 +255,7 @@ size_t moe_prefill_ffn_chunked_workspace_bytes(int T, int chunk_tokens, int H, i
  * In:  logits float [T, E]; X uint16 (bf16) [T, H]; weights as moe_expert_ffn_q4.
  *      chunk_tokens  tokens per chunk: a multiple of 4, at least 4 (a chunk
  *                    longer than T means one chunk).
- *      block_rows    0 (the default for a full chunk) or 16/32/64/128/256; the
+ *      block_rows    0 (the default for a full chunk) or 16/32/64/128/160/256; the
  *                    same for every chunk.
  *      workspace     device scratch of moe_prefill_ffn_chunked_workspace_bytes(
  *                    T, chunk_tokens, H, I, E, k, block_rows, shared) bytes,
@@ -435,7 +437,7 @@ size_t moe_layer_ffn_workspace_bytes(int T, int H, int I, int E, int k, int bloc
  * (as moe_expert_ffn_q4; the paths differ only in fp32 summation order).
  * In:  logits float [T, E]; X uint16 (bf16) [T, H]; weights as moe_expert_ffn_q4
  *      (tiled layout of moe_prepack_q4; the six sh_* all given or all NULL).
- *      block_rows  0 (default) or 16/32/64/128/256: the block height of the
+ *      block_rows  0 (default) or 16/32/64/128/160/256: the block height of the
  *                  routed path (unused by the other two).
  *      workspace   moe_layer_ffn_workspace_bytes(...) bytes, 16-byte aligned;
  *                  no initial contents needed.

@@ -13,7 +13,7 @@ thread_local char g_detail[256] = "";
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool valid_block_rows(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+bool valid_block_rows(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 160 || bm == 256; }
 
 int check_routing_shape(int T, int E, int k) {
   if (T < 0 || E < 1 || E > MOEQ4_MAX_EXPERTS || k < 1 || k > E) return MOEQ4_ERR_SHAPE;
@@ -98,12 +98,16 @@ const char* moe_strerror(int status) {
 int moe_default_block_rows(int T, int E, int k) {
   const int rc = check_routing_shape(T, E, k);
   if (rc != MOEQ4_OK) return rc;
-  // mean rows per expert, with headroom for the spread around it
+  // mean rows per expert, with headroom for the spread around it.  Below 64
+  // rows the 64-row tall-block kernel (one filled 32-row tile per block)
+  // measured fastest down to ~2 rows per expert; above 128, 160-row blocks
+  // (five tiles) hold a typical expert of a heavy load in one block, so its
+  // weights are streamed and rebuilt once (256-row blocks: on request,
+  // measured slower)
   const long long A = (long long)T * k;
   const long long want = (A * 5 + 4LL * E - 1) / (4LL * E);  // ceil(1.25 * A / E)
-  int bm = 16;
-  while (bm < 128 && bm < want) bm <<= 1;  // 256-row blocks: on request (measured slower)
-  return bm;
+  if (want > 128) return 160;
+  return want > 64 ? 128 : 64;
 }
 
 int moe_max_blocks(int T, int E, int k, int block_rows) {

@@ -519,7 +519,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   const uint16_t* __restrict__ St = a.St;
   const uint16_t* __restrict__ Bt = a.Bt;
   static_assert(BM <= 256 && BM <= WAVES * 64, "the epilogue table holds 256 rows, one per thread");
-  __shared__ EpiTab ep_tab;
+  // the epilogue table lives in the last bytes of the activation buffers,
+  // written once the main loop is done with them
+  EpiTab* const ep_tab = reinterpret_cast<EpiTab*>(reinterpret_cast<char*>(&xs[0][0]) + sizeof(xs) - sizeof(EpiTab));
   uint16_t* const Yout = a.Y;
   const int ldy = a.ldy;
 
@@ -687,9 +689,29 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   constexpr int kAhead = NBUF - 1;           // chunks the DMA runs ahead
   constexpr int kInFlight = (NBUF == 3 ? IPW : 0) + (S > 2 ? kLoadsPerChunk : 0);
   static_assert(kInFlight < 64, "vmcnt range");
+  // Blocks of more than four row tiles hold one activation fragment at a time
+  // (the next row tile's read in flight while this tile's MFMAs run) instead
+  // of every row tile's fragments for two K-steps: the accumulators of five
+  // row tiles leave no room for the double set.
+  constexpr bool LEAN = MF32 > 4 && NF32 > 1;
+  auto lean_step = [&](auto mfa_c, int buf, int ks, const bf16x8* bw) __attribute__((always_inline)) {
+    constexpr int MFA = decltype(mfa_c)::value;
+    const int gi = ks >> 2, s4 = ks & 3;
+    const uint16_t* xb = &xs[buf][col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8)];
+    bf16x8 a_cur = *(const bf16x8*)xb;
+#pragma unroll
+    for (int r = 0; r < MFA; ++r) {
+      bf16x8 a_next = a_cur;
+      if (r + 1 < MFA) a_next = *(const bf16x8*)(xb + (r + 1) * 32 * kKC);
+#pragma unroll
+      for (int f = 0; f < NF32; ++f)
+        acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[f], a_cur, acc[r][f], 0, 0, 0);
+      a_cur = a_next;
+    }
+  };
   auto run = [&](auto mfa_c) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
-    bf16x8 av[2][MFA];
+    bf16x8 av[LEAN ? 1 : 2][LEAN ? 1 : MFA];
     bf16x8 bw[2][NF32];
     if (nfull > 0) {
 #pragma unroll
@@ -714,17 +736,28 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
           // sink them and expose their latency)
           asm volatile("" ::: "memory");
           if (c < nfull) {
-            load_a(mfa_c, av[0], buf, 0);
-            rebuild_b(bw[0], st[u], 0);
+            if constexpr (LEAN) {
+              rebuild_b(bw[0], st[u], 0);
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-              const int p = ks & 1;
-              if (ks < 7) {
-                load_a(mfa_c, av[p ^ 1], buf, ks + 1);
-                rebuild_b(bw[p ^ 1], st[u], ks + 1);
+              for (int ks = 0; ks < 8; ++ks) {
+                const int p = ks & 1;
+                if (ks < 7) rebuild_b(bw[p ^ 1], st[u], ks + 1);
+                lean_step(mfa_c, buf, ks, bw[p]);
+                __builtin_amdgcn_sched_barrier(0);
               }
-              mfma_step(mfa_c, av[p], bw[p]);
-              __builtin_amdgcn_sched_barrier(0);
+            } else {
+              load_a(mfa_c, av[0], buf, 0);
+              rebuild_b(bw[0], st[u], 0);
+#pragma unroll
+              for (int ks = 0; ks < 8; ++ks) {
+                const int p = ks & 1;
+                if (ks < 7) {
+                  load_a(mfa_c, av[p ^ 1], buf, ks + 1);
+                  rebuild_b(bw[p ^ 1], st[u], ks + 1);
+                }
+                mfma_step(mfa_c, av[p], bw[p]);
+                __builtin_amdgcn_sched_barrier(0);
+              }
             }
           }
           // vmcnt <= kInFlight (expcnt and lgkmcnt unconstrained): this wave's DMA
@@ -748,9 +781,13 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
       __syncthreads();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        load_a(mfa_c, av[0], 0, ks);
         rebuild_b(bw[0], st[0], ks);
-        mfma_step(mfa_c, av[0], bw[0]);
+        if constexpr (LEAN) {
+          lean_step(mfa_c, 0, ks, bw[0]);
+        } else {
+          load_a(mfa_c, av[0], 0, ks);
+          mfma_step(mfa_c, av[0], bw[0]);
+        }
       }
     }
   };
@@ -772,11 +809,13 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   constexpr int SROW = WCOLS + 8;    // staged row, 16-byte pad
   constexpr int LPR = WCOLS / 8;     // lanes per staged row
   constexpr int RPI = 64 / LPR;      // rows per store instruction
-  static_assert(WAVES * 32 * SROW * 2 <= (int)sizeof(xs), "staging fits in the activation buffers");
+  static_assert(WAVES * 32 * SROW * 2 + (int)sizeof(EpiTab) <= (int)sizeof(xs),
+                "staging and the epilogue table fit in the activation buffers");
   if constexpr (EPI == kEpiScale) {
+    __syncthreads();  // every wave is done with the activation buffers
     if (tid < rows) {
-      ep_tab.as[tid] = ep_as;
-      ep_tab.w[tid] = ep_as >= 0 ? ep_w : 0.f;
+      ep_tab->as[tid] = ep_as;
+      ep_tab->w[tid] = ep_as >= 0 ? ep_w : 0.f;
     }
   }
   __syncthreads();  // every wave is done with the activation buffers; the table is written
@@ -785,7 +824,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   for (int r = 0; r < MF32; ++r) {
     if (r >= mfa) break;
     {
-      const EpiRow<EPI> er(Yout, ldy, row0, min(r * 32 + col, rows - 1), &ep_tab);
+      const EpiRow<EPI> er(Yout, ldy, row0, min(r * 32 + col, rows - 1), ep_tab);
       if constexpr (PAIRED) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -808,7 +847,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
       const int rr = i * RPI + lane / LPR, cq = lane % LPR;
       const int row = r * 32 + rr, n = n_wave + 8 * cq;
       const uint4 bits = *(const uint4*)&stg[rr * SROW + 8 * cq];
-      if (row < rows && n < NOUT) EpiRow<EPI>(Yout, ldy, row0, row, &ep_tab).store8(n, bits);
+      if (row < rows && n < NOUT) EpiRow<EPI>(Yout, ldy, row0, row, ep_tab).store8(n, bits);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads back before the next tile's writes
   }
@@ -1044,17 +1083,20 @@ const GemmVariant kVariants[] = {
     MOEQ4_GEMM16(32, 2, 3, 8, kEpiPlain),
     MOEQ4_GEMM32(64, 2, 2, 4, kEpiPlain),
     MOEQ4_GEMM32(128, 2, 2, 4, kEpiPlain),
+    MOEQ4_GEMM32(160, 2, 2, 4, kEpiPlain),
     MOEQ4_GEMM32(256, 1, 2, 8, kEpiPlain),
     // FFN: gate+up with SwiGLU, down scaled by the routing weight, shared down + combine
     MOEQ4_GEMM16(16, 2, 4, 8, kEpiSwiglu),
     MOEQ4_GEMM16(32, 2, 3, 8, kEpiSwiglu),
     MOEQ4_GEMM32(64, 2, 2, 4, kEpiSwiglu),
     MOEQ4_GEMM32(128, 2, 2, 4, kEpiSwiglu),
+    MOEQ4_GEMM32(160, 2, 2, 4, kEpiSwiglu),
     MOEQ4_GEMM32(256, 1, 2, 8, kEpiSwiglu),
     MOEQ4_GEMM16(16, 2, 4, 8, kEpiScale),
     MOEQ4_GEMM16(32, 2, 3, 8, kEpiScale),
     MOEQ4_GEMM32(64, 2, 2, 4, kEpiScale),
     MOEQ4_GEMM32(128, 2, 2, 4, kEpiScale),
+    MOEQ4_GEMM32(160, 2, 2, 4, kEpiScale),
     MOEQ4_GEMM32(256, 1, 2, 8, kEpiScale),
     MOEQ4_GEMM16(16, 2, 4, 8, kEpiTerm),
     MOEQ4_GEMM16(32, 2, 3, 8, kEpiTerm),

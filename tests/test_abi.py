@@ -45,18 +45,20 @@ def test_strerror_covers_codes():
                                    (0, 16, 2), (7, 1, 1), (100, 1024, 64)])
 def test_host_helpers(T, E, k):
     bm = q.moe_default_block_rows(T, E, k)
-    assert bm in (16, 32, 64, 128, 256)
-    for b in (16, 32, 64, 128, 256):
+    assert bm in (16, 32, 64, 128, 160, 256)
+    for b in (16, 32, 64, 128, 160, 256):
         assert q.moe_max_blocks(T, E, k, b) == oracle.max_blocks_bound(T * k, E, b)
     assert q.moe_max_blocks(T, E, k, 0) == q.moe_max_blocks(T, E, k, bm)
     assert q.moe_route_workspace_bytes(T, E, k, 0) >= 4 * T * k
 
 
 def test_default_block_rows_follows_expert_load():
-    assert q.moe_default_block_rows(512, 256, 8) == 32     # ~16 rows per expert
-    assert q.moe_default_block_rows(4096, 256, 8) == 128   # ~128 rows per expert
+    assert q.moe_default_block_rows(512, 256, 8) == 64     # ~16 rows per expert: one 64-row block each
+    assert q.moe_default_block_rows(4096, 256, 8) == 160   # ~128 rows per expert: one block each
+    assert q.moe_default_block_rows(16384, 256, 8) == 160  # heavy and skewed
     assert q.moe_default_block_rows(2048, 256, 8) == 128   # ~64 rows per expert
-    assert q.moe_default_block_rows(64, 16, 2) == 16       # ~8 rows per expert
+    assert q.moe_default_block_rows(1024, 256, 8) == 64    # ~32 rows per expert
+    assert q.moe_default_block_rows(64, 16, 2) == 64       # ~8 rows per expert
 
 
 def test_invalid_shapes_rejected():

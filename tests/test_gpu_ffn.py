@@ -67,12 +67,12 @@ class Layer:
         return out
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 160, 256])
 def test_ffn_small(bm):
     Layer(W.custom(70, 64, 16, 2, 256, 128, ffn=True)).check(bm)
 
 
-@pytest.mark.parametrize("bm", [32, 128, 256])
+@pytest.mark.parametrize("bm", [32, 128, 160, 256])
 def test_ffn_odd_groups(bm):
     # H = 320 and I = 192: odd group counts in both matrices; T*k not a multiple of BM
     Layer(W.custom(71, 200, 8, 3, 320, 192, ffn=True)).check(bm)
@@ -113,7 +113,7 @@ def test_ffn_oversized_block_bound():
 _C3_REF = {}
 
 
-@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("bm", [128, 160, 256])
 def test_ffn_workload_full_size(bm):
     # the expert-FFN workload: T=4096, 8 of 256 experts + shared, H=2048, I=512;
     # every one of the 4096 x 2048 outputs against the oracle

@@ -66,7 +66,7 @@ ROUTE_CASES = [
 
 
 @pytest.mark.parametrize("kind,T,E,k", ROUTE_CASES)
-@pytest.mark.parametrize("bm", [16, 128, 256])
+@pytest.mark.parametrize("bm", [16, 128, 160, 256])
 def test_route_bit_exact(kind, T, E, k, bm):
     _check_route(_logits(kind, T, E), k, bm)
 
@@ -169,12 +169,12 @@ def _gemm_full(w, bm, seed_logits=None, name=None):
     return Y, g, p
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 160, 256])
 def test_gemm_tiny_workload(bm):
     _gemm_full(W.WORKLOADS[1], bm)
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 160, 256])
 def test_gemm_ragged(bm):
     # N = 272 leaves a partial N tile; K = 320 is five K chunks; blocks end mid sub-tile
     _gemm_full(W.custom(31, 200, 8, 3, 320, 272), bm)
@@ -189,6 +189,20 @@ def test_gemm_ragged(bm):
 ])
 def test_gemm_edge_shapes(T, E, k, K, N, bm):
     _gemm_full(W.custom(32, T, E, k, K, N), bm)
+
+
+@pytest.mark.parametrize("T,E,k,K,N", [
+    (200, 8, 3, 512, 272),      # four chunks; a partial 512-column tile
+    (300, 16, 2, 1024, 128),    # narrower than one workgroup's 512 columns
+    (100, 64, 8, 2048, 512),    # the prefill shape with a few rows per expert
+    (50, 4, 2, 1536, 48),       # twelve chunks; three 16-column tiles
+    (40, 2, 1, 512, 16),        # one 16-column tile
+    (64, 16, 2, 4096, 64),      # activations too large for LDS: the streaming kernel
+])
+def test_gemm_short_blocks_lds_resident(T, E, k, K, N):
+    # 32-row blocks whose activations fit in LDS for all of K (K a multiple of
+    # 512, 32*K*2 <= 128 KB) run the LDS-resident kernel; others the streaming one
+    _gemm_full(W.custom(35, T, E, k, K, N), 32)
 
 
 def test_gemm_hot_expert():
@@ -209,7 +223,7 @@ def test_gemm_prefill_chunk_full_size_other_heights(bm):
     _gemm_full(w, bm, name=f"{w.name} BM={bm}")
 
 
-@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("bm", [128, 160, 256])
 def test_gemm_skewed_full_size(bm):
     # the skewed workload (T=16384, Zipf-biased logits): all 67,108,864 outputs
     w = W.WORKLOADS[4]
