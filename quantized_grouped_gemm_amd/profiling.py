@@ -134,7 +134,8 @@ def main(argv=None):
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
-    t.add_argument("--copy-regex", default="elementwise")
+    # the copy is torch.mul(src, 1.0, out=dst); the fill that creates src reads nothing
+    t.add_argument("--copy-regex", default="MulFunctor")
     t.add_argument("--per-step", type=int, default=1, help="dispatches of the matching kernels per step")
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
