@@ -188,6 +188,13 @@ __device__ __forceinline__ f32x4 quad(const f32x16& a, int j) {
   return f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
 }
 
+// silu(g) * u = g * u / (1 + e^-g), with the hardware exponential and
+// reciprocal (each within a few fp32 ulp; the result is then rounded to bf16).
+// g -> -inf: e^-g = inf, reciprocal 0, result -0; g -> +inf: e^-g = 0, result g * u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
 // Epilogue of one output row (row `row` of the block starting at sorted row row0).
 template <int EPI>
 struct EpiRow {
@@ -209,7 +216,7 @@ struct EpiRow {
       if (!y) return;
     }
     if constexpr (EPI == kEpiSwiglu) {
-      y[n] = f32_to_bf16_bits(v / (1.f + expf(-v)) * u);
+      y[n] = f32_to_bf16_bits(silu_mul(v, u));
     } else if constexpr (EPI == kEpiScale) {
       y[n] = term_bits(w * v);
     } else if constexpr (EPI == kEpiTerm) {
@@ -223,7 +230,7 @@ struct EpiRow {
     uint32_t b[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if constexpr (EPI == kEpiSwiglu) b[q] = f32_to_bf16_bits(v[q] / (1.f + expf(-v[q])) * u[q]);
+      if constexpr (EPI == kEpiSwiglu) b[q] = f32_to_bf16_bits(silu_mul(v[q], u[q]));
       else if constexpr (EPI == kEpiScale) b[q] = term_bits(w * v[q]);
       else if constexpr (EPI == kEpiTerm) b[q] = term_bits(v[q]);
       else b[q] = f32_to_bf16_bits(v[q]);
@@ -594,6 +601,12 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   // The tail chunk of an odd G has only 8 columns: the other slots get the
   // out-of-range offset (the range check covers the vector offset only, so the
   // row must not be overrun through the chunk offset).
+  // instruction i (0..IPW-1) of dma_x(c, buf, false) on its own
+  auto dma_op = [&](int c, int buf, int i) __attribute__((always_inline)) {
+    const int off = xoff[i];  // (passing xoff[i] itself drops the kernel's host-side stub)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, (lds_void*)&xs[buf][4 * (wave * IPW + i) * kKC], 16, off,
+                                             c * kKC * 2, 0, 0);
+  };
   auto dma_x = [&](int c, int buf, bool tail) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -620,6 +633,16 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
       s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, gbase, 0, 0);
       s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, gbase, 0, 0);
     }
+  };
+  // instruction j (0..4*NF32-1) of load(s, c) on its own: fragment j/4, part j%4
+  auto load_op = [&](St32& s, int c, int j) __attribute__((always_inline)) {
+    const int cl = min(c, nfull - 1);
+    const int f = j >> 2, part = j & 3;
+    const int base = (cl * NT + tile16[f]) * 1024 + r16 * 16;
+    const int gbase = ((cl * NT + tile16[f]) * 32 + 2 * r16) * 2;
+    if (part < 2) s.w[f][part] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, base + (2 * half + part) * 256, 0, 0);
+    else if (part == 2) s.s[f] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, gbase, 0, 0);
+    else s.b[f] = __builtin_amdgcn_raw_buffer_load_b32(bsrc, gbase, 0, 0);
   };
   auto load_tail = [&](St32& s) __attribute__((always_inline)) {
     const int c = nfull;
@@ -689,25 +712,59 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   constexpr int kAhead = NBUF - 1;           // chunks the DMA runs ahead
   constexpr int kInFlight = (NBUF == 3 ? IPW : 0) + (S > 2 ? kLoadsPerChunk : 0);
   static_assert(kInFlight < 64, "vmcnt range");
+  // The next chunks' loads are issued a few per K-step over the first kSpread
+  // K-steps, after that step's MFMAs, not all at the top of the chunk: issued
+  // together, the workgroup's waves queue behind each other at the vector
+  // memory unit and none of them reaches its MFMAs meanwhile.  The order is
+  // that of the burst it replaces (three buffers: weights, then DMA; two: DMA,
+  // then weights), so the counted wait at the end of the chunk is unchanged.
+  constexpr int kOps = IPW + kLoadsPerChunk;
+  constexpr int kSpread = 4;
+  constexpr int kPer = (kOps + kSpread - 1) / kSpread;
+  auto issue_ops = [&](St32& s, int c, int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int j = ks * kPer + t;
+      if (j >= kOps) break;
+      const int cd = min(c + kAhead, nfull - 1), bd = (c + kAhead) % NBUF;
+      if constexpr (NBUF == 3) {
+        if (j < kLoadsPerChunk) load_op(s, c + S - 1, j);
+        else dma_op(cd, bd, j - kLoadsPerChunk);
+      } else {
+        if (j < IPW) dma_op(cd, bd, j);
+        else load_op(s, c + S - 1, j - IPW);
+      }
+    }
+  };
   // Blocks of more than four row tiles hold one activation fragment at a time
   // (the next row tile's read in flight while this tile's MFMAs run) instead
   // of every row tile's fragments for two K-steps: the accumulators of five
   // row tiles leave no room for the double set.
   constexpr bool LEAN = MF32 > 4 && NF32 > 1;
-  auto lean_step = [&](auto mfa_c, int buf, int ks, const bf16x8* bw) __attribute__((always_inline)) {
+  // the activation fragment of row tile 0 at K-step ks of buffer buf
+  auto lean_first = [&](int buf, int ks) __attribute__((always_inline)) {
+    const int gi = ks >> 2, s4 = ks & 3;
+    return *(const bf16x8*)&xs[buf][col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8)];
+  };
+  // a0 holds row tile 0's fragment of K-step ks on entry and, when ks + 1 < kend,
+  // row tile 0's fragment of K-step ks + 1 on return (read during the last row
+  // tile's MFMAs, so no K-step starts on an LDS read it has just issued)
+  auto lean_step = [&](auto mfa_c, int buf, int ks, int kend, const bf16x8* bw, bf16x8& a0) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
     const int gi = ks >> 2, s4 = ks & 3;
     const uint16_t* xb = &xs[buf][col * kKC + (((gi * 8 + half * 4 + s4) ^ (col & 15)) * 8)];
-    bf16x8 a_cur = *(const bf16x8*)xb;
+    bf16x8 a_cur = a0;
 #pragma unroll
     for (int r = 0; r < MFA; ++r) {
       bf16x8 a_next = a_cur;
       if (r + 1 < MFA) a_next = *(const bf16x8*)(xb + (r + 1) * 32 * kKC);
+      else if (ks + 1 < kend) a_next = lean_first(buf, ks + 1);
 #pragma unroll
       for (int f = 0; f < NF32; ++f)
         acc[r][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[f], a_cur, acc[r][f], 0, 0, 0);
       a_cur = a_next;
     }
+    a0 = a_cur;
   };
   auto run = [&](auto mfa_c) __attribute__((always_inline)) {
     constexpr int MFA = decltype(mfa_c)::value;
@@ -725,24 +782,17 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
         for (int u = 0; u < S; ++u) {
           const int c = c0 + u;
           const int buf = c % NBUF;
-          if constexpr (NBUF == 3) {
-            load(st[(u + S - 1) % S], c + S - 1);
-            dma_x(min(c + kAhead, nfull - 1), (c + kAhead) % NBUF, false);
-          } else {
-            dma_x(min(c + kAhead, nfull - 1), (c + kAhead) % NBUF, false);
-            load(st[(u + S - 1) % S], c + S - 1);
-          }
-          // keep the loads ahead of the compute (the scheduler would otherwise
-          // sink them and expose their latency)
-          asm volatile("" ::: "memory");
+          St32& nxt = st[(u + S - 1) % S];
           if (c < nfull) {
             if constexpr (LEAN) {
               rebuild_b(bw[0], st[u], 0);
+              bf16x8 a0 = lean_first(buf, 0);
 #pragma unroll
               for (int ks = 0; ks < 8; ++ks) {
                 const int p = ks & 1;
                 if (ks < 7) rebuild_b(bw[p ^ 1], st[u], ks + 1);
-                lean_step(mfa_c, buf, ks, bw[p]);
+                lean_step(mfa_c, buf, ks, 8, bw[p], a0);
+                if (ks < kSpread) issue_ops(nxt, c, ks);
                 __builtin_amdgcn_sched_barrier(0);
               }
             } else {
@@ -756,9 +806,13 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
                   rebuild_b(bw[p ^ 1], st[u], ks + 1);
                 }
                 mfma_step(mfa_c, av[p], bw[p]);
+                if (ks < kSpread) issue_ops(nxt, c, ks);
                 __builtin_amdgcn_sched_barrier(0);
               }
             }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < kSpread; ++ks) issue_ops(nxt, c, ks);
           }
           // vmcnt <= kInFlight (expcnt and lgkmcnt unconstrained): this wave's DMA
           // of chunk c+1 has landed in LDS, and its LDS reads of this chunk have
@@ -783,7 +837,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
       for (int ks = 0; ks < 4; ++ks) {
         rebuild_b(bw[0], st[0], ks);
         if constexpr (LEAN) {
-          lean_step(mfa_c, 0, ks, bw[0]);
+          bf16x8 a0 = lean_first(0, ks);
+          lean_step(mfa_c, 0, ks, ks + 1, bw[0], a0);
         } else {
           load_a(mfa_c, av[0], 0, ks);
           mfma_step(mfa_c, av[0], bw[0]);

@@ -7,18 +7,24 @@
 // and a block map lists the fixed-size blocks the grouped GEMM processes.  The
 // whole sequence stays on the GPU: the block count never goes to the host.
 //
-// Two or three kernels, all on the caller's stream:
+// Two kernels up to kSmallAssignMax assignments, three above, all on the
+// caller's stream:
 //   k_topk_rank      one workgroup of 16 waves per "chunk" of tokens, one wave
 //                    per token: top-k by k rounds of a wave-wide argmax over
 //                    order-preserving integer keys (DPP max + ballot), softmax
-//                    over the k selected logits; then the chunk's histogram
-//                    and each assignment's stable rank among same-expert
-//                    assignments of the chunk (ballot match masks over the
-//                    expert-id bits + popcounts).
-//   k_scan_blockmap  one workgroup: per-expert exclusive scan over chunks,
-//                    counts, offsets, block counts and their scan, block map;
-//                    for up to kFusedScatterMax assignments also the scatter.
-//   k_scatter        (larger inputs) one thread per assignment: perm, inv_perm.
+//                    over the k selected logits; then (large inputs only) the
+//                    chunk's histogram and each assignment's stable rank
+//                    among same-expert assignments of the chunk (ballot match
+//                    masks over the expert-id bits + popcounts).
+//   k_route_small    (small inputs) one workgroup does the rest from the
+//                    expert ids alone: each wave ranks a contiguous range of
+//                    assignments the same way, a scan over the waves gives
+//                    each expert's count and per-wave bases; then offsets,
+//                    block map and the scatter.
+//   k_scan_blockmap  (large inputs) one workgroup: per-expert exclusive scan
+//                    over chunks, counts, offsets, block counts and their
+//                    scan, block map.
+//   k_scatter        (large inputs) one thread per assignment: perm, inv_perm.
 // Only integer adds decide positions, so every output is deterministic.
 #include "common.h"
 
@@ -28,10 +34,10 @@ constexpr int kRouteWaves = 16;            // waves per chunk workgroup
 constexpr int kRouteThreads = kRouteWaves * 64;
 constexpr int kChunkAssignMax = 2048;      // assignments per chunk (LDS bound)
 constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / kRouteWaves;
-constexpr int kFusedScatterMax = 8192;     // assignments the scan workgroup also scatters
-constexpr int kFusedBasesMax = 8192;       // chunk bases it keeps in LDS for that (32 KB)
+constexpr int kSmallAssignMax = 8192;      // assignments one workgroup ranks and scatters
 constexpr int kScanThreads = 1024;
-constexpr int kFusedPerThread = kFusedScatterMax / kScanThreads;  // assignments per scan thread
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kSmallSlicesPerWave = kSmallAssignMax / 64 / kScanWaves;  // 64-assignment slices per wave
 constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 
 // ----------------------------------------------------------------------------
@@ -41,7 +47,7 @@ constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 // Selection compares order-preserving integer keys of the logits (wave_topk).
 template <int VPT>
 __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
-    const float* __restrict__ logits, int T, int E, int k, int tpc, int nbits,
+    const float* __restrict__ logits, int T, int E, int k, int tpc, int nbits, int hist,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts,
     int32_t* __restrict__ local_rank) {
   extern __shared__ int smem[];
@@ -55,7 +61,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
   const int t0 = chunk * tpc;
   const int ntok = min(tpc, T - t0);
 
-  for (int i = threadIdx.x; i < NW * E; i += blockDim.x) cnt[i] = 0;
+  if (hist)
+    for (int i = threadIdx.x; i < NW * E; i += blockDim.x) cnt[i] = 0;
 
   // the next token's logits are in flight while the current one is selected
   float vn[VPT];
@@ -85,6 +92,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
       sids[i * k + lane] = my_id;
     }
   }
+  if (!hist) return;  // small inputs: k_route_small ranks from the ids
   __syncthreads();
 
   // ---- in-chunk histogram and stable ranks
@@ -178,29 +186,67 @@ __device__ int block_exclusive_scan(int v, int* scratch /* >= kScanThreads/64 + 
   return r;
 }
 
+// From each expert's count (thread e < E holds cnt_e): counts, offsets, block
+// offsets, the block count and the block map; offs_s / boffs_s (E + 1 ints in
+// LDS) keep the offsets and block offsets for the caller.  Every thread of the
+// kScanThreads workgroup calls it.
+__device__ void counts_to_blockmap(int cnt_e, int E, int BM, int A, int32_t* __restrict__ counts,
+                                   int32_t* __restrict__ offsets, int32_t* __restrict__ blocks,
+                                   int32_t* __restrict__ num_blocks, int* offs_s, int* boffs_s, int* scratch) {
+  const int tid = threadIdx.x;
+  // Below 2^16 assignments both scans run as one over (count | blocks << 16):
+  // the block total stays below E + A / BM < 2^15, so neither field carries
+  // into the other.
+  int total, nb_total, off, boff;
+  const int nb = tid < E ? (cnt_e + BM - 1) / BM : 0;
+  if (A < 65536) {
+    const int pk = block_exclusive_scan(tid < E ? cnt_e | (nb << 16) : 0, scratch, &total);
+    off = pk & 0xFFFF;
+    boff = pk >> 16;
+    nb_total = total >> 16;
+    total &= 0xFFFF;
+  } else {
+    off = block_exclusive_scan(tid < E ? cnt_e : 0, scratch, &total);
+    boff = block_exclusive_scan(nb, scratch, &nb_total);
+  }
+  if (tid < E) {
+    counts[tid] = cnt_e;
+    offsets[tid] = off;
+    offs_s[tid] = off;
+    boffs_s[tid] = boff;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    offs_s[E] = total;
+    boffs_s[E] = nb_total;
+    *num_blocks = nb_total;
+  }
+  __syncthreads();
+
+  // block map: entry b belongs to the expert e with boffs[e] <= b < boffs[e+1]
+  for (int b = tid; b < nb_total; b += kScanThreads) {
+    int lo = 0, hi = E;  // invariant: boffs_s[lo] <= b < boffs_s[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (boffs_s[mid] <= b) lo = mid; else hi = mid;
+    }
+    const int i = b - boffs_s[lo];
+    const int cnt = offs_s[lo + 1] - offs_s[lo];
+    blocks[4 * (size_t)b + 0] = lo;
+    blocks[4 * (size_t)b + 1] = offs_s[lo] + i * BM;
+    blocks[4 * (size_t)b + 2] = min(BM, cnt - i * BM);
+    blocks[4 * (size_t)b + 3] = i;
+  }
+}
+
 __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
-    int32_t* __restrict__ chunk_counts, int nchunks, int E, int BM, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks,
-    int fuse_scatter, const int32_t* __restrict__ ids, int A, int k, int tpc,
-    const int32_t* __restrict__ local_rank, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
-  extern __shared__ int cb_s[];  // fused scatter: the chunk bases [nchunks][E]
+    int32_t* __restrict__ chunk_counts, int nchunks, int E, int BM, int A, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks) {
   __shared__ int part[kScanThreads];
   __shared__ int offs_s[MOEQ4_MAX_EXPERTS + 1];
   __shared__ int boffs_s[MOEQ4_MAX_EXPERTS + 1];
   __shared__ int scratch[kScanThreads / 64 + 1];
   const int tid = threadIdx.x;
-
-  // ---- fused scatter: its inputs do not depend on the scan, so their loads
-  // go out first (indices clamped: unconditional loads)
-  int pf_e[kFusedPerThread], pf_r[kFusedPerThread];
-  if (fuse_scatter && A > 0) {
-#pragma unroll
-    for (int i = 0; i < kFusedPerThread; ++i) {
-      const int a = min(tid + i * kScanThreads, A - 1);
-      pf_e[i] = ids[a];
-      pf_r[i] = local_rank[a];
-    }
-  }
 
   // ---- per expert, exclusive scan over chunks (S threads per expert).  Each
   // thread holds its chunk counts in registers, fetched with independent loads.
@@ -241,10 +287,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
 #pragma unroll
     for (int i = 0; i < kScanRegs; ++i) {
       const int c = c_lo + i;
-      if (c < c_hi) {
-        if (fuse_scatter) cb_s[c * E + e] = run;  // bases stay in LDS for the scatter below
-        else chunk_counts[(size_t)c * E + e] = run;
-      }
+      if (c < c_hi) chunk_counts[(size_t)c * E + e] = run;
       run += vals[i];
     }
   } else if (act) {
@@ -255,66 +298,84 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
       run += x;
     }
   }
+  counts_to_blockmap(cnt_e, E, BM, A, counts, offsets, blocks, num_blocks, offs_s, boffs_s, scratch);
+}
 
-  // ---- counts, offsets, block offsets.  Below 2^16 assignments both scans
-  // run as one over (count | blocks << 16): the block total stays below
-  // E + A / BM < 2^15, so neither field carries into the other.
-  int total, nb_total, off, boff;
-  const int nb = tid < E ? (cnt_e + BM - 1) / BM : 0;
-  if (A < 65536) {
-    const int pk = block_exclusive_scan(tid < E ? cnt_e | (nb << 16) : 0, scratch, &total);
-    off = pk & 0xFFFF;
-    boff = pk >> 16;
-    nb_total = total >> 16;
-    total &= 0xFFFF;
-  } else {
-    off = block_exclusive_scan(tid < E ? cnt_e : 0, scratch, &total);
-    boff = block_exclusive_scan(nb, scratch, &nb_total);
+// ----------------------------------------------------------------------------
+// Up to kSmallAssignMax assignments: histogram, stable ranks, offsets, block
+// map and scatter in one workgroup, from the expert ids alone.  Wave w takes
+// the contiguous assignments [w * spw * 64, (w + 1) * spw * 64) in slices of
+// 64, in order: within a slice an assignment's rank among same-expert
+// assignments comes from ballot match masks over the expert-id bits, across
+// the wave's slices from its per-expert counter in LDS, across waves from
+// the scan of those counters.  Position = offsets[e] + (same-expert
+// assignments before it), the stable counting sort.
+__global__ __launch_bounds__(kScanThreads) void k_route_small(
+    const int32_t* __restrict__ ids, int A, int E, int BM, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ uint16_t cnt[kScanWaves][MOEQ4_MAX_EXPERTS];  // per-wave counts, then per-wave bases
+  __shared__ int offs_s[MOEQ4_MAX_EXPERTS + 1];
+  __shared__ int boffs_s[MOEQ4_MAX_EXPERTS + 1];
+  __shared__ int scratch[kScanThreads / 64 + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nslices = (A + 63) >> 6;
+  const int spw = (nslices + kScanWaves - 1) / kScanWaves;  // <= kSmallSlicesPerWave
+
+  // this wave's expert ids first (clamped indices: unconditional loads)
+  int eid[kSmallSlicesPerWave];
+#pragma unroll
+  for (int s = 0; s < kSmallSlicesPerWave; ++s) {
+    const int a = min((wv * spw + s) * 64 + lane, max(A - 1, 0));
+    eid[s] = A > 0 ? ids[a] : 0;
   }
-  if (tid < E) {
-    counts[tid] = cnt_e;
-    offsets[tid] = off;
-    offs_s[tid] = off;
-    boffs_s[tid] = boff;
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    offs_s[E] = total;
-    boffs_s[E] = nb_total;
-    *num_blocks = nb_total;
+  for (int e = lane; e < E; e += 64) cnt[wv][e] = 0;  // this wave's own row
+
+  const uint64_t lt = lanemask_lt();
+  int rank[kSmallSlicesPerWave];
+#pragma unroll
+  for (int s = 0; s < kSmallSlicesPerWave; ++s) {
+    rank[s] = -1;
+    if (s >= spw) continue;
+    const int a = (wv * spw + s) * 64 + lane;
+    const bool valid = a < A;
+    const int e = valid ? min(max(eid[s], 0), E - 1) : 0;
+    eid[s] = e;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      match &= bit ? bb : ~bb;
+    }
+    if (valid) {
+      const int old = cnt[wv][e];
+      rank[s] = old + __popcll(match & lt);
+      // the highest lane of each match group publishes the new count (a
+      // wave's LDS operations complete in order, so the next slice sees it)
+      if ((match >> lane) == 1ull) cnt[wv][e] = (uint16_t)(old + __popcll(match));
+    }
   }
   __syncthreads();
-
-  // ---- block map: entry b belongs to the expert e with boffs[e] <= b < boffs[e+1]
-  for (int b = tid; b < nb_total; b += kScanThreads) {
-    int lo = 0, hi = E;  // invariant: boffs_s[lo] <= b < boffs_s[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (boffs_s[mid] <= b) lo = mid; else hi = mid;
-    }
-    const int i = b - boffs_s[lo];
-    const int cnt = offs_s[lo + 1] - offs_s[lo];
-    blocks[4 * (size_t)b + 0] = lo;
-    blocks[4 * (size_t)b + 1] = offs_s[lo] + i * BM;
-    blocks[4 * (size_t)b + 2] = min(BM, cnt - i * BM);
-    blocks[4 * (size_t)b + 3] = i;
-  }
-
-  // ---- small inputs: the scatter too (chunk bases were written to LDS above,
-  // before the barriers of the scans)
-  if (fuse_scatter) {
-    const int ktpc = k * tpc;
+  int cnt_e = 0;
+  if (tid < E) {
+    int c[kScanWaves];
 #pragma unroll
-    for (int i = 0; i < kFusedPerThread; ++i) {
-      const int a = tid + i * kScanThreads;
-      if (a < A) {
-        const int e = pf_e[i];
-        const int c = a / ktpc;  // the chunk of token a / k
-        const int p = offs_s[e] + cb_s[c * E + e] + pf_r[i];
-        if (p >= 0 && p < A) perm[p] = a;
-        inv_perm[a] = p;
-      }
+    for (int w = 0; w < kScanWaves; ++w) c[w] = cnt[w][tid];
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) {
+      cnt[w][tid] = (uint16_t)cnt_e;
+      cnt_e += c[w];
     }
+  }
+  counts_to_blockmap(cnt_e, E, BM, A, counts, offsets, blocks, num_blocks, offs_s, boffs_s, scratch);
+  // (counts_to_blockmap ends its scans with a barrier: the bases are visible)
+#pragma unroll
+  for (int s = 0; s < kSmallSlicesPerWave; ++s) {
+    if (rank[s] < 0) continue;
+    const int a = (wv * spw + s) * 64 + lane;
+    const int p = offs_s[eid[s]] + cnt[wv][eid[s]] + rank[s];
+    if (p >= 0 && p < A) perm[p] = a;
+    inv_perm[a] = p;
   }
 }
 
@@ -365,6 +426,8 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
                         hipStream_t stream) {
   int32_t* chunk_counts = (int32_t*)((char*)workspace + plan.ws_chunk_counts);
   int32_t* local_rank = (int32_t*)((char*)workspace + plan.ws_local_rank);
+  const int A = T * k;
+  const int small = A <= kSmallAssignMax;
   hipError_t err = hipSuccess;
   if (plan.nchunks > 0) {
     const size_t shmem = sizeof(int) * (size_t)plan.tpc * k + sizeof(uint16_t) * (size_t)kRouteWaves * E;
@@ -375,22 +438,18 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
     else if (E <= 512) fn = (const void*)&k_topk_rank<8>;
     else fn = (const void*)&k_topk_rank<16>;
     err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T, E, k,
-                 plan.tpc, plan.nbits, ids, w, chunk_counts, local_rank);
+                 plan.tpc, plan.nbits, small ? 0 : 1, ids, w, chunk_counts, local_rank);
     if (err != hipSuccess) return err;
   }
-  const int A = T * k;
-  const int fuse = A <= kFusedScatterMax && (long long)plan.nchunks * E <= kFusedBasesMax;
-  const size_t cb_bytes = fuse ? sizeof(int) * (size_t)plan.nchunks * E : 0;
-  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), cb_bytes, stream, chunk_counts,
-               plan.nchunks, E, BM, counts, offsets, blocks, num_blocks, fuse, (const int32_t*)ids, A, k,
-               plan.tpc, (const int32_t*)local_rank, perm, inv_perm);
+  if (small)
+    return launch("k_route_small", (const void*)&k_route_small, dim3(1), dim3(kScanThreads), 0, stream,
+                  (const int32_t*)ids, A, E, BM, plan.nbits, counts, offsets, blocks, num_blocks, perm, inv_perm);
+  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), 0, stream, chunk_counts,
+               plan.nchunks, E, BM, A, counts, offsets, blocks, num_blocks);
   if (err != hipSuccess) return err;
-  if (A > 0 && !fuse) {
-    err = launch("k_scatter", (const void*)&k_scatter, dim3((A + 255) / 256), dim3(256), 0, stream,
-                 (const int32_t*)ids, A, E, k, plan.tpc, (const int32_t*)offsets,
-                 (const int32_t*)chunk_counts, (const int32_t*)local_rank, perm, inv_perm);
-  }
-  return err;
+  return launch("k_scatter", (const void*)&k_scatter, dim3((A + 255) / 256), dim3(256), 0, stream,
+                (const int32_t*)ids, A, E, k, plan.tpc, (const int32_t*)offsets, (const int32_t*)chunk_counts,
+                (const int32_t*)local_rank, perm, inv_perm);
 }
 
 }  // namespace moeq4
