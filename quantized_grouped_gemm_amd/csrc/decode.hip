@@ -23,10 +23,11 @@
 //                    up tile t + I/16 of expert e_j and writes
 //                    h_j[16t..16t+16) = bf16(silu(g) * u).  Workgroup 0 also
 //                    writes the k ids and softmax weights.
-//   k_decode_down    one 16-wave workgroup per 16-row tile of H: the sum over
+//   k_decode_down    one 16-wave workgroup per 8 rows of H (half a 16-row
+//                    tile, so the H / 8 workgroups cover every CU): the sum over
 //                    all selected experts of w_j * (Wd[e_j] h_j), with w = 1 for
-//                    the shared expert, reduced across the waves in a fixed
-//                    order, so the result is the same run after run.
+//                    the shared expert, reduced in a fixed order, so the result
+//                    is the same run after run.
 //
 // GEMV inner loop: a wave reads one 1 KB block of the tiled layout (16 rows x
 // 128 K values; lane 16q+r holds 32 codes of row r) and rebuilds every weight
@@ -48,7 +49,7 @@ constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecBatch = 4;          // weight blocks a gate/up wave keeps in flight
 constexpr int kDownWaves = 16;        // down workgroup
 constexpr int kDownThreads = kDownWaves * 64;
-constexpr int kDownBatch = 3;         // weight blocks a down wave keeps in flight
+constexpr int kDownBatch = 2;         // item pairs a down wave keeps in flight
 
 // Sum over the chunks c = c_first, c_first + c_step, ... of the full chunks
 // (nfull of them), batched so that a wave keeps kDecBatch block loads in flight.
@@ -158,15 +159,54 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_gateup(
 }
 
 // ----------------------------------------------------------------------------
+// Down projection over half tiles: workgroup u covers output rows [8u, 8u + 8),
+// half h = u & 1 of 16-row tile u / 2, so H / 8 workgroups spread the step's
+// weight reads and rebuilds over all CUs.  The work items are the blocks
+// (selected expert j, chunk c) of that tile, full chunks first, then the
+// half-size last chunks of an odd group count.  A wave takes two items at a
+// time: lane 16q + r reads K quarter q of row 8h + (r & 7) of item 2p + (r >> 3),
+// so all 64 lanes load and rebuild.  Partial sums meet in a fixed order (the
+// four K quarters, then the two items of a pair, then the waves), so the result
+// is the same run after run.
+struct DownItem {
+  int j, c;   // selected expert slot (k = shared expert) and chunk
+  bool tail;  // the half-size last chunk of an odd group count
+};
+
+__device__ __forceinline__ DownItem down_item(int it, int nfull, int J) {
+  DownItem d;
+  const int nf = J * nfull;
+  if (it < nf) {
+    d.j = it / nfull;
+    d.c = it % nfull;
+    d.tail = false;
+  } else {
+    d.j = it - nf;
+    d.c = nfull;
+    d.tail = true;
+  }
+  return d;
+}
+
+// a lane's share of one item: 32 codes of a full chunk (16 of a tail chunk)
+// and the scale / bias of its row's groups
+struct DownLoad {
+  uint4 codes;
+  uint32_t s2, b2;
+  float w;  // routing weight of the item's expert (1 for the shared expert)
+};
+
 __global__ __launch_bounds__(kDownThreads) void k_decode_down(
     int k, int H, int I, int J, const uint8_t* __restrict__ dn_q, const uint16_t* __restrict__ dn_s,
     const uint16_t* __restrict__ dn_b, const uint8_t* __restrict__ sh_q, const uint16_t* __restrict__ sh_s,
     const uint16_t* __restrict__ sh_b, const int32_t* __restrict__ ids_ws, const float* __restrict__ w_ws,
     const uint16_t* __restrict__ h_ws, uint16_t* __restrict__ out) {
   extern __shared__ uint4 dsm[];
-  __shared__ float red[kDownWaves][16];
+  __shared__ float red[kDownWaves][8];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x;  // 16-row tile of the output
+  const int t = blockIdx.x >> 1;                       // 16-row tile of the output
+  const int row = 8 * (blockIdx.x & 1) + (lane & 7);   // the lane's row inside the tile
+  const int q = lane >> 4, sub = (lane >> 3) & 1;      // K quarter, item of the pair
 
   const Staged<kDownPieces> hr = stage_load<kDownPieces>(h_ws, J * (I / 8));
   uint4* hl = dsm;  // [J][I] bf16: h of every expert of the step
@@ -174,66 +214,78 @@ __global__ __launch_bounds__(kDownThreads) void k_decode_down(
   const size_t mat_codes = (size_t)H * I / 2;
   const size_t mat_groups = (size_t)H * (I / kGroup);
   const int G = I / kGroup, nfull = G / 2;
-  const int nb = J * nfull;  // full blocks: (expert, chunk); wave w takes w, w+16, ...
-  auto mat = [&](int j, size_t e) {
-    TiledMat m1;
-    m1.q = j < k ? dn_q + e * mat_codes : sh_q;
-    m1.s = j < k ? dn_s + e * mat_groups : sh_s;
-    m1.b = j < k ? dn_b + e * mat_groups : sh_b;
-    m1.NT = H / 16;
-    return m1;
-  };
+  const int NT = H / 16;
+  const int nitems = J * nfull + ((G & 1) ? J : 0);
+  const int npairs = (nitems + 1) / 2;
+
   float acc = 0.f;
-  FullBlock f[kDownBatch];
-  float wb[kDownBatch];
-  // loads are unconditional (indices clamped, surplus results unused), so the
-  // expert ids arrive with one wait and the wait for h below is exact
-  auto load_batch = [&](int b0) {
+  DownLoad f[kDownBatch];
+  // loads are unconditional (item index clamped, surplus results unused), so
+  // the expert ids arrive with one wait and the wait for h below is exact
+  auto load_batch = [&](int p0) {
     int eb[kDownBatch];
 #pragma unroll
     for (int i = 0; i < kDownBatch; ++i) {
-      const int b = min(b0 + kDownWaves * i, nb - 1);
-      const int j = b / nfull, jc = min(j, k - 1);
+      const DownItem d = down_item(min(2 * (p0 + kDownWaves * i) + sub, nitems - 1), nfull, J);
+      const int jc = min(d.j, k - 1);
       eb[i] = ids_ws[jc];
       const float wl = w_ws[jc];
-      wb[i] = j < k ? wl : 1.f;
+      f[i].w = d.j < k ? wl : 1.f;
     }
 #pragma unroll
     for (int i = 0; i < kDownBatch; ++i) {
-      const int b = min(b0 + kDownWaves * i, nb - 1);
-      f[i] = load_full(mat(b / nfull, (size_t)eb[i]), t, b % nfull, lane);
+      const DownItem d = down_item(min(2 * (p0 + kDownWaves * i) + sub, nitems - 1), nfull, J);
+      const uint8_t* mq = d.j < k ? dn_q + (size_t)eb[i] * mat_codes : sh_q;
+      const uint16_t* ms = d.j < k ? dn_s + (size_t)eb[i] * mat_groups : sh_s;
+      const uint16_t* mb = d.j < k ? dn_b + (size_t)eb[i] * mat_groups : sh_b;
+      if (!d.tail) {
+        f[i].codes = *(const uint4*)(mq + ((size_t)d.c * NT + t) * 1024 + 16 * (16 * q + row));
+        const size_t g = 32 * ((size_t)d.c * NT + t) + 2 * row;
+        f[i].s2 = *(const uint32_t*)(ms + g);
+        f[i].b2 = *(const uint32_t*)(mb + g);
+      } else {
+        const uint2 cd = *(const uint2*)(mq + (size_t)d.c * NT * 1024 + (size_t)t * 512 + 8 * (16 * q + row));
+        f[i].codes = make_uint4(cd.x, cd.y, 0u, 0u);
+        const size_t g = 32 * (size_t)d.c * NT + 16 * (size_t)t + row;
+        f[i].s2 = ms[g];
+        f[i].b2 = mb[g];
+      }
     }
   };
-  auto compute_batch = [&](int b0) {
+  auto compute_batch = [&](int p0) {
 #pragma unroll
     for (int i = 0; i < kDownBatch; ++i) {
-      const int b = b0 + kDownWaves * i;
-      if (b < nb) acc = __builtin_fmaf(wb[i], gemv_full(f[i], b % nfull, lane, hl + (size_t)(b / nfull) * I / 8), acc);
+      const int it = 2 * (p0 + kDownWaves * i) + sub;
+      if (it >= nitems) continue;
+      const DownItem d = down_item(it, nfull, J);
+      const uint4* x = hl + (size_t)d.j * I / 8;
+      const int k0 = 128 * d.c + 16 * q;  // first K value of the lane's first 16
+      const float s0 = bf16_bits_to_f32(f[i].s2 & 0xFFFFu), b0 = bf16_bits_to_f32(f[i].b2 & 0xFFFFu);
+      float v = dot16(f[i].codes.x, f[i].codes.y, x[k0 / 8], x[k0 / 8 + 1], s0, b0);
+      if (!d.tail) {
+        const float s1 = bf16_bits_to_f32(f[i].s2 >> 16), b1 = bf16_bits_to_f32(f[i].b2 >> 16);
+        v += dot16(f[i].codes.z, f[i].codes.w, x[(k0 + 64) / 8], x[(k0 + 64) / 8 + 1], s1, b1);
+      }
+      acc = __builtin_fmaf(f[i].w, v, acc);
     }
   };
   load_batch(wv);  // in flight while h is staged
   stage_store(hr, J * (I / 8), hl);
   __syncthreads();
   compute_batch(wv);
-  for (int b0 = wv + kDownWaves * kDownBatch; b0 < nb; b0 += kDownWaves * kDownBatch) {
-    load_batch(b0);
-    compute_batch(b0);
+  for (int p0 = wv + kDownWaves * kDownBatch; p0 < npairs; p0 += kDownWaves * kDownBatch) {
+    load_batch(p0);
+    compute_batch(p0);
   }
-  if (G & 1) {  // half-size last chunk of every expert
-    for (int j = wv; j < J; j += kDownWaves) {
-      const float wj = j < k ? w_ws[j] : 1.f;
-      acc = __builtin_fmaf(wj, gemv_tail(mat(j, j < k ? (size_t)ids_ws[j] : 0), t, nfull, lane, hl + (size_t)j * I / 8),
-                           acc);
-    }
-  }
-  acc = sum_quarters(acc);
-  if (lane < 16) red[wv][lane] = acc;
+  acc = sum_quarters(acc);         // the four K quarters of a row
+  acc += __shfl_xor(acc, 8);       // the two items of a pair
+  if (lane < 8) red[wv][lane] = acc;
   __syncthreads();
-  if (threadIdx.x < 16) {
+  if (threadIdx.x < 8) {
     float p = 0.f;
 #pragma unroll
     for (int w = 0; w < kDownWaves; ++w) p += red[w][threadIdx.x];
-    out[16 * t + threadIdx.x] = f32_to_bf16_bits(p);
+    out[8 * blockIdx.x + threadIdx.x] = f32_to_bf16_bits(p);
   }
 }
 
@@ -312,7 +364,7 @@ hipError_t decode_launch(const DecodePlan& p, const float* logits, const uint16_
                           logits, x, E, k, H, I, gu_q, gu_s, gu_b, sh_gu_q, sh_gu_s, sh_gu_b, ids_ws, w_ws, h_ws,
                           ids_out, w_out);
   if (err != hipSuccess) return err;
-  return launch("k_decode_down", (const void*)&k_decode_down, dim3(H / 16), dim3(kDownThreads), p.lds_down,
+  return launch("k_decode_down", (const void*)&k_decode_down, dim3(H / 8), dim3(kDownThreads), p.lds_down,
                 stream, k, H, I, p.J, dn_q, dn_s, dn_b, sh_dn_q, sh_dn_s, sh_dn_b, (const int32_t*)ids_ws,
                 (const float*)w_ws, (const uint16_t*)h_ws, out);
 }
