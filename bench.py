@@ -192,6 +192,33 @@ def graph_ms_per_step(torch, args, capture_step, layers):
     return (time.perf_counter() - t0) * 1e3 / args.steps
 
 
+def graph_kernel_ms(torch, capture, layers, reps):
+    """Average duration of one launch of the measured call (the dominant
+    kernel or kernel group): a HIP graph holds a chain of `layers` calls, each
+    on its own resident weight copy, replayed `reps` times back to back
+    between two HIP events recorded on the launch stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm the call once outside capture
+        capture(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(layers):
+            capture(l)
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * layers)
+
+
 def decode_graph_ms_per_step(torch, args, capture_step, layers):
     """Decode steps replayed from HIP graphs: steps warmup .. warmup+steps-1 in
     chains of `layers` consecutive steps, each captured with its own inputs and
@@ -212,11 +239,16 @@ def decode_graph_ms_per_step(torch, args, capture_step, layers):
         chains.append(g)
     chains[0].replay()                   # warm the graph path once
     torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(s)
     for g in chains:
         g.replay()
+    e1.record(s)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / args.steps
+    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    return wall, e0.elapsed_time(e1) / args.steps
 
 
 def base_line(args, w, value, ms_per_step, config, roof):
@@ -254,11 +286,15 @@ def bench_gemm(args, torch, q, W, w, d):
 
     eager_ms, (route_all, gemm_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
     gemm_ms = float(gemm_all.mean())
+    gemm_eager_ms = gemm_ms
     ms_per_step = eager_ms
     if not args.no_graph:
         ms_per_step = graph_ms_per_step(torch, args, lambda l: (
             q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
             q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y, stream=torch.cuda.current_stream())), layers)
+        gemm_ms = graph_kernel_ms(torch, lambda l: q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y,
+                                                                     stream=torch.cuda.current_stream()),
+                                  layers, max(1, args.steps // layers))
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     A = T * k
@@ -271,7 +307,7 @@ def bench_gemm(args, torch, q, W, w, d):
                     roofline(flops, alg_bytes, gemm_ms, "k_gemm_q4", w.name))
     out.update({
         "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
-        "gemm": {"us": gemm_ms * 1e3, "TFLOP/s": flops / (gemm_ms * 1e-3) / 1e12,
+        "gemm": {"us": gemm_ms * 1e3, "eager_event_us": gemm_eager_ms * 1e3, "TFLOP/s": flops / (gemm_ms * 1e-3) / 1e12,
                  "weight_GB/s": w_bytes / (gemm_ms * 1e-3) / 1e9, "experts_touched": touched,
                  "rows_max_over_mean": float(counts.max() / counts.mean()),
                  "experts_below_2_rows": float((counts < 2).mean())},
@@ -281,7 +317,9 @@ def bench_gemm(args, torch, q, W, w, d):
                   ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
                    "(route + GEMM launches, one weight copy each)") +
                   f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB) so each "
-                  "GEMM reads them from HBM; route and GEMM split by HIP events on the launch stream in an eager run",
+                  "GEMM reads them from HBM; GEMM time (gemm.us, the roofline's) by HIP events around graph replays "
+                  "of GEMM launches alone, back to back" + (" (eager: route and GEMM split by HIP events)" if
+                  args.no_graph else "; route_us and gemm.eager_event_us by HIP events in an eager run"),
         "gemm_us_p10_p90": [float(np.percentile(gemm_all, 10)) * 1e3, float(np.percentile(gemm_all, 90)) * 1e3],
     })
     if not args.no_cpu_baseline:
@@ -359,9 +397,14 @@ def bench_ffn(args, torch, q, W, w, d):
 
     eager_ms, (route_all, ffn_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
     ffn_ms = float(ffn_all.mean())
+    ffn_eager_ms = ffn_ms
     ms_per_step = eager_ms
     if not args.no_graph:
         ms_per_step = graph_ms_per_step(torch, args, graph_step, layers)
+        if chunked is None:  # the FFN launches alone (a chunked call also routes each chunk)
+            ffn_ms = graph_kernel_ms(torch, lambda l: q.expert_ffn(X, k, rt, *packs[l], bufs=bufs,
+                                                                   stream=torch.cuda.current_stream()),
+                                     layers, max(1, args.steps // layers))
     if chunked is not None:
         q.route(logits, k, bufs=rt, stream=stream)   # expert counts of the whole batch, for the byte count
     counts = rt["counts"].cpu().numpy()
@@ -376,7 +419,8 @@ def bench_ffn(args, torch, q, W, w, d):
                     roofline(flops, alg_bytes, ffn_ms, "expert_ffn" + ("_chunked" if args.chunk else ""), w.name))
     out.update({
         "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
-        "ffn": {"us": ffn_ms * 1e3, "TFLOP/s": flops / (ffn_ms * 1e-3) / 1e12, "experts_touched": touched,
+        "ffn": {"us": ffn_ms * 1e3, "eager_event_us": ffn_eager_ms * 1e3, "TFLOP/s": flops / (ffn_ms * 1e-3) / 1e12,
+                "experts_touched": touched,
                 "kernels": "routed + shared gate+up (SwiGLU) in one launch, routed (x routing weight) + "
                            "shared down in one launch, combine"},
         "route_us": float(route_all.mean()) * 1e3,
@@ -388,8 +432,10 @@ def bench_ffn(args, torch, q, W, w, d):
         "timing": f"steps back to back, wall clock between two synchronisations" +
                   ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
                    "(route + FFN launches, one weight copy each)") +
-                  f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB); route "
-                  "and FFN split by HIP events on the launch stream in an eager run",
+                  f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB); FFN time "
+                  "(ffn.us, the roofline's) by HIP events around graph replays of the FFN launches alone, back to back"
+                  + (" (eager or chunked: route and FFN split by HIP events)" if (args.no_graph or args.chunk) else
+                     "; route_us and ffn.eager_event_us by HIP events in an eager run"),
     })
     if not args.no_cpu_baseline:
         import oracle
@@ -631,10 +677,12 @@ def bench_decode(args, torch, q, W, w, d):
             ev[1].record(stream)
 
     eager_ms, (dec_all,) = Timer(torch, 2).run(step, args.warmup, args.steps)
-    dec_ms = float(dec_all.mean())
-    ms_per_step = eager_ms if args.no_graph else decode_graph_ms_per_step(
-        torch, args, lambda i: q.decode_ffn(lg[i], xs[i], k, *packs[i % layers], bufs=bufs,
-                                            stream=torch.cuda.current_stream()), layers)
+    dec_ms = dec_eager_ms = float(dec_all.mean())
+    ms_per_step = eager_ms
+    if not args.no_graph:
+        ms_per_step, dec_ms = decode_graph_ms_per_step(
+            torch, args, lambda i: q.decode_ffn(lg[i], xs[i], k, *packs[i % layers], bufs=bufs,
+                                                stream=torch.cuda.current_stream()), layers)
     flops = ffn_flops(1, H, I, k, True)
     alg_bytes = step_bytes + H * 2 * 2 + E * 4
     out = base_line(args, w, flops / (ms_per_step * 1e-3) / 1e12, ms_per_step,
@@ -643,14 +691,17 @@ def bench_decode(args, torch, q, W, w, d):
                     roofline(flops, alg_bytes, dec_ms, "decode_step", w.name))
     out.update({
         "weight_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "decode": {"us_per_step_kernels": dec_ms * 1e3, "weight_GB/s": step_bytes / (dec_ms * 1e-3) / 1e9,
+        "decode": {"us_per_step_kernels": dec_ms * 1e3, "eager_event_us": dec_eager_ms * 1e3,
+                   "weight_GB/s": step_bytes / (dec_ms * 1e-3) / 1e9,
                    "weight_bytes_per_step": step_bytes,
                    "kernels": "k_decode_gateup (routing + gate/up + SwiGLU), k_decode_down (down + combine)"},
         "timing": f"steps back to back, wall clock between two synchronisations" +
                   ("" if args.no_graph else f", replayed from HIP graphs each holding {layers} consecutive steps "
                    "(every step its own fresh logits and activations and its own weight copy)") +
                   f"; weights rotate over {layers} resident copies so more than 256 MB "
-                  "of other weights are read between two uses of a copy; kernel time by HIP events in an eager run",
+                  "of other weights are read between two uses of a copy; kernel time (decode.us_per_step_kernels, "
+                  "the roofline's) by HIP events around the graph replays" + (" (eager run)" if args.no_graph else
+                  "; decode.eager_event_us by HIP events in an eager run"),
         "eager_ms_per_step": eager_ms,
         "p10_p90_us": [float(np.percentile(dec_all, 10)) * 1e3, float(np.percentile(dec_all, 90)) * 1e3],
     })
