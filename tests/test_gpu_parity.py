@@ -62,6 +62,9 @@ ROUTE_CASES = [
     ("normal", 200, 300, 6), ("normal", 5, 256, 8), ("normal", 1000, 128, 3), ("normal", 2500, 512, 16),
     # T*k on both sides of 2^16: the scan kernel's packed single scan stops at 65535
     ("normal", 13107, 64, 5), ("normal", 8192, 256, 8),
+    # T*k on both sides of 8192, where one workgroup stops ranking from the ids
+    # alone; the largest expert count on that path; one expert taking them all
+    ("normal", 1024, 256, 8), ("normal", 8193, 1, 1), ("normal", 100, 1024, 64), ("hot", 8192, 64, 1),
 ]
 
 
