@@ -128,8 +128,8 @@ hipError_t ffn_launch(const FfnPlan& p, const uint16_t* X, int T, int H, int I, 
   const int sh_blocks = (T + p.bm_shared - 1) / p.bm_shared;
 
   // The shared expert's two projections join the routed launches as their
-  // dense second problem when the routed blocks are tall (64 or 128 rows: the
-  // kernels that take one); otherwise they are launches of their own.
+  // dense second problem when the routed blocks are tall (64 rows and up: the
+  // tall-block kernels take one); otherwise they are launches of their own.
   const bool fuse = shared && BM >= 64;
 
   // 0. tall-block launches take the routed blocks tallest first

@@ -41,7 +41,7 @@ constexpr int kSmallSlicesPerWave = kSmallAssignMax / 64 / kScanWaves;  // 64-as
 constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 
 // ----------------------------------------------------------------------------
-// top-k + softmax + chunk histogram + in-chunk stable ranks.
+// top-k + softmax; for large inputs also the chunk histogram and in-chunk stable ranks.
 // A workgroup of NW waves handles one chunk of tpc tokens; wave w takes tokens
 // w, w+NW, ...  Lane l of a token's wave holds experts [l*VPT, (l+1)*VPT).
 // Selection compares order-preserving integer keys of the logits (wave_topk).
