@@ -369,14 +369,27 @@ __global__ __launch_bounds__(kScanThreads) void k_route_small(
   }
   counts_to_blockmap(cnt_e, E, BM, A, counts, offsets, blocks, num_blocks, offs_s, boffs_s, scratch);
   // (counts_to_blockmap ends its scans with a barrier: the bases are visible)
+  int pos[kSmallSlicesPerWave];
 #pragma unroll
   for (int s = 0; s < kSmallSlicesPerWave; ++s) {
+    pos[s] = -1;
     if (rank[s] < 0) continue;
     const int a = (wv * spw + s) * 64 + lane;
     const int p = offs_s[eid[s]] + cnt[wv][eid[s]] + rank[s];
-    if (p >= 0 && p < A) perm[p] = a;
     inv_perm[a] = p;
+    if (p >= 0 && p < A) pos[s] = p;
   }
+  // perm = the inverse, scattered in LDS (the counters' 32 KB, no longer
+  // read, hold A <= kSmallAssignMax ints) and written out in order, so the
+  // stores to memory are coalesced
+  static_assert(sizeof(cnt) >= kSmallAssignMax * sizeof(int), "the counters hold the permutation");
+  int* const perm_s = reinterpret_cast<int*>(&cnt[0][0]);
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kSmallSlicesPerWave; ++s)
+    if (pos[s] >= 0) perm_s[pos[s]] = (wv * spw + s) * 64 + lane;
+  __syncthreads();
+  for (int i = tid; i < A; i += kScanThreads) perm[i] = perm_s[i];
 }
 
 // ----------------------------------------------------------------------------
