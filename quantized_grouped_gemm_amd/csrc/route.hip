@@ -9,10 +9,11 @@
 //
 // Two kernels up to kSmallAssignMax assignments, three above, all on the
 // caller's stream:
-//   k_topk_rank      one workgroup of 16 waves per "chunk" of tokens, one wave
-//                    per token: top-k by k rounds of a wave-wide argmax over
-//                    order-preserving integer keys (DPP max + ballot), softmax
-//                    over the k selected logits; then (large inputs only) the
+//   k_topk_rank      one wave per token (large inputs: workgroups of 16 waves
+//                    per "chunk" of tokens; small: of 2): top-k by k rounds
+//                    of a wave-wide argmax over order-preserving integer keys
+//                    (DPP max + ballot), softmax over the k selected logits;
+//                    then (large inputs only) the
 //                    chunk's histogram and each assignment's stable rank
 //                    among same-expert assignments of the chunk (ballot match
 //                    masks over the expert-id bits + popcounts).
@@ -30,7 +31,8 @@
 
 namespace moeq4 {
 
-constexpr int kRouteWaves = 16;            // waves per chunk workgroup
+constexpr int kRouteWaves = 16;            // waves per chunk workgroup (with the histogram)
+constexpr int kTopkSmallWaves = 2;         // waves (= tokens) per top-k workgroup for small inputs
 constexpr int kRouteThreads = kRouteWaves * 64;
 constexpr int kChunkAssignMax = 2048;      // assignments per chunk (LDS bound)
 constexpr int kMaxSlicesPerWave = kChunkAssignMax / 64 / kRouteWaves;
@@ -42,9 +44,12 @@ constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 
 // ----------------------------------------------------------------------------
 // top-k + softmax; for large inputs also the chunk histogram and in-chunk stable ranks.
-// A workgroup of NW waves handles one chunk of tpc tokens; wave w takes tokens
-// w, w+NW, ...  Lane l of a token's wave holds experts [l*VPT, (l+1)*VPT).
+// A workgroup of nw waves handles one chunk of tpc tokens; wave w takes tokens
+// w, w+nw, ...  Lane l of a token's wave holds experts [l*VPT, (l+1)*VPT).
 // Selection compares order-preserving integer keys of the logits (wave_topk).
+// With the histogram the workgroup has kRouteWaves waves (the counters' rows);
+// without it, small workgroups of one token per wave spread the selections
+// over more CUs, and no LDS is used.
 template <int VPT>
 __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
     const float* __restrict__ logits, int T, int E, int k, int tpc, int nbits, int hist,
@@ -61,6 +66,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
   const int t0 = chunk * tpc;
   const int ntok = min(tpc, T - t0);
 
+  const int nw = hist ? NW : (int)(blockDim.x >> 6);
   if (hist)
     for (int i = threadIdx.x; i < NW * E; i += blockDim.x) cnt[i] = 0;
 
@@ -75,12 +81,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
     }
   };
   fetch(wv);
-  for (int i = wv; i < ntok; i += NW) {
+  for (int i = wv; i < ntok; i += nw) {
     const int t = t0 + i;
     int key[VPT];
 #pragma unroll
     for (int s = 0; s < VPT; ++s) key[s] = (lane * VPT + s < E) ? order_key(vn[s]) : kKeyTaken;
-    fetch(i + NW);
+    fetch(i + nw);
     int my_id;
     float my_v, v0;
     wave_topk<VPT>(key, E, k, my_id, my_v, v0);
@@ -89,7 +95,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_topk_rank(
     if (lane < k) {
       ids_out[(size_t)t * k + lane] = my_id;
       w_out[(size_t)t * k + lane] = ex / sum;
-      sids[i * k + lane] = my_id;
+      if (hist) sids[i * k + lane] = my_id;
     }
   }
   if (!hist) return;  // small inputs: k_route_small ranks from the ids
@@ -443,15 +449,20 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
   const int small = A <= kSmallAssignMax;
   hipError_t err = hipSuccess;
   if (plan.nchunks > 0) {
-    const size_t shmem = sizeof(int) * (size_t)plan.tpc * k + sizeof(uint16_t) * (size_t)kRouteWaves * E;
     const void* fn;
     if (E <= 64) fn = (const void*)&k_topk_rank<1>;
     else if (E <= 128) fn = (const void*)&k_topk_rank<2>;
     else if (E <= 256) fn = (const void*)&k_topk_rank<4>;
     else if (E <= 512) fn = (const void*)&k_topk_rank<8>;
     else fn = (const void*)&k_topk_rank<16>;
-    err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T, E, k,
-                 plan.tpc, plan.nbits, small ? 0 : 1, ids, w, chunk_counts, local_rank);
+    if (small) {
+      err = launch("k_topk_rank", fn, dim3((T + kTopkSmallWaves - 1) / kTopkSmallWaves), dim3(64 * kTopkSmallWaves),
+                   0, stream, logits, T, E, k, kTopkSmallWaves, plan.nbits, 0, ids, w, chunk_counts, local_rank);
+    } else {
+      const size_t shmem = sizeof(int) * (size_t)plan.tpc * k + sizeof(uint16_t) * (size_t)kRouteWaves * E;
+      err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T, E, k,
+                   plan.tpc, plan.nbits, 1, ids, w, chunk_counts, local_rank);
+    }
     if (err != hipSuccess) return err;
   }
   if (small)
