@@ -13,19 +13,21 @@
 //                    per "chunk" of tokens; small: of 2): top-k by k rounds
 //                    of a wave-wide argmax over order-preserving integer keys
 //                    (DPP max + ballot), softmax over the k selected logits;
-//                    then (large inputs only) the
-//                    chunk's histogram and each assignment's stable rank
-//                    among same-expert assignments of the chunk (ballot match
-//                    masks over the expert-id bits + popcounts).
+//                    then (large inputs only) the chunk's histogram and each
+//                    assignment's stable rank among same-expert assignments
+//                    of the chunk (ballot match masks over the expert-id bits
+//                    + popcounts).
 //   k_route_small    (small inputs) one workgroup does the rest from the
 //                    expert ids alone: each wave ranks a contiguous range of
 //                    assignments the same way, a scan over the waves gives
 //                    each expert's count and per-wave bases; then offsets,
 //                    block map and the scatter.
-//   k_scan_blockmap  (large inputs) one workgroup: per-expert exclusive scan
-//                    over chunks, counts, offsets, block counts and their
-//                    scan, block map.
-//   k_scatter        (large inputs) one thread per assignment: perm, inv_perm.
+//   k_chunk_scan     (large inputs) one workgroup per 64 experts: per-expert
+//                    exclusive scan over the chunks, and the counts.
+//   k_scatter        (large inputs) one thread per assignment: perm and
+//                    inv_perm from the offsets, which every workgroup scans
+//                    from the counts; workgroup 0 also writes the offsets,
+//                    the block counts' scan and the block map.
 // Only integer adds decide positions, so every output is deterministic.
 #include "common.h"
 
@@ -192,10 +194,10 @@ __device__ int block_exclusive_scan(int v, int* scratch /* >= kScanThreads/64 + 
   return r;
 }
 
-// From each expert's count (thread e < E holds cnt_e): counts, offsets, block
-// offsets, the block count and the block map; offs_s / boffs_s (E + 1 ints in
-// LDS) keep the offsets and block offsets for the caller.  Every thread of the
-// kScanThreads workgroup calls it.
+// From each expert's count (thread e < E holds cnt_e): counts (unless null),
+// offsets, block offsets, the block count and the block map; offs_s / boffs_s
+// (E + 1 ints in LDS) keep the offsets and block offsets for the caller.  Every
+// thread of the kScanThreads workgroup calls it.
 __device__ void counts_to_blockmap(int cnt_e, int E, int BM, int A, int32_t* __restrict__ counts,
                                    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks,
                                    int32_t* __restrict__ num_blocks, int* offs_s, int* boffs_s, int* scratch) {
@@ -216,7 +218,7 @@ __device__ void counts_to_blockmap(int cnt_e, int E, int BM, int A, int32_t* __r
     boff = block_exclusive_scan(nb, scratch, &nb_total);
   }
   if (tid < E) {
-    counts[tid] = cnt_e;
+    if (counts) counts[tid] = cnt_e;
     offsets[tid] = off;
     offs_s[tid] = off;
     boffs_s[tid] = boff;
@@ -245,66 +247,60 @@ __device__ void counts_to_blockmap(int cnt_e, int E, int BM, int A, int32_t* __r
   }
 }
 
-__global__ __launch_bounds__(kScanThreads) void k_scan_blockmap(
-    int32_t* __restrict__ chunk_counts, int nchunks, int E, int BM, int A, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks) {
-  __shared__ int part[kScanThreads];
-  __shared__ int offs_s[MOEQ4_MAX_EXPERTS + 1];
-  __shared__ int boffs_s[MOEQ4_MAX_EXPERTS + 1];
-  __shared__ int scratch[kScanThreads / 64 + 1];
-  const int tid = threadIdx.x;
+// Large inputs: per expert, the exclusive scan over chunks, in place (chunk
+// counts become chunk bases), and each expert's total into counts.  Workgroup
+// g takes experts [64g, 64g + 64), one per lane, so every chunk row is read
+// coalesced; its waves split the chunks into contiguous ranges, and a scan
+// over the waves gives each range's base.  A range's first kChunkRegs counts
+// stay in registers, loaded unconditionally (clamped rows) so they are in
+// flight together.
+constexpr int kChunkScanWaves = 16;
+constexpr int kChunkRegs = 16;
 
-  // ---- per expert, exclusive scan over chunks (S threads per expert).  Each
-  // thread holds its chunk counts in registers, fetched with independent loads.
-  const int S = kScanThreads / E;  // >= 1 since E <= 1024
-  const int e = tid % E, s = tid / E;
-  const bool act = s < S;
-  const int cpc = (nchunks + S - 1) / S;
-  const int c_lo = min(nchunks, s * cpc), c_hi = min(nchunks, (s + 1) * cpc);
-  int vals[kScanRegs];
+__global__ __launch_bounds__(kChunkScanWaves * 64) void k_chunk_scan(int32_t* __restrict__ chunk_counts, int nchunks,
+                                                                     int E, int32_t* __restrict__ counts) {
+  __shared__ int part[kChunkScanWaves][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = min(blockIdx.x * 64 + lane, E - 1);  // lanes past E repeat the last expert, unstored
+  const bool act = blockIdx.x * 64 + lane < E;
+  const int cpw = (nchunks + kChunkScanWaves - 1) / kChunkScanWaves;
+  const int c_lo = min(nchunks, wv * cpw), c_hi = min(nchunks, c_lo + cpw);
+  int vals[kChunkRegs];
+#pragma unroll
+  for (int i = 0; i < kChunkRegs; ++i) {
+    const int c = c_lo + i;
+    const int v = chunk_counts[(size_t)min(c, nchunks - 1) * E + e];
+    vals[i] = c < c_hi ? v : 0;
+  }
   int psum = 0;
-  const bool in_regs = cpc <= kScanRegs;
-  if (act && in_regs) {
 #pragma unroll
-    for (int i = 0; i < kScanRegs; ++i) {
-      const int c = c_lo + i;
-      vals[i] = (c < c_hi) ? chunk_counts[(size_t)c * E + e] : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < kScanRegs; ++i) psum += vals[i];
-  } else if (act) {
-    for (int c = c_lo; c < c_hi; ++c) psum += chunk_counts[(size_t)c * E + e];
-  }
-  part[tid] = act ? psum : 0;
+  for (int i = 0; i < kChunkRegs; ++i) psum += vals[i];
+  for (int c = c_lo + kChunkRegs; c < c_hi; ++c) psum += chunk_counts[(size_t)c * E + e];
+  part[wv][lane] = psum;
   __syncthreads();
-  int cnt_e = 0;
-  if (tid < E) {
+  if (wv == 0) {
     int run = 0;
-    for (int i = 0; i < S; ++i) {
-      const int x = part[i * E + tid];
-      part[i * E + tid] = run;
+    for (int w = 0; w < kChunkScanWaves; ++w) {
+      const int x = part[w][lane];
+      part[w][lane] = run;
       run += x;
     }
-    cnt_e = run;
+    if (act) counts[e] = run;
   }
   __syncthreads();
-  if (act && in_regs) {
-    int run = part[tid];
+  if (!act) return;
+  int run = part[wv][lane];
 #pragma unroll
-    for (int i = 0; i < kScanRegs; ++i) {
-      const int c = c_lo + i;
-      if (c < c_hi) chunk_counts[(size_t)c * E + e] = run;
-      run += vals[i];
-    }
-  } else if (act) {
-    int run = part[tid];
-    for (int c = c_lo; c < c_hi; ++c) {
-      const int x = chunk_counts[(size_t)c * E + e];
-      chunk_counts[(size_t)c * E + e] = run;
-      run += x;
-    }
+  for (int i = 0; i < kChunkRegs; ++i) {
+    const int c = c_lo + i;
+    if (c < c_hi) chunk_counts[(size_t)c * E + e] = run;
+    run += vals[i];
   }
-  counts_to_blockmap(cnt_e, E, BM, A, counts, offsets, blocks, num_blocks, offs_s, boffs_s, scratch);
+  for (int c = c_lo + kChunkRegs; c < c_hi; ++c) {
+    const int x = chunk_counts[(size_t)c * E + e];
+    chunk_counts[(size_t)c * E + e] = run;
+    run += x;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -399,17 +395,32 @@ __global__ __launch_bounds__(kScanThreads) void k_route_small(
 }
 
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, int A, int E, int k,
-                                                 int tpc, const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ chunk_base,
-                                                 const int32_t* __restrict__ local_rank,
-                                                 int32_t* __restrict__ perm,
-                                                 int32_t* __restrict__ inv_perm) {
-  const int a = blockIdx.x * 256 + threadIdx.x;
-  if (a >= A) return;
-  const int e = ids[a];
+__global__ __launch_bounds__(kScanThreads) void k_scatter(
+    const int32_t* __restrict__ ids, int A, int E, int k, int tpc, int BM, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ local_rank, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm) {
+  __shared__ int offs_s[MOEQ4_MAX_EXPERTS + 1];
+  __shared__ int boffs_s[MOEQ4_MAX_EXPERTS + 1];
+  __shared__ int scratch[kScanThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  const int a = blockIdx.x * kScanThreads + tid;
+  const bool va = a < A;
+  // the assignment's own loads go out together with the counts
+  const int cnt_e = tid < E ? counts[tid] : 0;
+  const int e = va ? ids[a] : 0;
+  const int lr = va ? local_rank[a] : 0;
+  if (blockIdx.x == 0) {
+    counts_to_blockmap(cnt_e, E, BM, A, nullptr, offsets, blocks, num_blocks, offs_s, boffs_s, scratch);
+  } else {
+    int total;
+    const int off = block_exclusive_scan(tid < E ? cnt_e : 0, scratch, &total);
+    if (tid < E) offs_s[tid] = off;
+    __syncthreads();
+  }
+  if (!va) return;
   const int c = a / (k * tpc);  // the chunk of token a / k
-  const int p = offsets[e] + chunk_base[(size_t)c * E + e] + local_rank[a];
+  const int p = offs_s[e] + chunk_base[(size_t)c * E + e] + lr;
   if (p >= 0 && p < A) perm[p] = a;
   inv_perm[a] = p;
 }
@@ -468,12 +479,12 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
   if (small)
     return launch("k_route_small", (const void*)&k_route_small, dim3(1), dim3(kScanThreads), 0, stream,
                   (const int32_t*)ids, A, E, BM, plan.nbits, counts, offsets, blocks, num_blocks, perm, inv_perm);
-  err = launch("k_scan_blockmap", (const void*)&k_scan_blockmap, dim3(1), dim3(kScanThreads), 0, stream, chunk_counts,
-               plan.nchunks, E, BM, A, counts, offsets, blocks, num_blocks);
+  err = launch("k_chunk_scan", (const void*)&k_chunk_scan, dim3((E + 63) / 64), dim3(kChunkScanWaves * 64), 0, stream,
+               chunk_counts, plan.nchunks, E, counts);
   if (err != hipSuccess) return err;
-  return launch("k_scatter", (const void*)&k_scatter, dim3((A + 255) / 256), dim3(256), 0, stream,
-                (const int32_t*)ids, A, E, k, plan.tpc, (const int32_t*)offsets, (const int32_t*)chunk_counts,
-                (const int32_t*)local_rank, perm, inv_perm);
+  return launch("k_scatter", (const void*)&k_scatter, dim3((A + kScanThreads - 1) / kScanThreads), dim3(kScanThreads),
+                0, stream, (const int32_t*)ids, A, E, k, plan.tpc, BM, (const int32_t*)counts,
+                (const int32_t*)chunk_counts, (const int32_t*)local_rank, offsets, blocks, num_blocks, perm, inv_perm);
 }
 
 }  // namespace moeq4
