@@ -223,7 +223,8 @@ def decode_graph_ms_per_step(torch, args, capture_step, layers):
     """Decode steps replayed from HIP graphs: steps warmup .. warmup+steps-1 in
     chains of `layers` consecutive steps, each captured with its own inputs and
     weight copy (a decode pass through consecutive layers in one graph).
-    capture_step(i) launches step i on torch's current stream."""
+    capture_step(i) launches step i on torch's current stream.  Returns
+    (wall-clock ms per step, HIP-event ms per step) over the replays."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -494,13 +495,13 @@ def bench_crossover(args, torch, q, W, d):
             distinct.append(len(np.unique(sb["topk_ids"].cpu().numpy())))
         u = float(np.mean(distinct))
         row = {"T": T, "distinct_experts_mean": u}
-        row["small_us"] = decode_graph_ms_per_step(torch, args, small_step, layers) * 1e3
-        row["prefill_path_us"] = decode_graph_ms_per_step(torch, args, prefill_step, layers) * 1e3
+        row["small_us"] = decode_graph_ms_per_step(torch, args, small_step, layers)[0] * 1e3
+        row["prefill_path_us"] = decode_graph_ms_per_step(torch, args, prefill_step, layers)[0] * 1e3
         if T == 1:
             db = q.alloc_decode(E, k, H, I, True, device=xs.device)
             row["decode_us"] = decode_graph_ms_per_step(
                 torch, args, lambda i: q.decode_ffn(lg[i][0], xs[i][0], k, *packs[i % layers], bufs=db,
-                                                    stream=torch.cuda.current_stream()), layers) * 1e3
+                                                    stream=torch.cuda.current_stream()), layers)[0] * 1e3
         row["small_weight_GBps"] = (u + 1) * expert_bytes / (row["small_us"] * 1e-6) / 1e9
         row["small_us_per_row"] = row["small_us"] / T
         rows.append(row)
