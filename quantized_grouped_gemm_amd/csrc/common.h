@@ -79,16 +79,6 @@ __device__ __forceinline__ float dpp_f32(float x) {
       __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_max_f32(float x) {
-  x = fmaxf(x, dpp_f32<0xB1>(x));         // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f32<0x4E>(x));         // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f32<0x141>(x));        // row_half_mirror
-  x = fmaxf(x, dpp_f32<0x140>(x));        // row_mirror
-  x = fmaxf(x, dpp_f32<0x142, 0xA>(x));   // row_bcast:15 into rows 1 and 3
-  x = fmaxf(x, dpp_f32<0x143, 0xC>(x));   // row_bcast:31 into rows 2 and 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ int dpp_i32(int x) {
   return __builtin_amdgcn_update_dpp(x, x, CTRL, ROW_MASK, 0xF, false);
@@ -96,12 +86,12 @@ __device__ __forceinline__ int dpp_i32(int x) {
 
 // wave-wide maximum of a signed int; the result is uniform (SGPR)
 __device__ __forceinline__ int wave_max_i32(int x) {
-  x = max(x, dpp_i32<0xB1>(x));
-  x = max(x, dpp_i32<0x4E>(x));
-  x = max(x, dpp_i32<0x141>(x));
-  x = max(x, dpp_i32<0x140>(x));
-  x = max(x, dpp_i32<0x142, 0xA>(x));
-  x = max(x, dpp_i32<0x143, 0xC>(x));
+  x = max(x, dpp_i32<0xB1>(x));        // quad_perm [1,0,3,2]
+  x = max(x, dpp_i32<0x4E>(x));        // quad_perm [2,3,0,1]
+  x = max(x, dpp_i32<0x141>(x));       // row_half_mirror
+  x = max(x, dpp_i32<0x140>(x));       // row_mirror
+  x = max(x, dpp_i32<0x142, 0xA>(x));  // row_bcast:15 into rows 1 and 3
+  x = max(x, dpp_i32<0x143, 0xC>(x));  // row_bcast:31 into rows 2 and 3
   return __builtin_amdgcn_readlane(x, 63);
 }
 

@@ -42,7 +42,6 @@ constexpr int kSmallAssignMax = 8192;      // assignments one workgroup ranks an
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kSmallSlicesPerWave = kSmallAssignMax / 64 / kScanWaves;  // 64-assignment slices per wave
-constexpr int kScanRegs = 64;  // chunk counts a scan thread keeps in registers
 
 // ----------------------------------------------------------------------------
 // top-k + softmax; for large inputs also the chunk histogram and in-chunk stable ranks.
