@@ -65,8 +65,9 @@ ROUTE_CASES = [
     # T*k on both sides of 8192, where one workgroup stops ranking from the ids
     # alone; the largest expert count on that path; one expert taking them all
     ("normal", 1024, 256, 8), ("normal", 8193, 1, 1), ("normal", 100, 1024, 64), ("hot", 8192, 64, 1),
-    # more chunks than the chunk scan's waves hold in registers (313 chunks of 128 tokens)
-    ("normal", 40000, 64, 16),
+    # more chunks than the chunk scan's waves hold in registers (313 chunks of 128 tokens);
+    # an expert count that leaves the chunk scan's last workgroup partly idle
+    ("normal", 40000, 64, 16), ("normal", 3000, 300, 6),
 ]
 
 
