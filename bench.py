@@ -192,31 +192,47 @@ def graph_ms_per_step(torch, args, capture_step, layers):
     return (time.perf_counter() - t0) * 1e3 / args.steps
 
 
-def graph_kernel_ms(torch, capture, layers, reps):
-    """Average duration of one launch of the measured call (the dominant
-    kernel or kernel group): a HIP graph holds a chain of `layers` calls, each
-    on its own resident weight copy, replayed `reps` times back to back
-    between two HIP events recorded on the launch stream."""
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):       # warm the call once outside capture
-        capture(0)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for l in range(layers):
-            capture(l)
-    g.replay()
-    torch.cuda.synchronize()
+def graph_split_ms(torch, pre, call, layers, reps, rounds=3):
+    """Time of `call` inside the step it belongs to: HIP graphs hold a chain of
+    `layers` steps (pre(l) then call(l), each on its own resident weight copy)
+    and the same chain of pre(l) alone; both are replayed `reps` times back to
+    back between two HIP events on the launch stream, alternating over
+    `rounds` rounds, and the call's time per step is the difference of the
+    two per-step times.  A back-to-back chain of the call alone would time it
+    in another context than the step's (at the prefill shapes the GEMMs then
+    run several percent slower).  Returns (step ms, pre ms, call ms)."""
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(reps):
-        g.replay()
-    e1.record(s)
+    side = torch.cuda.Stream()
+    side.wait_stream(s)
+    with torch.cuda.stream(side):       # warm the calls once outside capture
+        pre(0)
+        call(0)
+    s.wait_stream(side)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * layers)
+    g_step, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        for l in range(layers):
+            pre(l)
+            call(l)
+    with torch.cuda.graph(g_pre):
+        for l in range(layers):
+            pre(l)
+    g_step.replay()
+    g_pre.replay()
+    torch.cuda.synchronize()
+    tot = {"step": 0.0, "pre": 0.0}
+    for _ in range(rounds):
+        for name, g in (("step", g_step), ("pre", g_pre)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+            torch.cuda.synchronize()
+            tot[name] += e0.elapsed_time(e1)
+    n = rounds * reps * layers
+    step_ms, pre_ms = tot["step"] / n, tot["pre"] / n
+    return step_ms, pre_ms, step_ms - pre_ms
 
 
 def decode_graph_ms_per_step(torch, args, capture_step, layers):
@@ -293,9 +309,10 @@ def bench_gemm(args, torch, q, W, w, d):
         ms_per_step = graph_ms_per_step(torch, args, lambda l: (
             q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
             q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y, stream=torch.cuda.current_stream())), layers)
-        gemm_ms = graph_kernel_ms(torch, lambda l: q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y,
-                                                                     stream=torch.cuda.current_stream()),
-                                  layers, max(1, args.steps // layers))
+        _, _, gemm_ms = graph_split_ms(
+            torch, lambda l: q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
+            lambda l: q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y, stream=torch.cuda.current_stream()),
+            layers, max(1, args.steps // layers))
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     A = T * k
@@ -318,8 +335,9 @@ def bench_gemm(args, torch, q, W, w, d):
                   ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
                    "(route + GEMM launches, one weight copy each)") +
                   f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB) so each "
-                  "GEMM reads them from HBM; GEMM time (gemm.us, the roofline's) by HIP events around graph replays "
-                  "of GEMM launches alone, back to back" + (" (eager: route and GEMM split by HIP events)" if
+                  "GEMM reads them from HBM; GEMM time (gemm.us, the roofline's) by HIP events around graph replays: "
+                  "a chain of route + GEMM steps minus the same chain of routing alone, per step" +
+                  (" (eager: route and GEMM split by HIP events)" if
                   args.no_graph else "; route_us and gemm.eager_event_us by HIP events in an eager run"),
         "gemm_us_p10_p90": [float(np.percentile(gemm_all, 10)) * 1e3, float(np.percentile(gemm_all, 90)) * 1e3],
     })
@@ -403,9 +421,10 @@ def bench_ffn(args, torch, q, W, w, d):
     if not args.no_graph:
         ms_per_step = graph_ms_per_step(torch, args, graph_step, layers)
         if chunked is None:  # the FFN launches alone (a chunked call also routes each chunk)
-            ffn_ms = graph_kernel_ms(torch, lambda l: q.expert_ffn(X, k, rt, *packs[l], bufs=bufs,
-                                                                   stream=torch.cuda.current_stream()),
-                                     layers, max(1, args.steps // layers))
+            _, _, ffn_ms = graph_split_ms(
+                torch, lambda l: q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
+                lambda l: q.expert_ffn(X, k, rt, *packs[l], bufs=bufs, stream=torch.cuda.current_stream()),
+                layers, max(1, args.steps // layers))
     if chunked is not None:
         q.route(logits, k, bufs=rt, stream=stream)   # expert counts of the whole batch, for the byte count
     counts = rt["counts"].cpu().numpy()
@@ -434,7 +453,8 @@ def bench_ffn(args, torch, q, W, w, d):
                   ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
                    "(route + FFN launches, one weight copy each)") +
                   f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB); FFN time "
-                  "(ffn.us, the roofline's) by HIP events around graph replays of the FFN launches alone, back to back"
+                  "(ffn.us, the roofline's) by HIP events around graph replays: a chain of route + FFN steps minus "
+                  "the same chain of routing alone, per step"
                   + (" (eager or chunked: route and FFN split by HIP events)" if (args.no_graph or args.chunk) else
                      "; route_us and ffn.eager_event_us by HIP events in an eager run"),
     })
