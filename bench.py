@@ -420,7 +420,7 @@ def bench_ffn(args, torch, q, W, w, d):
     ms_per_step = eager_ms
     if not args.no_graph:
         ms_per_step = graph_ms_per_step(torch, args, graph_step, layers)
-        if chunked is None:  # the FFN launches alone (a chunked call also routes each chunk)
+        if chunked is None:  # the FFN inside its step (a chunked call routes each chunk itself)
             _, _, ffn_ms = graph_split_ms(
                 torch, lambda l: q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
                 lambda l: q.expert_ffn(X, k, rt, *packs[l], bufs=bufs, stream=torch.cuda.current_stream()),
