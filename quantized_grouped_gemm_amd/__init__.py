@@ -18,6 +18,8 @@ import os
 import torch  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
+# The in-tree build, unless MOEQ4_LIB names another build of the same library
+# (an installed copy, or a build of other sources to compare against).
 LIB_PATH = os.environ.get("MOEQ4_LIB") or os.path.join(_PKG, "_lib", "libmoeq4.so")
 
 MOEQ4_OK = 0
