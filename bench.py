@@ -1,9 +1,11 @@
 """Benchmark of the MoE routing + Q4 grouped-GEMM hot path on one MI355X.
 
 Default (the prefill-chunk workload: T=512 tokens, E=256 experts, top-8,
-K=2048 -> N=512, group-64 affine 4-bit weights): one step = moe_route (top-k,
-histogram, scan, block map, scatter) followed by moe_grouped_gemm_q4 over the
-routed rows; the same JSON line also carries, under "c3", the expert-FFN
+K=2048 -> N=512, group-64 affine 4-bit weights): one step = the routing (top-k,
+histogram, scan, block map, scatter) and the grouped GEMM over the routed rows,
+as one moe_route_grouped_gemm_q4 call (its GEMM launch ranks each expert's rows
+itself; at other shapes moe_route then moe_grouped_gemm_q4); the same JSON
+line also carries, under "c3", the expert-FFN
 step at T=4096 below (the metric is quoted at T=512 and T=4096), with its own
 roofline and CPU baseline (--no-c3 leaves it out).  Other workloads:
   --workload 4   the same step at T=16384 with Zipf-skewed routing
@@ -192,28 +194,35 @@ def graph_ms_per_step(torch, args, capture_step, layers):
     return (time.perf_counter() - t0) * 1e3 / args.steps
 
 
-def graph_split_ms(torch, pre, call, layers, reps, rounds=3):
+def graph_split_ms(torch, pre, call, layers, reps, rounds=3, whole=None):
     """Time of `call` inside the step it belongs to: HIP graphs hold a chain of
-    `layers` steps (pre(l) then call(l), each on its own resident weight copy)
-    and the same chain of pre(l) alone; both are replayed `reps` times back to
-    back between two HIP events on the launch stream, alternating over
-    `rounds` rounds, and the call's time per step is the difference of the
-    two per-step times.  A back-to-back chain of the call alone would time it
-    in another context than the step's (at the prefill shapes the GEMMs then
-    run several percent slower).  Returns (step ms, pre ms, call ms)."""
+    `layers` steps (pre(l) then call(l), or whole(l): one call that does pre's
+    work and then the call's, each on its own resident weight copy) and the
+    same chain of pre(l) alone; both are replayed `reps` times back to back
+    between two HIP events on the launch stream, alternating over `rounds`
+    rounds, and the call's time per step is the difference of the two
+    per-step times.  A back-to-back chain of the call alone would time it in
+    another context than the step's (at the prefill shapes the GEMMs then run
+    several percent slower).  Returns (step ms, pre ms, call ms)."""
+    def step(l):
+        if whole is not None:
+            whole(l)
+        else:
+            pre(l)
+            call(l)
+
     s = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side.wait_stream(s)
     with torch.cuda.stream(side):       # warm the calls once outside capture
         pre(0)
-        call(0)
+        step(0)
     s.wait_stream(side)
     torch.cuda.synchronize()
     g_step, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_step):
         for l in range(layers):
-            pre(l)
-            call(l)
+            step(l)
     with torch.cuda.graph(g_pre):
         for l in range(layers):
             pre(l)
@@ -290,29 +299,50 @@ def bench_gemm(args, torch, q, W, w, d):
     rt = q.alloc_route(T, E, k, args.block_rows, device=X.device)
     Y = torch.empty((T * k, N), dtype=torch.int16, device=X.device)
     stream = torch.cuda.current_stream()
+    # 64-row blocks up to 8192 assignments: one call, whose GEMM launch ranks
+    # each expert's rows itself after the top-k (moe_route_grouped_gemm_q4);
+    # the routing that precedes the GEMM launch is then the top-k alone
+    fused = rt["block_rows"] == 64 and 0 < T * k <= 8192
+    cur = torch.cuda.current_stream
+
+    def pre(l, st=None):
+        if fused:
+            q.topk_softmax(logits, k, rt, stream=st or cur())
+        else:
+            q.route(logits, k, bufs=rt, stream=st or cur())
+
+    def whole(l, st=None):
+        if fused:
+            q.route_grouped_gemm_q4(logits, X, k, packs[l], rt, Y=Y, stream=st or cur())
+        else:
+            q.route(logits, k, bufs=rt, stream=st or cur())
+            q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y, stream=st or cur())
 
     def step(i, ev):
         if ev is not None:
             ev[0].record(stream)
-        q.route(logits, k, bufs=rt, stream=stream)
+        whole(i % layers, stream)
         if ev is not None:
             ev[1].record(stream)
-        q.grouped_gemm_q4(X, k, packs[i % layers], rt, Y=Y, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
-    eager_ms, (route_all, gemm_all) = Timer(torch, 3).run(step, args.warmup, args.steps)
+    def pre_step(i, ev):
+        if ev is not None:
+            ev[0].record(stream)
+        pre(i, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    # eager: the steps between HIP events, then (separately) the routing that
+    # precedes the GEMM launch on its own
+    eager_ms, (whole_all,) = Timer(torch, 2).run(step, args.warmup, args.steps)
+    _, (route_all,) = Timer(torch, 2).run(pre_step, 2, min(args.steps, 20))
+    gemm_all = whole_all - float(route_all.mean())
     gemm_ms = float(gemm_all.mean())
     gemm_eager_ms = gemm_ms
     ms_per_step = eager_ms
     if not args.no_graph:
-        ms_per_step = graph_ms_per_step(torch, args, lambda l: (
-            q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
-            q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y, stream=torch.cuda.current_stream())), layers)
-        _, _, gemm_ms = graph_split_ms(
-            torch, lambda l: q.route(logits, k, bufs=rt, stream=torch.cuda.current_stream()),
-            lambda l: q.grouped_gemm_q4(X, k, packs[l], rt, Y=Y, stream=torch.cuda.current_stream()),
-            layers, max(1, args.steps // layers))
+        ms_per_step = graph_ms_per_step(torch, args, whole, layers)
+        _, _, gemm_ms = graph_split_ms(torch, pre, None, layers, max(1, args.steps // layers), whole=whole)
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     A = T * k
@@ -323,6 +353,9 @@ def bench_gemm(args, torch, q, W, w, d):
                     {"workload": w.name, "T": T, "E": E, "top_k": k, "K": K, "N": N,
                      "block_rows": rt["block_rows"], "group": 64, "parallelism": "single GPU"},
                     roofline(flops, alg_bytes, gemm_ms, "k_gemm_q4", w.name))
+    out["roofline"]["kernel_detail"] = (
+        "the GEMM launch that also ranks each expert's rows (moe_route_grouped_gemm_q4)" if fused
+        else "the grouped GEMM launch after moe_route")
     out.update({
         "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
         "gemm": {"us": gemm_ms * 1e3, "eager_event_us": gemm_eager_ms * 1e3, "TFLOP/s": flops / (gemm_ms * 1e-3) / 1e12,
@@ -331,14 +364,18 @@ def bench_gemm(args, torch, q, W, w, d):
                  "experts_below_2_rows": float((counts < 2).mean())},
         "route_us": float(route_all.mean()) * 1e3,
         "eager_ms_per_step": eager_ms,
-        "timing": f"steps back to back, wall clock between two synchronisations" +
+        "step_call": ("moe_route_grouped_gemm_q4 (top-k launch, then one GEMM launch that ranks each expert's "
+                      "rows itself)" if fused else "moe_route then moe_grouped_gemm_q4"),
+        "timing": f"steps back to back" +
                   ("" if args.no_graph else f", replayed from HIP graphs each holding a chain of {layers} steps "
-                   "(route + GEMM launches, one weight copy each)") +
+                   "(the step's launches, one weight copy each), wall clock between two synchronisations") +
                   f"; weights rotate over {layers} resident copies ({layers * w_layer / 2**30:.2f} GiB) so each "
                   "GEMM reads them from HBM; GEMM time (gemm.us, the roofline's) by HIP events around graph replays: "
-                  "a chain of route + GEMM steps minus the same chain of routing alone, per step" +
-                  (" (eager: route and GEMM split by HIP events)" if
-                  args.no_graph else "; route_us and gemm.eager_event_us by HIP events in an eager run"),
+                  "a chain of steps minus the same chain of the routing that precedes the GEMM launch ("
+                  + ("moe_topk_softmax" if fused else "moe_route") + "), per step" +
+                  (" (eager: the step and the routing alone by HIP events)" if
+                  args.no_graph else "; route_us and gemm.eager_event_us by HIP events in eager runs (the "
+                   "step, then the routing alone)"),
         "gemm_us_p10_p90": [float(np.percentile(gemm_all, 10)) * 1e3, float(np.percentile(gemm_all, 90)) * 1e3],
     })
     if not args.no_cpu_baseline:

@@ -119,6 +119,17 @@ int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t*
               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
               int32_t* blocks, int32_t* num_blocks, void* workspace, size_t ws_bytes, void* stream);
 
+/* The first step of moe_route alone (section "Keep expert routing on the
+ * GPU"): each token's k largest logits and the softmax over them.
+ * In:  logits float32 [T, E].
+ * Out: topk_ids int32 [T, k], topk_w float [T, k], exactly as moe_route writes
+ *      them (same selection, same order, same weights).
+ * Sizes: as moe_route.  T = 0 writes nothing.  Errors: MOEQ4_ERR_SHAPE,
+ * MOEQ4_ERR_UNSUPPORTED (k > MOEQ4_MAX_TOPK), MOEQ4_ERR_NULL, MOEQ4_ERR_ALIGN,
+ * MOEQ4_ERR_HIP. */
+int moe_topk_softmax(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                     void* stream);
+
 /* Tiled copy of a stack of group-wise affine 4-bit matrices, the layout the
  * grouped GEMM streams.  It holds the same bytes as the row-major format
  * (codes E*N*K/2 bytes, scales and biases E*N*K/64 values each), re-ordered so
@@ -190,6 +201,38 @@ int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
                         const uint16_t* biases_t, const int32_t* perm, const int32_t* blocks,
                         const int32_t* num_blocks, int max_blocks, int block_rows, uint16_t* Y,
                         void* stream);
+
+/* Routing and the grouped GEMM of one prefill chunk in one call (section
+ * "Keep expert routing on the GPU": selection, histogram, scan, scatter and
+ * block map stay on the GPU next to the grouped GEMM; section "Dequantize
+ * weights during matrix multiplication" for the GEMM).  Outputs are exactly
+ * those of moe_route followed by moe_grouped_gemm_q4 with the same block_rows:
+ * topk_ids, topk_w, counts, offsets, perm, inv_perm, blocks, num_blocks and Y,
+ * bit for bit.
+ *
+ * With 64-row blocks (block_rows 64, or 0 when moe_default_block_rows picks
+ * 64) and T*k <= 4096 it runs two kernels: the top-k, then one GEMM launch in
+ * which each workgroup takes one expert and one 256-column tile, starts
+ * streaming that expert's weights at once, ranks the expert's assignments
+ * from the ids with wave ballots (the stable counting sort), writes the
+ * expert's part of perm and inv_perm (from its first column tile) and
+ * multiplies its rows 64 at a time; one more workgroup writes counts,
+ * offsets and the block map.  Otherwise it runs moe_route's kernels and then
+ * the grouped GEMM.
+ *
+ * In:  logits, X, codes_t, scales_t, biases_t as for moe_route and
+ *      moe_grouped_gemm_q4; block_rows, max_blocks as there.
+ * Out: the outputs of both calls.
+ * workspace: at least moe_route_workspace_bytes(T, E, k, block_rows) bytes.
+ * Sizes: those of both calls.  T = 0 writes what moe_route writes for T = 0.
+ * Errors: as for the two calls.  Output buffers must not overlap each other,
+ * the inputs or the workspace. */
+int moe_route_grouped_gemm_q4(const float* logits, const uint16_t* X, int T, int K, int N, int E, int k,
+                              const uint8_t* codes_t, const uint16_t* scales_t, const uint16_t* biases_t,
+                              int block_rows, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                              int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* blocks,
+                              int32_t* num_blocks, int max_blocks, uint16_t* Y, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /* Bytes of device scratch moe_expert_ffn_q4 needs (0 on invalid sizes):
  * 2*T*k*(I + H) bytes, plus 2*T*(I + H) with a shared expert, rounded up.

@@ -49,9 +49,12 @@ SIGNATURES = {
     "moe_max_blocks": (_i, [_i, _i, _i, _i]),
     "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "moe_route": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_topk_softmax": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
     "moe_prepack_q4": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_q4": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                  _vp, _vp]),
+    "moe_route_grouped_gemm_q4": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i] + [_vp] * 8 + [_i, _vp, _vp,
+                                                                                          _sz, _vp]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn_q4": (_i, [_vp, _i, _i, _i, _i, _i] + [_vp] * 12 + [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz,
                                                                        _vp]),
@@ -151,6 +154,11 @@ def moe_route(logits, T, E, k, block_rows, topk_ids, topk_w, counts, offsets, pe
         _stream(stream)))
 
 
+def moe_topk_softmax(logits, T, E, k, topk_ids, topk_w, stream=None):
+    _ok("moe_topk_softmax", lib().moe_topk_softmax(_p(logits), T, E, k, _p(topk_ids), _p(topk_w),
+                                                   _stream(stream)))
+
+
 def moe_prepack_q4(codes, scales, biases, E, N, K, codes_t, scales_t, biases_t, stream=None):
     _ok("moe_prepack_q4", lib().moe_prepack_q4(
         _p(codes), _p(scales), _p(biases), E, N, K, _p(codes_t), _p(scales_t), _p(biases_t),
@@ -162,6 +170,15 @@ def moe_grouped_gemm_q4(X, T, K, N, E, k, codes_t, scales_t, biases_t, perm, blo
     _ok("moe_grouped_gemm_q4", lib().moe_grouped_gemm_q4(
         _p(X), T, K, N, E, k, _p(codes_t), _p(scales_t), _p(biases_t), _p(perm), _p(blocks),
         _p(num_blocks), max_blocks, block_rows, _p(Y), _stream(stream)))
+
+
+def moe_route_grouped_gemm_q4(logits, X, T, K, N, E, k, codes_t, scales_t, biases_t, block_rows, topk_ids,
+                              topk_w, counts, offsets, perm, inv_perm, blocks, num_blocks, max_blocks, Y,
+                              workspace, ws_bytes, stream=None):
+    _ok("moe_route_grouped_gemm_q4", lib().moe_route_grouped_gemm_q4(
+        _p(logits), _p(X), T, K, N, E, k, _p(codes_t), _p(scales_t), _p(biases_t), block_rows, _p(topk_ids),
+        _p(topk_w), _p(counts), _p(offsets), _p(perm), _p(inv_perm), _p(blocks), _p(num_blocks), max_blocks,
+        _p(Y), _p(workspace), int(ws_bytes), _stream(stream)))
 
 
 def moe_expert_ffn_workspace_bytes(T: int, H: int, I: int, E: int, k: int, shared: bool) -> int:
@@ -284,6 +301,13 @@ def route(logits, k: int, block_rows: int = 0, bufs=None, stream=None):
     return b
 
 
+def topk_softmax(logits, k: int, bufs, stream=None):
+    """moe_topk_softmax of [T, E] float32 logits into bufs["topk_ids"] / bufs["topk_w"] (alloc_route)."""
+    T, E = logits.shape
+    moe_topk_softmax(logits, T, E, k, bufs["topk_ids"], bufs["topk_w"], stream)
+    return bufs
+
+
 def prepack(codes, scales, biases, stream=None):
     """Tiled copies (moe_prepack_q4) of [E, N, K/2] codes and [E, N, K/64] scales/biases."""
     E, N, K2 = codes.shape
@@ -302,6 +326,21 @@ def grouped_gemm_q4(X, k, packed, rt, Y=None, stream=None):
         Y = torch.empty((max(T * k, 1), N), dtype=torch.int16, device=X.device)
     moe_grouped_gemm_q4(X, T, K, N, E, k, codes_t, scales_t, biases_t, rt["perm"], rt["blocks"],
                         rt["num_blocks"], rt["max_blocks"], rt["block_rows"], Y, stream)
+    return Y
+
+
+def route_grouped_gemm_q4(logits, X, k, packed, rt, Y=None, stream=None):
+    """moe_route_grouped_gemm_q4: routing of [T, E] logits into the tables of ``rt`` (alloc_route) and
+    Y [T*k, N] bf16 bit patterns in sorted order, in one call; returns Y."""
+    codes_t, scales_t, biases_t = packed
+    T, K = X.shape
+    E, N, _ = codes_t.shape
+    if Y is None:
+        Y = torch.empty((max(T * k, 1), N), dtype=torch.int16, device=X.device)
+    moe_route_grouped_gemm_q4(logits, X, T, K, N, E, k, codes_t, scales_t, biases_t, rt["block_rows"],
+                              rt["topk_ids"], rt["topk_w"], rt["counts"], rt["offsets"], rt["perm"],
+                              rt["inv_perm"], rt["blocks"], rt["num_blocks"], rt["max_blocks"], Y,
+                              rt["workspace"], rt["ws_bytes"], stream)
     return Y
 
 

@@ -150,6 +150,15 @@ int moe_route(const float* logits, int T, int E, int k, int block_rows, int32_t*
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 
+int moe_topk_softmax(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, void* stream) {
+  const int rc = check_routing_shape(T, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  if (T == 0) return MOEQ4_OK;
+  if (!logits || !topk_ids || !topk_w) return MOEQ4_ERR_NULL;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOEQ4_ERR_ALIGN;
+  return topk_launch(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream) == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
 int moe_prepack_q4(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int E,
                    int N, int K, uint8_t* codes_t, uint16_t* scales_t, uint16_t* biases_t,
                    void* stream) {
@@ -201,6 +210,50 @@ int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
   const hipError_t err = gemm_q4_launch(X, T, K, N, E, k, codes_t, scales_t, biases_t, perm,
                                         blocks, num_blocks, max_blocks, bm, Y,
                                         (hipStream_t)stream);
+  return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
+}
+
+int moe_route_grouped_gemm_q4(const float* logits, const uint16_t* X, int T, int K, int N, int E, int k,
+                              const uint8_t* codes_t, const uint16_t* scales_t, const uint16_t* biases_t,
+                              int block_rows, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                              int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* blocks,
+                              int32_t* num_blocks, int max_blocks, uint16_t* Y, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  int rc = check_routing_shape(T, E, k);
+  if (rc != MOEQ4_OK) return rc;
+  if (K < 64 || K % 64 != 0 || N < 16 || N % 16 != 0) return MOEQ4_ERR_SHAPE;
+  if ((long long)T * K * 2 >= (1LL << 31) || (long long)E * N * (K / 2) >= (1LL << 31))
+    return MOEQ4_ERR_SHAPE;
+  const int bm = resolve_block_rows(T, E, k, block_rows);
+  if (bm <= 0) return bm;
+  const int bound = moe_max_blocks(T, E, k, bm);
+  if (bound < 0) return bound;
+  if (max_blocks < bound) return MOEQ4_ERR_SHAPE;
+  if (!counts || !offsets || !num_blocks) return MOEQ4_ERR_NULL;
+  if (T > 0 && (!logits || !X || !codes_t || !scales_t || !biases_t || !topk_ids || !topk_w || !perm ||
+                !inv_perm || !blocks || !Y))
+    return MOEQ4_ERR_NULL;
+  const RoutePlan plan = route_plan(T, E, k);
+  if (ws_bytes < plan.ws_bytes) return MOEQ4_ERR_WORKSPACE;
+  if (plan.ws_bytes > 0 && !workspace) return MOEQ4_ERR_NULL;
+  const void* ptrs[] = {logits, X, codes_t, scales_t, biases_t, topk_ids, topk_w, counts, offsets,
+                        perm, inv_perm, blocks, num_blocks, Y, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t err;
+  if (T > 0 && bm == 64 && (long long)T * k <= kRouteInLaunchMax) {
+    err = topk_launch(logits, T, E, k, topk_ids, topk_w, st);
+    if (err == hipSuccess)
+      err = route_gemm_q4_launch(topk_ids, X, T, K, N, E, k, codes_t, scales_t, biases_t, counts, offsets, perm,
+                                 inv_perm, blocks, num_blocks, Y, st);
+  } else {
+    err = route_launch(plan, logits, T, E, k, bm, topk_ids, topk_w, counts, offsets, perm, inv_perm, blocks,
+                       num_blocks, workspace, st);
+    if (err == hipSuccess && T > 0)
+      err = gemm_q4_launch(X, T, K, N, E, k, codes_t, scales_t, biases_t, perm, blocks, num_blocks, max_blocks, bm,
+                           Y, st);
+  }
   return err == hipSuccess ? MOEQ4_OK : MOEQ4_ERR_HIP;
 }
 

@@ -189,6 +189,10 @@ struct RoutePlan {
 
 RoutePlan route_plan(int T, int E, int k);
 
+// top-k + softmax alone (ids and weights), one wave per token
+hipError_t topk_launch(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                       hipStream_t stream);
+
 hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E, int k, int block_rows,
                         int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
                         int32_t* perm, int32_t* inv_perm, int32_t* blocks, int32_t* num_blocks,
@@ -228,7 +232,23 @@ struct GemmArgs {
   const uint16_t* dSt;
   const uint16_t* dBt;
   uint16_t* dY;
+  // Routing in the launch (tall-block kernels, no dense problem): non-null ids
+  // (the T*k selected experts) make each task one expert x one N tile; the
+  // task finds its expert's rows from the ids, writes the routing tables of
+  // its expert (N tile 0 only) and runs the expert's rows BM at a time.
+  const int32_t* ids;
+  int32_t* r_counts;
+  int32_t* r_offsets;
+  int32_t* r_perm;
+  int32_t* r_inv_perm;
+  int32_t* r_blocks;
+  int32_t* r_num_blocks;
 };
+
+// Assignments (T*k) up to which a tall-block GEMM launch can do the routing's
+// counting sort itself (one expert per task; each lane keeps one id per 256
+// assignments in registers).
+constexpr int kRouteInLaunchMax = 4096;
 
 // Workgroup -> (block, N tile) of a launch with dense_blocks dense blocks ahead
 // of the routed ones (routed_blocks, counted on the device), ntiles N tiles each.
@@ -279,6 +299,14 @@ hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, 
                           const uint16_t* St, const uint16_t* Bt, const int32_t* perm,
                           const int32_t* blocks, const int32_t* num_blocks, int max_blocks,
                           int block_rows, uint16_t* Y, hipStream_t stream);
+
+// Routing's counting sort (counts, offsets, perm, inv_perm, block map of 64-row
+// blocks) and the grouped GEMM in one launch, from the top-k ids; T*k <=
+// kRouteInLaunchMax.
+hipError_t route_gemm_q4_launch(const int32_t* ids, const uint16_t* X, int T, int K, int N, int E, int k,
+                                const uint8_t* Wt, const uint16_t* St, const uint16_t* Bt, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* blocks,
+                                int32_t* num_blocks, uint16_t* Y, hipStream_t stream);
 
 // prepack.hip: every weight rebuilt exactly into row-major bf16 [E][N][K]
 hipError_t dequant_launch(const uint8_t* codes_t, const uint16_t* scales_t, const uint16_t* biases_t, int E, int N,

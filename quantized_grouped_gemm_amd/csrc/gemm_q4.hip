@@ -8,6 +8,10 @@
 // expert load": each output tile of an expert maps to one workgroup, and the
 // tile height follows the rows per expert.
 //
+// With the routing's top-k done, the 64-row kernel can also rank the rows
+// itself (k_gemm_q4_w32 with FR, route_gemm_q4_launch): the routing's
+// histogram, scan and scatter then need no launches of their own.
+//
 // Blocks of up to 32 rows (k_gemm_q4): one workgroup = one block-map entry
 // (<= BM routed rows of one expert) x one N tile of WAVES*NF*16 columns.  Its
 // waves split the N tile; each wave owns NF 16-column fragments and every row
@@ -478,6 +482,95 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
   }
 }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for the wave's global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// The routing tables of a launch that routes, by one workgroup of NTHR
+// threads: counts, offsets, the block map of BM-row blocks and its count,
+// from a histogram of the ids (LDS atomics) and one scan over the experts in
+// order (thread t takes experts [t*EPT, t*EPT + EPT)).  lds: at least
+// MOEQ4_MAX_EXPERTS + 2 * NTHR / 64 ints.
+template <int BM, int NTHR>
+__device__ void route_tables(const GemmArgs& a, int* lds) {
+  constexpr int NW = NTHR / 64;
+  constexpr int EPT = (MOEQ4_MAX_EXPERTS + NTHR - 1) / NTHR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int A = a.A, E = a.E;
+  int* const hist = lds;
+  int* const part = lds + MOEQ4_MAX_EXPERTS;  // [2][NW] wave totals of rows and blocks
+  for (int j = tid; j < E; j += NTHR) hist[j] = 0;
+  lds_barrier();
+  constexpr int U = 8;  // loads in flight per thread
+  for (int i0 = 0; i0 < A; i0 += U * NTHR) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = a.ids[min(i0 + u * NTHR + tid, A - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + u * NTHR + tid < A) atomicAdd(&hist[min(max(v[u], 0), E - 1)], 1);
+  }
+  lds_barrier();
+  int c[EPT], nb[EPT], sc = 0, sb = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    c[j] = e < E ? hist[e] : 0;
+    nb[j] = (c[j] + BM - 1) / BM;
+    sc += c[j];
+    sb += nb[j];
+  }
+  int ic = sc, ib = sb;  // inclusive scans over the wave's lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int tc = __shfl_up(ic, o), tb = __shfl_up(ib, o);
+    if (lane >= o) {
+      ic += tc;
+      ib += tb;
+    }
+  }
+  if (lane == 63) {
+    part[wave] = ic;
+    part[NW + wave] = ib;
+  }
+  lds_barrier();
+  int oc = ic - sc, ob = ib - sb, nbt = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) {
+      oc += part[w];
+      ob += part[NW + w];
+    }
+    nbt += part[NW + w];
+  }
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid * EPT + j;
+    if (e < E) {
+      a.r_counts[e] = c[j];
+      a.r_offsets[e] = oc;
+      for (int b = 0; b < nb[j]; ++b)
+        *(int4*)&a.r_blocks[4 * (size_t)(ob + b)] = make_int4(e, oc + b * BM, min(BM, c[j] - b * BM), b);
+    }
+    oc += c[j];
+    ob += nb[j];
+  }
+  if (tid == 0) {
+    a.r_offsets[E] = A;
+    *a.r_num_blocks = nbt;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tall blocks (64/128/256 rows): bf16 MFMA 32x32x16, exact bf16 rebuild (DQ).
 //
@@ -494,7 +587,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_q4(const GemmArgs a) {
 // g then takes K indices g*64 + 32h + 8*s4 + [0,8) from lane half h, for both
 // operands, so every K-step stays inside one scale group.
 // OCC: workgroups per CU the kernel is sized for (registers and LDS)
-template <int BM, int NF32, int S, int WAVES, int EPI, int OCC>
+// FR: routing in the launch (section "Keep expert routing on the GPU"): the
+// tasks are experts instead of block-map entries; a workgroup ranks its
+// expert's assignments from the top-k ids (the stable counting sort), writes
+// that expert's part of perm and inv_perm, and runs the expert's rows BM at a
+// time; the grid's last workgroup writes counts, offsets and the block map
+// (route_tables).  The outputs are those of the routing kernels followed by
+// the same launch without FR.
+template <int BM, int NF32, int S, int WAVES, int EPI, int OCC, bool FR = false>
 __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs a0) {
   constexpr bool PAIRED = EPI == kEpiSwiglu && NF32 == 1;  // gate and up in one tile
   static_assert(EPI != kEpiSwiglu || NF32 % 2 == 0 || PAIRED, "SwiGLU pairs gate and up fragments");
@@ -519,7 +619,19 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   const int ntiles = (NOUT + TILE_N - 1) / TILE_N;
   bool dense;
   int blk, ntile, e, row0, rows;
-  if (!gemm_task_entry(a0, BM, ntiles, dense, blk, ntile, e, row0, rows)) return;
+  if constexpr (FR) {  // one expert per task; its rows come from the routing below
+    if (blockIdx.x == gridDim.x - 1) {  // the last workgroup writes the other routing tables
+      static_assert(!FR || (MOEQ4_MAX_EXPERTS + 2 * WAVES) * 4 <= (int)sizeof(xs), "table scratch fits");
+      route_tables<BM, NTHR>(a0, reinterpret_cast<int*>(&xs[0][0]));
+      return;
+    }
+    if (!gemm_task(0, a0.E, ntiles, dense, blk, ntile)) return;
+    e = blk;
+    row0 = 0;
+    rows = 1;
+  } else {
+    if (!gemm_task_entry(a0, BM, ntiles, dense, blk, ntile, e, row0, rows)) return;
+  }
   const GemmArgs a = dense ? gemm_dense(a0) : a0;
   const int K = a.K, N = a.N;
   const uint8_t* __restrict__ Wt = a.Wt;
@@ -547,7 +659,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   const int G = K / kGroup;
   const int nfull = G >> 1;
   const bool odd_tail = (G & 1) != 0;
-  const int mfa = (rows + 31) >> 5;  // row tiles holding rows
+  int mfa = (rows + 31) >> 5;  // row tiles holding rows
   const int NT = N / 16;
 
   const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -576,15 +688,18 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   const int x_oob = a.xrows * K * 2;  // rows past the block: the load returns zeros, no traffic
   // this lane's DMA source per instruction: row rb + lane/16, 16-byte column
   // (lane & 15) ^ (row & 15) of it
-  int xoff[IPW], xr[IPW], xg[IPW];
+  int xoff[IPW], xr[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) xr[i] = 4 * (wave * IPW + i) + (lane >> 4);
-  gemm_xrows(a, row0, rows, xr, xg);
+  if constexpr (!FR) {
+    int xg[IPW];
+    gemm_xrows(a, row0, rows, xr, xg);
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int r = xr[i];
-    const int c16 = (lane & 15) ^ (r & 15);
-    xoff[i] = r < rows ? xg[i] + c16 * 16 : x_oob;
+    for (int i = 0; i < IPW; ++i) {
+      const int r = xr[i];
+      const int c16 = (lane & 15) ^ (r & 15);
+      xoff[i] = r < rows ? xg[i] + c16 * 16 : x_oob;
+    }
   }
   if constexpr (EPI == kEpiScale)
     if (a.perm) ep_as = a.perm[row0 + min(tid, rows - 1)];
@@ -661,12 +776,15 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   };
 
   f32x16 acc[MF32][NF32];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < MF32; ++r)
+    for (int r = 0; r < MF32; ++r)
 #pragma unroll
-    for (int f = 0; f < NF32; ++f)
+      for (int f = 0; f < NF32; ++f)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[r][f][i] = 0.f;
+        for (int i = 0; i < 16; ++i) acc[r][f][i] = 0.f;
+  };
+  if constexpr (!FR) zero_acc();  // (routing in the launch: at the start of each pass)
 
   // K-step ks (0..7) of a chunk: K indices 64*(ks/4) + 32*half + 8*(ks%4) + [0,8) of the
   // chunk, from lane half `half`, for the activations (LDS, row col + 32 per row
@@ -771,8 +889,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
     bf16x8 av[LEAN ? 1 : 2][LEAN ? 1 : MFA];
     bf16x8 bw[2][NF32];
     if (nfull > 0) {
+      if constexpr (!FR)  // (routing in the launch: issued before each pass)
 #pragma unroll
-      for (int s = 0; s < S - 1; ++s) load(st[s], s);
+        for (int s = 0; s < S - 1; ++s) load(st[s], s);
 #pragma unroll
       for (int b = 0; b < kAhead; ++b) dma_x(min(b, nfull - 1), b, false);
       ep_weight();
@@ -847,64 +966,178 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
     }
   };
   static_assert(MF32 >= 1 && MF32 <= 8, "row tiles per block");
-  with_mfa<MF32>(mfa, run);
-
-  // epilogue: the MFMAs take the weights as the A operand, so each 32x32
-  // accumulator tile is transposed: lane l holds block row r*32 + l%32 and tile
-  // rows 8*(i/4) + 4*(l/32) + i%4 (i = 0..15), i.e. four runs of 4 adjacent
-  // columns.  Paired SwiGLU: runs 0 and 1 are gate columns whose up partners
-  // are runs 2 and 3.  Each wave converts its outputs of one 32-row tile into
-  // its own staging rows in LDS (the activation buffers, free after the
-  // loop), then reads them back row-wise: a lane stores 16 contiguous bytes
-  // and WCOLS/8 lanes one contiguous row segment, so a store instruction
-  // covers 64*8/WCOLS rows instead of 32 rows of 16 bytes each.  Only this
-  // wave touches its staging rows, and a wave's LDS operations complete in
-  // order, so the waits between writes and reads are the wave's own.
-  constexpr int WCOLS = NFO * OUTF;  // output columns of a wave
-  constexpr int SROW = WCOLS + 8;    // staged row, 16-byte pad
-  constexpr int LPR = WCOLS / 8;     // lanes per staged row
-  constexpr int RPI = 64 / LPR;      // rows per store instruction
-  static_assert(WAVES * 32 * SROW * 2 + (int)sizeof(EpiTab) <= (int)sizeof(xs),
-                "staging and the epilogue table fit in the activation buffers");
-  if constexpr (EPI == kEpiScale) {
-    __syncthreads();  // every wave is done with the activation buffers
-    if (tid < rows) {
-      ep_tab->as[tid] = ep_as;
-      ep_tab->w[tid] = ep_as >= 0 ? ep_w : 0.f;
+  int r_cnt = 0, r_off = 0;  // routing in the launch: the expert's rows and its first sorted row
+  // Routing in the launch keeps its state in registers and in the activation
+  // buffers before each pass's first DMA: the launch needs no LDS beyond them
+  // (measured: a 64-row launch with even 256 B of LDS past its 32 KB of
+  // buffers runs about 10% slower).
+  constexpr int RR = FR ? kRouteInLaunchMax / NTHR : 1;  // rounds of 64 assignments per wave
+  int v[RR];              // this lane's expert ids, one per round
+  int lim = 0, seg0 = 0;  // rounds of valid assignments of this lane; this wave's first rank
+  int* const red = reinterpret_cast<int*>(&xs[0][0]);  // [3][WAVES] partial counts
+  int* const rlp = red + 4 * WAVES;                     // [BM] the pass's rows: their tokens
+  // Ranks of this lane's rows of expert e (rounds in order, then waves, then
+  // lanes: the stable counting sort), from the wave's ballots; f(i, rank) for each.
+  auto for_ranks = [&](auto&& f) __attribute__((always_inline)) {
+    const uint64_t ltm = lanemask_lt();
+    int run = seg0;
+#pragma unroll
+    for (int i = 0; i < RR; ++i) {
+      const bool eq = (i < lim) & (v[i] == e);
+      const uint64_t b = __ballot(eq);
+      if (eq) f(i, run + (int)__popcll(b & ltm));
+      run += (int)__popcll(b);
     }
+  };
+  // rlp = the tokens of ranks [pass*BM, pass*BM + BM)
+  auto fill_pass_rows = [&](int pass) __attribute__((always_inline)) {
+    const int lo = pass * BM;
+    for_ranks([&](int i, int rank) {
+      if (rank >= lo && rank < lo + BM) rlp[rank - lo] = (wave * RR * 64 + i * 64 + lane) / a0.k;
+    });
+  };
+  if constexpr (FR) {
+    // The expert's rows from the ids.  Wave w takes the assignments [w*Q,
+    // (w+1)*Q), Q = RR*64, one per lane and round.  The expert's first weight
+    // loads need no routing: they go out right behind the ids, so the waits
+    // for the ids leave them in flight.  Ballots count the
+    // wave's rows of e and its assignments to experts below e; the waves'
+    // counts give each wave's first rank, the expert's row count and its
+    // offset.  (The ids come from this call's top-k, so they lie in [0, E).)
+    static_assert(!FR || (EPI == kEpiPlain && (4 * WAVES + BM) * 4 <= (int)sizeof(xs)), "routing in the launch");
+    const int A = a0.A;
+    constexpr int Q = RR * 64;
+    const int a_w = wave * Q;
+#pragma unroll
+    for (int i = 0; i < RR; ++i) v[i] = a0.ids[min(a_w + i * 64 + lane, A - 1)];  // clamped: all in flight
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) load(st[s], s);
+    __builtin_amdgcn_sched_barrier(0);
+    lim = min(RR, max(0, (A - a_w - lane + 63) >> 6));
+    int run = 0, lt = 0;
+#pragma unroll
+    for (int i = 0; i < RR; ++i) {
+      const bool valid = i < lim;
+      lt += valid & (v[i] < e) ? 1 : 0;
+      run += (int)__popcll(__ballot(valid & (v[i] == e)));
+    }
+    lt = wave_sum_i32(lt);
+    if (lane == 0) {
+      red[wave] = run;
+      red[WAVES + wave] = lt;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      seg0 += w < wave ? red[w] : 0;
+      r_cnt += red[w];
+      r_off += red[WAVES + w];
+    }
+    // this expert's part of perm and inv_perm (the other tables: the last
+    // workgroup), and the first pass's rows
+    const bool tab = ntile == 0;
+    for_ranks([&](int i, int rank) {
+      const int as = a_w + i * 64 + lane;
+      if (tab) {
+        a0.r_perm[r_off + rank] = as;
+        a0.r_inv_perm[as] = r_off + rank;
+      }
+      if (rank < BM) rlp[rank] = as / a0.k;
+    });
+    if (r_cnt == 0) {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no load left in flight
+      return;
+    }
+    lds_barrier();
   }
-  __syncthreads();  // every wave is done with the activation buffers; the table is written
-  uint16_t* const stg = &xs[0][0] + wave * 32 * SROW;
+
+  // One pass per BM rows of the expert when routing in the launch; one pass otherwise.
+  for (int pass = 0;; ++pass) {
+    if constexpr (FR) {
+      row0 = r_off + pass * BM;
+      rows = min(BM, r_cnt - pass * BM);
+      mfa = (rows + 31) >> 5;
 #pragma unroll
-  for (int r = 0; r < MF32; ++r) {
-    if (r >= mfa) break;
-    {
-      const EpiRow<EPI> er(Yout, ldy, row0, min(r * 32 + col, rows - 1), ep_tab);
-      if constexpr (PAIRED) {
+      for (int i = 0; i < IPW; ++i) {
+        const int r = xr[i];
+        const int c16 = (lane & 15) ^ (r & 15);
+        const int tok = rlp[min(r, rows - 1)];
+        xoff[i] = r < rows ? tok * K * 2 + c16 * 16 : x_oob;
+      }
+      zero_acc();
+      if (pass > 0)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          *(uint2*)&stg[col * SROW + 8 * j + 4 * half] = er.pack4(quad(acc[r][0], j), quad(acc[r][0], j + 2));
-      } else {
-#pragma unroll
-        for (int f = 0; f < NFO; ++f)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 v = quad(acc[r][f], j);
-            f32x4 u = v;
-            if constexpr (EPI == kEpiSwiglu) u = quad(acc[r][f + NFO], j);
-            *(uint2*)&stg[col * SROW + f * 32 + 8 * j + 4 * half] = er.pack4(v, u);
-          }
+        for (int s = 0; s < S - 1; ++s) load(st[s], s);
+      lds_barrier();  // every wave has its rows before the DMA overwrites them
+    }
+    with_mfa<MF32>(mfa, run);
+
+    // epilogue: the MFMAs take the weights as the A operand, so each 32x32
+    // accumulator tile is transposed: lane l holds block row r*32 + l%32 and tile
+    // rows 8*(i/4) + 4*(l/32) + i%4 (i = 0..15), i.e. four runs of 4 adjacent
+    // columns.  Paired SwiGLU: runs 0 and 1 are gate columns whose up partners
+    // are runs 2 and 3.  Each wave converts its outputs of one 32-row tile into
+    // its own staging rows in LDS (the activation buffers, free after the
+    // loop), then reads them back row-wise: a lane stores 16 contiguous bytes
+    // and WCOLS/8 lanes one contiguous row segment, so a store instruction
+    // covers 64*8/WCOLS rows instead of 32 rows of 16 bytes each.  Only this
+    // wave touches its staging rows, and a wave's LDS operations complete in
+    // order, so the waits between writes and reads are the wave's own.
+    constexpr int WCOLS = NFO * OUTF;  // output columns of a wave
+    constexpr int SROW = WCOLS + 8;    // staged row, 16-byte pad
+    constexpr int LPR = WCOLS / 8;     // lanes per staged row
+    constexpr int RPI = 64 / LPR;      // rows per store instruction
+    static_assert(WAVES * 32 * SROW * 2 + (int)sizeof(EpiTab) <= (int)sizeof(xs),
+                  "staging and the epilogue table fit in the activation buffers");
+    if constexpr (EPI == kEpiScale) {
+      __syncthreads();  // every wave is done with the activation buffers
+      if (tid < rows) {
+        ep_tab->as[tid] = ep_as;
+        ep_tab->w[tid] = ep_as >= 0 ? ep_w : 0.f;
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave is done with the activation buffers; the table is written
+    uint16_t* const stg = &xs[0][0] + wave * 32 * SROW;
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int rr = i * RPI + lane / LPR, cq = lane % LPR;
-      const int row = r * 32 + rr, n = n_wave + 8 * cq;
-      const uint4 bits = *(const uint4*)&stg[rr * SROW + 8 * cq];
-      if (row < rows && n < NOUT) EpiRow<EPI>(Yout, ldy, row0, row, ep_tab).store8(n, bits);
+    for (int r = 0; r < MF32; ++r) {
+      if (r >= mfa) break;
+      {
+        const EpiRow<EPI> er(Yout, ldy, row0, min(r * 32 + col, rows - 1), ep_tab);
+        if constexpr (PAIRED) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            *(uint2*)&stg[col * SROW + 8 * j + 4 * half] = er.pack4(quad(acc[r][0], j), quad(acc[r][0], j + 2));
+        } else {
+#pragma unroll
+          for (int f = 0; f < NFO; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const f32x4 v = quad(acc[r][f], j);
+              f32x4 u = v;
+              if constexpr (EPI == kEpiSwiglu) u = quad(acc[r][f + NFO], j);
+              *(uint2*)&stg[col * SROW + f * 32 + 8 * j + 4 * half] = er.pack4(v, u);
+            }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int rr = i * RPI + lane / LPR, cq = lane % LPR;
+        const int row = r * 32 + rr, n = n_wave + 8 * cq;
+        const uint4 bits = *(const uint4*)&stg[rr * SROW + 8 * cq];
+        if (row < rows && n < NOUT) EpiRow<EPI>(Yout, ldy, row0, row, ep_tab).store8(n, bits);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads back before the next tile's writes
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads back before the next tile's writes
+    if constexpr (!FR) {
+      break;
+    } else {
+      if ((pass + 1) * BM >= r_cnt) break;
+      __syncthreads();  // every wave's staging reads are done before the next pass's rows
+      fill_pass_rows(pass + 1);
+      lds_barrier();
+    }
   }
 }
 
@@ -1286,6 +1519,40 @@ hipError_t gemm_q4_launch(const uint16_t* X, int T, int K, int N, int E, int k, 
   a.Y = Y;
   a.ldy = N;
   return gemm_launch(a, kEpiPlain, BM, max_blocks, stream);
+}
+
+hipError_t route_gemm_q4_launch(const int32_t* ids, const uint16_t* X, int T, int K, int N, int E, int k,
+                                const uint8_t* Wt, const uint16_t* St, const uint16_t* Bt, int32_t* counts,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* blocks,
+                                int32_t* num_blocks, uint16_t* Y, hipStream_t stream) {
+  if ((long long)T * k > kRouteInLaunchMax || T < 1) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.X = X;
+  a.xrows = T;
+  a.K = K;
+  a.N = N;
+  a.E = E;
+  a.A = T * k;
+  a.k = k;
+  a.Wt = Wt;
+  a.St = St;
+  a.Bt = Bt;
+  a.Y = Y;
+  a.ldy = N;
+  a.ids = ids;
+  a.r_counts = counts;
+  a.r_offsets = offsets;
+  a.r_perm = perm;
+  a.r_inv_perm = inv_perm;
+  a.r_blocks = blocks;
+  a.r_num_blocks = num_blocks;
+  // the 64-row tall-block kernel: 4 waves x 2 fragments of 32 columns per task
+  constexpr int kTileN = 4 * 2 * 32;
+  const void* fn = (const void*)&k_gemm_q4_w32<64, 2, 2, 4, kEpiPlain, 2, true>;
+  // one more workgroup, the last, for the routing tables
+  dim3 grid = task_grid(0, E, (N + kTileN - 1) / kTileN);
+  grid.x += 1;
+  return launch("k_gemm_q4_w32 (routing)", fn, grid, dim3(4 * 64), 0, stream, a);
 }
 
 }  // namespace moeq4

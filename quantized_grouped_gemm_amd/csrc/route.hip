@@ -449,6 +449,23 @@ RoutePlan route_plan(int T, int E, int k) {
   return p;
 }
 
+static const void* topk_kernel(int E) {
+  if (E <= 64) return (const void*)&k_topk_rank<1>;
+  if (E <= 128) return (const void*)&k_topk_rank<2>;
+  if (E <= 256) return (const void*)&k_topk_rank<4>;
+  if (E <= 512) return (const void*)&k_topk_rank<8>;
+  return (const void*)&k_topk_rank<16>;
+}
+
+hipError_t topk_launch(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  return launch("k_topk_rank", topk_kernel(E), dim3((T + kTopkSmallWaves - 1) / kTopkSmallWaves),
+                dim3(64 * kTopkSmallWaves), 0, stream, logits, T, E, k, kTopkSmallWaves, nbits, 0, ids, w,
+                (int32_t*)nullptr, (int32_t*)nullptr);
+}
+
 hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E, int k, int BM,
                         int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv_perm, int32_t* blocks, int32_t* num_blocks, void* workspace,
@@ -459,19 +476,12 @@ hipError_t route_launch(const RoutePlan& plan, const float* logits, int T, int E
   const int small = A <= kSmallAssignMax;
   hipError_t err = hipSuccess;
   if (plan.nchunks > 0) {
-    const void* fn;
-    if (E <= 64) fn = (const void*)&k_topk_rank<1>;
-    else if (E <= 128) fn = (const void*)&k_topk_rank<2>;
-    else if (E <= 256) fn = (const void*)&k_topk_rank<4>;
-    else if (E <= 512) fn = (const void*)&k_topk_rank<8>;
-    else fn = (const void*)&k_topk_rank<16>;
     if (small) {
-      err = launch("k_topk_rank", fn, dim3((T + kTopkSmallWaves - 1) / kTopkSmallWaves), dim3(64 * kTopkSmallWaves),
-                   0, stream, logits, T, E, k, kTopkSmallWaves, plan.nbits, 0, ids, w, chunk_counts, local_rank);
+      err = topk_launch(logits, T, E, k, ids, w, stream);
     } else {
       const size_t shmem = sizeof(int) * (size_t)plan.tpc * k + sizeof(uint16_t) * (size_t)kRouteWaves * E;
-      err = launch("k_topk_rank", fn, dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T, E, k,
-                   plan.tpc, plan.nbits, 1, ids, w, chunk_counts, local_rank);
+      err = launch("k_topk_rank", topk_kernel(E), dim3(plan.nchunks), dim3(kRouteThreads), shmem, stream, logits, T,
+                   E, k, plan.tpc, plan.nbits, 1, ids, w, chunk_counts, local_rank);
     }
     if (err != hipSuccess) return err;
   }

@@ -114,6 +114,40 @@ def test_gemm_validation():
     assert _gemm(T=0, X=None, Y=None) == q.MOEQ4_OK     # nothing to do: no launch
 
 
+def test_topk_validation():
+    f = q.lib().moe_topk_softmax
+    assert f(FAKE, 8, 16, 0, FAKE, FAKE, None) == q.MOEQ4_ERR_SHAPE
+    assert f(FAKE, 8, 16, 17, FAKE, FAKE, None) == q.MOEQ4_ERR_SHAPE
+    assert f(FAKE, 8, 2048, 8, FAKE, FAKE, None) == q.MOEQ4_ERR_SHAPE        # E > MOEQ4_MAX_EXPERTS
+    assert f(FAKE, 8, 256, 65, FAKE, FAKE, None) == q.MOEQ4_ERR_UNSUPPORTED   # k > MOEQ4_MAX_TOPK
+    assert f(None, 8, 16, 2, FAKE, FAKE, None) == q.MOEQ4_ERR_NULL
+    assert f(FAKE, 8, 16, 2, FAKE + 4, FAKE, None) == q.MOEQ4_ERR_ALIGN
+    assert f(None, 0, 16, 2, None, None, None) == q.MOEQ4_OK                # T = 0: nothing to do
+
+
+def _route_gemm(**kw):
+    a = dict(logits=FAKE, X=FAKE, T=8, K=256, N=128, E=16, k=2, Wq=FAKE, scales=FAKE, biases=FAKE,
+             block_rows=64, topk_ids=FAKE, topk_w=FAKE, counts=FAKE, offsets=FAKE, perm=FAKE, inv_perm=FAKE,
+             blocks=FAKE, num_blocks=FAKE, max_blocks=1000, Y=FAKE, workspace=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return q.lib().moe_route_grouped_gemm_q4(*a.values())
+
+
+def test_route_gemm_validation():
+    assert _route_gemm(K=96) == q.MOEQ4_ERR_SHAPE
+    assert _route_gemm(N=120) == q.MOEQ4_ERR_SHAPE
+    assert _route_gemm(k=0) == q.MOEQ4_ERR_SHAPE
+    assert _route_gemm(block_rows=48) == q.MOEQ4_ERR_SHAPE
+    assert _route_gemm(max_blocks=q.moe_max_blocks(8, 16, 2, 64) - 1) == q.MOEQ4_ERR_SHAPE
+    assert _route_gemm(logits=None) == q.MOEQ4_ERR_NULL
+    assert _route_gemm(X=None) == q.MOEQ4_ERR_NULL
+    assert _route_gemm(inv_perm=None) == q.MOEQ4_ERR_NULL
+    assert _route_gemm(num_blocks=None) == q.MOEQ4_ERR_NULL
+    assert _route_gemm(ws_bytes=0, block_rows=128) == q.MOEQ4_ERR_WORKSPACE
+    assert _route_gemm(Y=FAKE + 2) == q.MOEQ4_ERR_ALIGN
+    assert _route_gemm(topk_w=FAKE + 4) == q.MOEQ4_ERR_ALIGN
+
+
 def test_single_hip_runtime_in_process():
     # torch's HIP runtime must be the one libmoeq4 binds to (streams and
     # pointers come from torch); two copies of libamdhip64 would not share them
