@@ -28,6 +28,9 @@
 //                    inv_perm from the offsets, which every workgroup scans
 //                    from the counts; workgroup 0 also writes the offsets,
 //                    the block counts' scan and the block map.
+// moe_topk_softmax runs k_topk_rank alone; moe_route_grouped_gemm_q4 runs it
+// and leaves the rest to the GEMM launch when that launch can rank the rows
+// itself (gemm_q4.hip).
 // Only integer adds decide positions, so every output is deterministic.
 #include "common.h"
 
