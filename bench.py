@@ -612,7 +612,8 @@ def host_block_map(counts, bm):
 def bench_ablation(args, torch, q, W, T, d):
     """The pages' two prefill mechanisms, each against its unfused alternative,
     on the single-projection shape (E=256, k=8, K=2048, N=512) at T tokens:
-      fused     moe_route + moe_grouped_gemm_q4 (the product path);
+      fused     moe_route + moe_grouped_gemm_q4 (the product path as two calls; every arm
+                routes with the same moe_route call);
       unfused   moe_route + moe_dequant_q4 (every weight rebuilt as bf16 into
                 HBM) + a bf16 grouped GEMM on the expanded weights: the vendor
                 batched GEMM (torch.bmm -> hipBLASLt) over per-expert padded
