@@ -342,7 +342,8 @@ def bench_gemm(args, torch, q, W, w, d):
     ms_per_step = eager_ms
     if not args.no_graph:
         ms_per_step = graph_ms_per_step(torch, args, whole, layers)
-        _, _, gemm_ms = graph_split_ms(torch, pre, None, layers, max(1, args.steps // layers), whole=whole)
+        split_step_ms, split_pre_ms, gemm_ms = graph_split_ms(torch, pre, None, layers, max(1, args.steps // layers),
+                                                              whole=whole)
     counts = rt["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     A = T * k
@@ -359,6 +360,8 @@ def bench_gemm(args, torch, q, W, w, d):
     out.update({
         "weight_GBps_step": w_bytes / (ms_per_step * 1e-3) / 1e9,
         "gemm": {"us": gemm_ms * 1e3, "eager_event_us": gemm_eager_ms * 1e3, "TFLOP/s": flops / (gemm_ms * 1e-3) / 1e12,
+                 "split_step_us": None if args.no_graph else split_step_ms * 1e3,
+                 "split_pre_us": None if args.no_graph else split_pre_ms * 1e3,
                  "weight_GB/s": w_bytes / (gemm_ms * 1e-3) / 1e9, "experts_touched": touched,
                  "rows_max_over_mean": float(counts.max() / counts.mean()),
                  "experts_below_2_rows": float((counts < 2).mean())},

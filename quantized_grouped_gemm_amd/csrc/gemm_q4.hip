@@ -1036,7 +1036,10 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
     }
     // this expert's part of perm and inv_perm (the other tables: the last
     // workgroup), and the first pass's rows
-    const bool tab = ntile == 0;
+    // (r_off + r_cnt <= A holds for ids in [0, E); the check keeps every
+    // write inside perm, inv_perm and Y whatever the ids)
+    const bool in_range = r_off + r_cnt <= A;
+    const bool tab = ntile == 0 && in_range;
     for_ranks([&](int i, int rank) {
       const int as = a_w + i * 64 + lane;
       if (tab) {
@@ -1045,7 +1048,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
       }
       if (rank < BM) rlp[rank] = as / a0.k;
     });
-    if (r_cnt == 0) {
+    if (r_cnt == 0 || !in_range) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no load left in flight
       return;
     }
