@@ -974,10 +974,11 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
   constexpr int RR = FR ? kRouteInLaunchMax / NTHR : 1;  // rounds of 64 assignments per wave
   int v[RR];              // this lane's expert ids, one per round
   int lim = 0, seg0 = 0;  // rounds of valid assignments of this lane; this wave's first rank
-  int* const red = reinterpret_cast<int*>(&xs[0][0]);  // [3][WAVES] partial counts
+  int* const red = reinterpret_cast<int*>(&xs[0][0]);  // [2][WAVES] the waves' counts
   int* const rlp = red + 4 * WAVES;                     // [BM] the pass's rows: their tokens
-  // Ranks of this lane's rows of expert e (rounds in order, then waves, then
-  // lanes: the stable counting sort), from the wave's ballots; f(i, rank) for each.
+  // Ranks of this lane's rows of expert e in assignment order (waves, then
+  // rounds, then lanes: the stable counting sort), from the wave's ballots;
+  // f(i, rank) for each.
   auto for_ranks = [&](auto&& f) __attribute__((always_inline)) {
     const uint64_t ltm = lanemask_lt();
     int run = seg0;
@@ -1000,10 +1001,10 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_gemm_q4_w32(const GemmArgs 
     // The expert's rows from the ids.  Wave w takes the assignments [w*Q,
     // (w+1)*Q), Q = RR*64, one per lane and round.  The expert's first weight
     // loads need no routing: they go out right behind the ids, so the waits
-    // for the ids leave them in flight.  Ballots count the
-    // wave's rows of e and its assignments to experts below e; the waves'
-    // counts give each wave's first rank, the expert's row count and its
-    // offset.  (The ids come from this call's top-k, so they lie in [0, E).)
+    // for the ids leave them in flight.  Ballots count the wave's rows of e
+    // and its assignments to experts below e; the waves' counts give each
+    // wave's first rank, the expert's row count and its offset.  (The ids
+    // come from this call's top-k, so they lie in [0, E).)
     static_assert(!FR || (EPI == kEpiPlain && (4 * WAVES + BM) * 4 <= (int)sizeof(xs)), "routing in the launch");
     const int A = a0.A;
     constexpr int Q = RR * 64;

@@ -36,11 +36,21 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("gemm_q4.hip", "common.h", "ffn.hip", "decode.hip", "gemv.h")
 
 
-def kernel_source_hash(files=KERNEL_SOURCES) -> str:
+def _code_only(text: str) -> str:
+    """The source without its comments and blank space: what the compiler sees
+    (string literals in these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(files=KERNEL_SOURCES, root=None) -> str:
+    """Hash of the kernels' code (comments and spacing ignored): counters taken
+    on one hash stay valid while the code they measured is unchanged."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(_PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root or os.path.join(_PKG, "csrc"), f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
