@@ -96,6 +96,7 @@ def test_route_gemm_prefill_chunk_full_size():
     (512, 8, 8, 128, 64),      # k = E: every token picks every expert (8 passes each)
     (40, 4, 2, 64, 32),        # one group of K: no full chunk to start early
     (700, 64, 4, 256, 48),     # 11 rounds of 256 assignments; a 48-column tile
+    (64, 1024, 64, 128, 32),   # the widest top-k over the most experts: 4096 assignments
 ])
 def test_route_gemm_shapes(T, E, k, K, N):
     _check(W.custom(90, T, E, k, K, N), 64)
@@ -106,6 +107,14 @@ def test_route_gemm_hot_expert_many_passes():
     w = W.custom(91, 500, 256, 8, 256, 128)
     g = _check(w, 64, logits=_hot_logits(w.T, w.E, 91))
     assert g["counts"][3] == w.T
+
+
+def test_route_gemm_tied_logits():
+    # logits on a coarse grid: most tokens hold exact ties inside and at the
+    # edge of their top k, settled by the lower expert id as in the oracle
+    w = W.custom(97, 256, 64, 6, 128, 64)
+    l = np.random.default_rng([97, 256, 64]).standard_normal((256, 64))
+    _check(w, 64, logits=(np.round(l * 2) / 2).astype(np.float32))
 
 
 @pytest.mark.parametrize("T,E,k,bm", [
