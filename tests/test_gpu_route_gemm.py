@@ -102,6 +102,31 @@ def test_route_gemm_shapes(T, E, k, K, N):
     _check(W.custom(90, T, E, k, K, N), 64)
 
 
+def _random_shape(seed):
+    # a seeded shape inside the one-launch limits (T*k <= 4096), weights kept small
+    r = np.random.default_rng([98, seed])
+    E = int(r.choice([1, 3, 8, 17, 64, 200, 256, 511, 1024]))
+    k = int(r.integers(1, min(E, 64) + 1))
+    T = int(r.integers(1, 4096 // k + 1))
+    K = 64 * int(r.integers(1, 9))
+    N = 16 * int(r.integers(1, 17))
+    while E * N * K > (1 << 24):  # halve N, then K, in whole tiles
+        if N > 16:
+            N = 16 * max(1, N // 32)
+        else:
+            K = 64 * max(1, K // 128)
+    return T, E, k, K, N
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_route_gemm_random_shapes(seed):
+    # seeded shapes across the limits: tables against the oracle, Y against the
+    # oracle and bit for bit against the two calls
+    T, E, k, K, N = _random_shape(seed)
+    print(f"route+gemm random case {seed}: T={T} E={E} k={k} K={K} N={N}", flush=True)
+    _check(W.custom(100 + seed, T, E, k, K, N), 64)
+
+
 def test_route_gemm_hot_expert_many_passes():
     # one expert takes all 500 tokens: its workgroups run 8 passes of 64 rows
     w = W.custom(91, 500, 256, 8, 256, 128)
