@@ -88,6 +88,8 @@ def test_decode_tied_logits(decode_model):
     (8, 1, 256, 128, True),
     (1024, 64, 256, 128, True),  # the largest expert count and top-k
     (32, 32, 128, 128, True),    # k = E, smallest sizes
+    (8, 2, 8192, 128, True),     # the largest H: x staged as two 16-byte pieces per thread
+    (64, 63, 256, 512, True),    # J * I = 32768, the most h one down workgroup stages (64 KB of LDS)
 ])
 def test_decode_shapes(E, k, H, I, shared):
     m = Model(W.custom(60 + k, 1, E, k, H, I, ffn=True), shared=shared)
