@@ -83,6 +83,17 @@ def test_ffn_no_shared(bm):
     Layer(W.custom(72, 100, 16, 4, 256, 128, ffn=True), shared=False).check(bm)
 
 
+@pytest.mark.parametrize("bm", [16, 64, 160])
+def test_ffn_smallest_dims(bm):
+    # H = I = 64: one scale group along each contraction, one 64-column tile
+    Layer(W.custom(75, 50, 8, 2, 64, 64, ffn=True)).check(bm)
+
+
+def test_ffn_most_experts_widest_topk():
+    # E = 1024 experts, k = 64 of them per token
+    Layer(W.custom(76, 20, 1024, 64, 128, 64, ffn=True)).check(64)
+
+
 def test_ffn_few_tokens():
     Layer(W.custom(73, 3, 32, 8, 256, 128, ffn=True)).check(16)
 
