@@ -299,10 +299,11 @@ def bench_gemm(args, torch, q, W, w, d):
     rt = q.alloc_route(T, E, k, args.block_rows, device=X.device)
     Y = torch.empty((T * k, N), dtype=torch.int16, device=X.device)
     stream = torch.cuda.current_stream()
-    # 64-row blocks up to 8192 assignments: one call, whose GEMM launch ranks
-    # each expert's rows itself after the top-k (moe_route_grouped_gemm_q4);
-    # the routing that precedes the GEMM launch is then the top-k alone
-    fused = rt["block_rows"] == 64 and 0 < T * k <= 8192
+    # 64-row blocks up to MOEQ4_ROUTE_IN_LAUNCH_MAX assignments: one call, whose
+    # GEMM launch ranks each expert's rows itself after the top-k
+    # (moe_route_grouped_gemm_q4); the routing that precedes the GEMM launch is
+    # then the top-k alone
+    fused = rt["block_rows"] == 64 and 0 < T * k <= q.MOEQ4_ROUTE_IN_LAUNCH_MAX
     cur = torch.cuda.current_stream
 
     def pre(l, st=None):

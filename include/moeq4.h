@@ -202,6 +202,10 @@ int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
                         const int32_t* num_blocks, int max_blocks, int block_rows, uint16_t* Y,
                         void* stream);
 
+/* Most assignments (T*k) whose rows moe_route_grouped_gemm_q4 ranks inside
+ * its GEMM launch. */
+#define MOEQ4_ROUTE_IN_LAUNCH_MAX 4096
+
 /* Routing and the grouped GEMM of one prefill chunk in one call (section
  * "Keep expert routing on the GPU": selection, histogram, scan, scatter and
  * block map stay on the GPU next to the grouped GEMM; section "Dequantize
@@ -211,7 +215,7 @@ int moe_grouped_gemm_q4(const uint16_t* X, int T, int K, int N, int E, int k,
  * bit for bit.
  *
  * With 64-row blocks (block_rows 64, or 0 when moe_default_block_rows picks
- * 64) and T*k <= 4096 it runs two kernels: the top-k, then one GEMM launch in
+ * 64) and T*k <= MOEQ4_ROUTE_IN_LAUNCH_MAX it runs two kernels: the top-k, then one GEMM launch in
  * which each workgroup takes one expert and one 256-column tile, starts
  * streaming that expert's weights at once, ranks the expert's assignments
  * from the ids with wave ballots (the stable counting sort), writes the

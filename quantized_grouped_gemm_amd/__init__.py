@@ -32,6 +32,7 @@ MOEQ4_ERR_HIP = -6
 MOEQ4_MAX_EXPERTS = 1024
 MOEQ4_MAX_TOPK = 64
 MOEQ4_SMALL_MAX_T = 8
+MOEQ4_ROUTE_IN_LAUNCH_MAX = 4096
 MOEQ4_DECODE_SCRATCH_BYTES = 256 * 1024
 MOEQ4_PATH_DECODE = 1
 MOEQ4_PATH_FEW_ROWS = 2

@@ -242,7 +242,8 @@ int moe_route_grouped_gemm_q4(const float* logits, const uint16_t* X, int T, int
     if (p && !aligned16(p)) return MOEQ4_ERR_ALIGN;
   const hipStream_t st = (hipStream_t)stream;
   hipError_t err;
-  if (T > 0 && bm == 64 && (long long)T * k <= kRouteInLaunchMax) {
+  static_assert(kRouteInLaunchMax == MOEQ4_ROUTE_IN_LAUNCH_MAX, "the launch's ranking limit");
+  if (T > 0 && bm == 64 && (long long)T * k <= MOEQ4_ROUTE_IN_LAUNCH_MAX) {
     err = topk_launch(logits, T, E, k, topk_ids, topk_w, st);
     if (err == hipSuccess)
       err = route_gemm_q4_launch(topk_ids, X, T, K, N, E, k, codes_t, scales_t, biases_t, counts, offsets, perm,

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_limits_match_header():
     src = open(HDR).read()
-    for name in ("MOEQ4_MAX_EXPERTS", "MOEQ4_MAX_TOPK", "MOEQ4_SMALL_MAX_T"):
+    for name in ("MOEQ4_MAX_EXPERTS", "MOEQ4_MAX_TOPK", "MOEQ4_SMALL_MAX_T", "MOEQ4_ROUTE_IN_LAUNCH_MAX"):
         m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
         assert m and int(m.group(1)) == getattr(q, name), name
 
